@@ -1,0 +1,173 @@
+"""fp64 CPU oracle of the causal linear-attention (Lightning Attention) layer.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library never
+imports, links or calls it, and it shares no code with the HIP library.
+
+The arithmetic lives in ``la_oracle.c`` (plain C, double precision, OpenMP over
+independent (batch, head, value-column block) tasks); this module only builds
+and loads it and marshals numpy arrays.  Every function takes inputs as float32
+arrays (exact images of bf16 or fp32 data) and returns float64 results.
+
+What each function follows (pages cited by title and section):
+  * ``rmsnorm_row`` / ``rope_row`` / ``prologue`` -- QK-normalization and RoPE of
+    the linear layers: "創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B模型"
+    (MiniCPM-SALA technical-report rendering), 02 模型架構 (3) 線性注意力模塊 and
+    (4) 混合位置編碼 (HyPE).
+  * ``forward`` -- the state update S_t = S_{t-1} + k_t v_t^T of "MiniCPM-SALA:
+    Hybridizing Sparse and Linear Attention for Efficient Long-Context Modeling"
+    (paper digest), 前置知识 > 线性注意力, read out as o_t = sigmoid(g_t) * (q_t S_t).
+  * ``chunked`` -- the same sum regrouped by chunks (for the chunk invariance check).
+  * ``decode_step`` -- ``forward`` with one token.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_DIR, "la_oracle.c")
+_LIB = os.path.join(_DIR, "liblaoracle.so")
+_lib = None
+
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile la_oracle.c into liblaoracle.so with gcc (-O2 -fopenmp)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(lib):
+    lib.lao_set_threads.argtypes = [ctypes.c_int]
+    lib.lao_get_threads.restype = ctypes.c_int
+    lib.lao_rmsnorm_row.argtypes = [_f64p, ctypes.c_int, ctypes.c_double, _f32p, _f64p]
+    lib.lao_rope_row.argtypes = [_f64p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, _f64p]
+    lib.lao_prologue.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_int64, ctypes.c_double, ctypes.c_double, _f32p, _f64p]
+    common = [_f32p, _f32p, _f32p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+              ctypes.c_int64, ctypes.c_double, ctypes.c_double, _f32p, _f32p]
+    lib.lao_forward.argtypes = common + [_f64p, _f64p]
+    lib.lao_chunked.argtypes = common + [ctypes.c_int, _f64p, _f64p]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+@contextlib.contextmanager
+def use_library(path: str):
+    """Temporarily route every call of this module to another build of la_oracle.c
+    (used by the tests that plant mistakes in a copy of the oracle)."""
+    global _lib
+    saved = _load()
+    _lib = _bind(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _lib = saved
+
+
+def set_threads(n: int) -> None:
+    _load().lao_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(_load().lao_get_threads())
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _p32(a):
+    return None if a is None else a.ctypes.data_as(_f32p)
+
+
+def _p64(a):
+    return a.ctypes.data_as(_f64p)
+
+
+def rmsnorm_row(x, eps: float = 1e-6, w=None) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    w = None if w is None else _f32(w)
+    out = np.empty_like(x)
+    _load().lao_rmsnorm_row(_p64(x), x.shape[-1], float(eps), _p32(w), _p64(out))
+    return out
+
+
+def rope_row(x, pos: int, base: float = 10000.0) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    _load().lao_rope_row(_p64(x), x.shape[-1], int(pos), float(base), _p64(out))
+    return out
+
+
+def prologue(x, pos0: int = 0, base: float = 10000.0, eps: float = 1e-6, w=None) -> np.ndarray:
+    """RMSNorm then RoPE on a [B, T, H, D] tensor (token t at position pos0 + t)."""
+    x = _f32(x)
+    B, T, H, D = x.shape
+    w = None if w is None else _f32(w)
+    out = np.empty(x.shape, dtype=np.float64)
+    _load().lao_prologue(_p32(x), B, T, H, D, int(pos0), float(base), float(eps), _p32(w), _p64(out))
+    return out
+
+
+def _prep(q, k, v, g, S):
+    q, k, v, g = _f32(q), _f32(k), _f32(v), _f32(g)
+    B, T, H, D = q.shape
+    for a in (k, v, g):
+        assert a.shape == q.shape, (a.shape, q.shape)
+    St = np.zeros((B, H, D, D), np.float64) if S is None else np.array(S, dtype=np.float64, order="C")
+    assert St.shape == (B, H, D, D)
+    return q, k, v, g, St, (B, T, H, D)
+
+
+def forward(q, k, v, g, S=None, pos0: int = 0, base: float = 10000.0, eps: float = 1e-6,
+            q_w=None, k_w=None):
+    """Token-by-token recurrence.  Returns (o [B,T,H,D] f64, S_out [B,H,D,D] f64)."""
+    q, k, v, g, St, (B, T, H, D) = _prep(q, k, v, g, S)
+    q_w = None if q_w is None else _f32(q_w)
+    k_w = None if k_w is None else _f32(k_w)
+    o = np.empty((B, T, H, D), np.float64)
+    _load().lao_forward(_p32(q), _p32(k), _p32(v), _p32(g), B, T, H, D, int(pos0), float(base),
+                        float(eps), _p32(q_w), _p32(k_w), _p64(St), _p64(o))
+    return o, St
+
+
+def chunked(q, k, v, g, C: int, S=None, pos0: int = 0, base: float = 10000.0, eps: float = 1e-6,
+            q_w=None, k_w=None):
+    """Chunk-by-chunk form of the same layer.  Returns (o, S_out) in f64."""
+    q, k, v, g, St, (B, T, H, D) = _prep(q, k, v, g, S)
+    q_w = None if q_w is None else _f32(q_w)
+    k_w = None if k_w is None else _f32(k_w)
+    o = np.empty((B, T, H, D), np.float64)
+    _load().lao_chunked(_p32(q), _p32(k), _p32(v), _p32(g), B, T, H, D, int(pos0), float(base),
+                        float(eps), _p32(q_w), _p32(k_w), int(C), _p64(St), _p64(o))
+    return o, St
+
+
+def decode_step(q, k, v, g, S, pos: int, base: float = 10000.0, eps: float = 1e-6,
+                q_w=None, k_w=None):
+    """One token per sequence: q, k, v, g are [B, H, D]; S is [B, H, D, D].
+
+    Returns (o [B, H, D] f64, S_new [B, H, D, D] f64)."""
+    q, k, v, g = (np.asarray(a)[:, None] for a in (q, k, v, g))
+    o, S_new = forward(q, k, v, g, S=S, pos0=pos, base=base, eps=eps, q_w=q_w, k_w=k_w)
+    return o[:, 0], S_new

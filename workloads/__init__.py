@@ -1,0 +1,84 @@
+"""Seeded synthetic inputs for the linear-attention layer.
+
+This module only draws random numbers; it holds none of the layer's arithmetic.
+Both the HIP path's tests/benchmark and the oracle's checks take their inputs
+from here, so the two sides see identical data.
+
+Recipe (the pages measure whole-model latency on long prompts and quality on
+public suites; i.i.d. Gaussian tensors at the layer's real shapes stand in for
+them, since the layer has no data-dependent control flow):
+  * q, k, v, gate logits ~ N(0, 1), drawn in that order from one
+    ``torch.Generator`` seeded with the workload's seed, in float32, then rounded
+    to nearest-even bfloat16 (or kept float32 where the workload says so);
+  * the decode state S ~ N(0, 0.02^2) in float32, drawn after the activations;
+  * layout [B, T, H, D] for activations, [B, H, D, D] for states.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    seed: int
+    dtype: torch.dtype = torch.bfloat16
+    chunk: int = 0
+    pos0: int = 0
+    segments: int = 1
+    steps: int = 1
+    state_std: float = 0.0
+
+
+# The five workloads of the layer (tiny CPU check, 32K prefill, 256K prefill,
+# 1M streamed prefill, batched decode).  Seeds 0..4.
+TINY = Workload("tiny_b1_h2_d16_t256_fp32", 1, 256, 2, 16, seed=0, dtype=torch.float32, chunk=32)
+PREFILL_32K = Workload("prefill_b1_h32_d128_t32768", 1, 32768, 32, 128, seed=1)
+PREFILL_256K = Workload("prefill_b1_h32_d128_t262144", 1, 262144, 32, 128, seed=2)
+STREAM_1M = Workload("stream_b1_h32_d128_t1048576_seg65536", 1, 1048576, 32, 128, seed=3,
+                     segments=16)
+DECODE_B64 = Workload("decode_b64_h32_d128_pos262144", 64, 1, 32, 128, seed=4, pos0=262144,
+                      steps=1000, state_std=0.02)
+
+ALL = (TINY, PREFILL_32K, PREFILL_256K, STREAM_1M, DECODE_B64)
+
+
+def generator(seed: int, device="cpu") -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    return g
+
+
+def activations(B: int, T: int, H: int, D: int, seed: int, device="cpu",
+                dtype=torch.bfloat16, gen: torch.Generator | None = None):
+    """q, k, v, gate logits: [B, T, H, D], N(0, 1) drawn in fp32 then cast to ``dtype``."""
+    gen = gen if gen is not None else generator(seed, device)
+    out = []
+    for _ in range(4):
+        x = torch.randn((B, T, H, D), generator=gen, device=device, dtype=torch.float32)
+        out.append(x.to(dtype))
+        del x
+    return tuple(out)
+
+
+def state(B: int, H: int, D: int, std: float, gen: torch.Generator, device="cpu"):
+    """fp32 state [B, H, D, D] ~ N(0, std^2)."""
+    return torch.randn((B, H, D, D), generator=gen, device=device, dtype=torch.float32) * std
+
+
+def decode_inputs(w: Workload, steps: int | None = None, device="cpu"):
+    """(S0, q, k, v, g) for the batched-decode workload.
+
+    S0 [B, H, D, D] fp32 is drawn first, then q, k, v, g as [steps, B, H, D]
+    tensors (one token per sequence per step), each drawn whole, in that order."""
+    steps = w.steps if steps is None else steps
+    gen = generator(w.seed, device)
+    S0 = state(w.B, w.H, w.D, w.state_std, gen, device)
+    toks = activations(steps, w.B, w.H, w.D, w.seed, device, w.dtype, gen=gen)
+    return (S0,) + tuple(toks)
