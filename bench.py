@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X linear-attention layer (one GPU).
+
+One timed step = one la_prefill over the 256K-token workload (B = 1, 32 heads x
+128, bf16 q/k/v/gate, fp32 state, S0 = 0): QK-RMSNorm + RoPE prologue,
+intra-chunk masked scores and P V, inter-chunk Qh S_pre, the state scan and the
+sigmoid gate epilogue.  After the K timed prefill steps, the batched decode
+workload (64 sequences x 32 heads, 1000 consecutive steps from position 262144)
+is timed too and reported under "decode".  Inputs are generated on the GPU
+before any timed region; nothing is skipped inside it.
+
+Prints one JSON line (rank 0, N = 1):
+  value     prefill tokens/s (B * T * K / wall time of the K steps)
+  roofline  the dominant kernel (the chunk-output kernel) against HBM bandwidth,
+            from HIP events recorded on the library's stream around each kernel
+  cpu_baseline  the fp64 oracle timed on this host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 (256 CU x 2.4 GHz x 4096 flop/clk)
+TOKEN_HEAD_BYTES = 1280         # read q, k, v, gate (4 x 256 B) + write o (256 B)
+STATE_BYTES = 128 * 128 * 4     # one fp32 D x D state
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_output_kernel.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_linear_la_amd", "csrc", f)
+                  for f in ("la_prefill.hip", "la_device.hpp")]
+
+
+class HipEvents:
+    """hipEvent_t helpers through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        path = None
+        for line in open("/proc/self/maps"):
+            if "libamdhip64" in line:
+                path = line.split()[-1]
+                break
+        self.hip = ctypes.CDLL(path or "libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            out.append(ev.value)
+        return out
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) == 0
+
+    def ms(self, a, b):
+        assert self.hip.hipEventSynchronize(ctypes.c_void_p(b)) == 0
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return float(out.value)
+
+    def destroy(self, evs):
+        for ev in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(launch_tokens: int):
+    """HBM bytes per output-kernel launch from committed rocprofv3 counters, if they
+    were taken on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash() or rec.get("tokens") != launch_tokens:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def bench_prefill(la, torch, workloads, hip, args):
+    w = workloads.PREFILL_256K
+    B, T, H, D = w.B, w.T, w.H, w.D
+    q, k, v, g = workloads.activations(B, T, H, D, w.seed, "cuda")
+    o = torch.empty_like(q)
+    S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(la.prefill_workspace_bytes(B, T, H, D, args.chunk), dtype=torch.uint8, device="cuda")
+    plan_nseg = ws.numel() // (B * H * STATE_BYTES)
+    chunk = args.chunk or la.DEFAULT_CHUNK
+
+    for _ in range(args.warmup):
+        la.prefill(q, k, v, g, chunk=args.chunk, out=o, S_out=S_out, workspace=ws)
+    evs = [hip.create(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        la.prefill(q, k, v, g, chunk=args.chunk, out=o, S_out=S_out, workspace=ws, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ("chunk_state", "state_scan", "chunk_output")
+    per = {n: sum(hip.ms(e[i], e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    gpu_ms = sum(hip.ms(e[0], e[3]) for e in evs) / args.steps
+    for e in evs:
+        hip.destroy(e)
+
+    tokens = B * T
+    step_s = wall / args.steps
+    comp_bytes = TOKEN_HEAD_BYTES * B * T * H
+    out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
+    state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
+    scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
+    flops = (4 * D * D + 2 * D * (chunk + 1)) * B * T * H
+    out_s = per["chunk_output"] / 1e3
+    traffic = measured_traffic(tokens)
+    roofline = {
+        "bound": "hbm",
+        "kernel": "la_chunk_output_kernel",
+        "achieved": round(out_bytes / out_s / 1e9, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(out_bytes / out_s / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "algorithmic_bytes_per_launch": out_bytes,
+        "avg_launch_ms": round(per["chunk_output"], 4),
+    }
+    t_roof = comp_bytes / (HBM_PEAK_GBS * 1e9)
+    detail = {
+        "kernels_ms": {n: round(x, 4) for n, x in per.items()},
+        "kernels_GBps": {"chunk_state": round(state_bytes / (per["chunk_state"] / 1e3) / 1e9, 1),
+                         "state_scan": round(scan_bytes / (per["state_scan"] / 1e3) / 1e9, 1),
+                         "chunk_output": roofline["achieved"]},
+        "gpu_ms_per_step_events": round(gpu_ms, 4),
+        "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / step_s, 4),
+                          "compulsory_bytes": comp_bytes,
+                          "achieved_GBps": round(comp_bytes / step_s / 1e9, 1)},
+        "mfma": {"algorithmic_tflop": round(flops / 1e12, 4),
+                 "achieved_tflops": round(flops / step_s / 1e12, 2),
+                 "frac_of_bf16_peak": round(flops / step_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                 "ceiling_frac_at_hbm_roof": round(flops / t_roof / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "segments_per_head": plan_nseg,
+        "chunk": chunk,
+    }
+    return w, tokens * args.steps / wall, step_s, roofline, detail, (q, k, v, g)
+
+
+def bench_decode(la, torch, workloads, hip, args):
+    w = workloads.DECODE_B64
+    steps = args.decode_steps
+    S0, q, k, v, g = workloads.decode_inputs(w, steps=steps, device="cuda")
+    out = torch.empty_like(q)
+    S = S0.clone()
+    for n in range(min(3, steps)):  # warm-up on a scratch copy of the state
+        la.decode_step(q[n], k[n], v[n], g[n], S, w.pos0 + n, out=out[n])
+    S.copy_(S0)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(ev[0], stream)
+    for n in range(steps):
+        la.decode_step(q[n], k[n], v[n], g[n], S, w.pos0 + n, out=out[n])
+    hip.record(ev[1], stream)
+    ms = hip.ms(ev[0], ev[1])
+    hip.destroy(ev)
+    us = ms * 1e3 / steps
+    bytes_step = 2 * w.B * w.H * STATE_BYTES + 5 * w.B * w.H * w.D * 2
+    # the same steps captured in one HIP graph
+    graph_us = None
+    if not args.no_graph:
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for n in range(steps):
+                la.decode_step(q[n], k[n], v[n], g[n], S, w.pos0 + n, out=out[n])
+        S.copy_(S0)
+        torch.cuda.synchronize()
+        ev = hip.create(2)
+        stream = torch.cuda.current_stream().cuda_stream
+        hip.record(ev[0], stream)
+        graph.replay()
+        hip.record(ev[1], stream)
+        graph_us = hip.ms(ev[0], ev[1]) * 1e3 / steps
+        hip.destroy(ev)
+        del graph
+    best = min(us, graph_us) if graph_us else us
+    return {
+        "workload": w.name, "steps": steps, "us_per_step": round(us, 3),
+        "us_per_step_hipgraph": None if graph_us is None else round(graph_us, 3),
+        "GB_per_s": round(bytes_step / (best * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "la_decode_kernel",
+                     "achieved": round(bytes_step / (best * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(bytes_step / (best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": bytes_step,
+                     "note": "the 128 MiB state fits the 256 MB Infinity Cache; above 8 TB/s means cache-assisted"},
+    }
+
+
+def cpu_baseline(tensors, args):
+    """The oracle, untuned, on the first `cpu_tokens` tokens of the same input (all heads)."""
+    import oracle
+    q, k, v, g = tensors
+    n = args.cpu_tokens
+    host = [t[:, :n].float().cpu().numpy() for t in (q, k, v, g)]
+    t0 = time.perf_counter()
+    oracle.forward(*host)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 1), "unit": "tokens/s", "cores": oracle.get_threads(), "kind": "oracle",
+            "sample": f"first {n} tokens x {q.shape[2]} heads of the 256K-token prefill input "
+                      f"(fp64 token-by-token recurrence, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--cpu-tokens", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
+              "(heads and sequences shard with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import hybrid_sparse_linear_la_amd as la
+    import workloads
+
+    la.library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    hip = HipEvents()
+    w, tps, step_s, roofline, detail, tensors = bench_prefill(la, torch, workloads, hip, args)
+    decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
+    line = {
+        "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
+        "value": round(tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v/gate logits, S0 = 0)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "D": w.D,
+                   "chunk": detail["chunk"], "pos0": 0},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "prefill_detail": detail,
+        "decode": decode,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

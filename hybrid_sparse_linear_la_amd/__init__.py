@@ -1,0 +1,169 @@
+"""MI355X (gfx950) causal linear-attention ("Lightning Attention") layer.
+
+A thin ctypes binding over ``liblightning_la.so`` (C ABI in
+``include/lightning_la.h``).  This module only marshals arguments: it checks
+dtypes/shapes, allocates outputs and workspace with torch on the tensors' device
+and passes raw pointers plus the current HIP stream.  Every step of the layer
+runs in the library's HIP kernels; there is no fallback path.  If the library
+is missing, every call raises.
+
+    o, S_out = prefill(q, k, v, gate, S_in=None, pos0=0)
+    o = decode_step(q, k, v, gate, S, pos)        # S updated in place
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["prefill", "decode_step", "prefill_workspace_bytes", "LAError", "library", "lib_path",
+           "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "liblightning_la.so")
+
+HEAD_DIM = 128
+DEFAULT_CHUNK = 64
+SUPPORTED_CHUNKS = (0, 64)
+STATUS = {
+    0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
+    4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",
+}
+
+_vp = ctypes.c_void_p
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def library():
+    """Load liblightning_la.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise ImportError(f"{lib_path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(lib_path)
+        lib.la_version.restype = ctypes.c_int
+        lib.la_status_string.restype = ctypes.c_char_p
+        lib.la_status_string.argtypes = [ctypes.c_int]
+        lib.la_prefill_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_prefill_workspace_bytes.argtypes = [ctypes.c_int] * 5
+        lib.la_prefill.restype = ctypes.c_int
+        lib.la_prefill.argtypes = [_vp] * 7 + [ctypes.c_int] * 4 + [
+            ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp,
+            ctypes.c_size_t, _vp]
+        lib.la_prefill_profiled.restype = ctypes.c_int
+        lib.la_prefill_profiled.argtypes = lib.la_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p),
+                                                                      ctypes.c_int]
+        lib.la_decode_step.restype = ctypes.c_int
+        lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
+            ctypes.c_int64, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = library().la_status_string(status).decode()
+        raise LAError(status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _act(name, t, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != ndim or t.shape[-1] != HEAD_DIM:
+        raise ValueError(f"{name} must have {ndim} dims with last dim {HEAD_DIM}, got {tuple(t.shape)}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+
+
+def _f32(name, t, shape):
+    if t is None:
+        return
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 GPU tensor of shape {tuple(shape)}")
+
+
+def prefill_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, chunk: int = 0) -> int:
+    return int(library().la_prefill_workspace_bytes(B, T, H, D, chunk))
+
+
+def prefill(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: float = 10000.0,
+            rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None, out=None, S_out=None,
+            workspace=None, events=None):
+    """Chunked prefill.  q, k, v, gate: bf16 [B, T, H, 128] on the GPU.
+
+    Returns (o bf16 [B, T, H, 128], S_out fp32 [B, H, 128, 128]).  ``S_out`` may be
+    given (and may be ``S_in`` itself, for an in-place carry).  ``events``: four raw
+    hipEvent_t handles recorded around the library's three kernels (profiling)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+        _act(n, t, 4)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    B, T, H, D = q.shape
+    _f32("S_in", S_in, (B, H, D, D))
+    _f32("q_norm_w", q_norm_w, (D,))
+    _f32("k_norm_w", k_norm_w, (D,))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _act("out", out, 4)
+    if S_out is None:
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    else:
+        _f32("S_out", S_out, (B, H, D, D))
+    need = int(lib.la_prefill_workspace_bytes(B, T, H, D, chunk))
+    if need == 0:
+        status = 3 if (D != HEAD_DIM or chunk not in SUPPORTED_CHUNKS) else 2
+        raise LAError(status, lib.la_status_string(status).decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(S_out), _ptr(out),
+            B, T, H, D, int(pos0), int(chunk), float(rope_base), float(rms_eps),
+            _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device))
+    if events is None:
+        _check(lib.la_prefill(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check(lib.la_prefill_profiled(*args, arr, len(events)))
+    return out, S_out
+
+
+def decode_step(q, k, v, gate, S, pos: int, rope_base: float = 10000.0, rms_eps: float = 1e-6,
+                q_norm_w=None, k_norm_w=None, out=None):
+    """One decode step.  q, k, v, gate: bf16 [B, H, 128]; S: fp32 [B, H, 128, 128],
+    updated in place.  Returns o bf16 [B, H, 128]."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+        _act(n, t, 3)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    B, H, D = q.shape
+    _f32("S", S, (B, H, D, D))
+    _f32("q_norm_w", q_norm_w, (D,))
+    _f32("k_norm_w", k_norm_w, (D,))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _act("out", out, 3)
+    _check(lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S), _ptr(out), B, H, D,
+                              int(pos), float(rope_base), float(rms_eps), _ptr(q_norm_w),
+                              _ptr(k_norm_w), _stream(q.device)))
+    return out

@@ -1,0 +1,203 @@
+// C ABI of the linear-attention library: argument validation, work planning and
+// kernel launch.  Validation finishes before anything is enqueued, so every
+// error status leaves the outputs untouched.
+#include <math.h>
+#include <stdint.h>
+
+#include "la_internal.hpp"
+#include "lightning_la.h"
+
+namespace la {
+
+namespace {
+
+constexpr int kDefaultChunk = 64;
+// Workgroups a prefill launch aims for: a multiple of the 256 compute units, so
+// the chunk-walking workgroups fill the chip in whole rounds.
+constexpr int64_t kTargetWorkgroups = 1024;
+// Launch-size limits (grid.x * block.x must stay below 2^32 work-items).
+constexpr int64_t kMaxWorkgroups = (int64_t)1 << 23;
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, uint64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + (uintptr_t)bytes};
+}
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const Range x = range_of(a, na), y = range_of(b, nb);
+  return x.lo < y.hi && y.lo < x.hi;
+}
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+void rope_freqs(float base, RopeFreqs* f) {
+  for (int i = 0; i < kFreqs; ++i) f->theta[i] = pow((double)base, -2.0 * (double)i / (double)kHeadDim);
+}
+
+bool finite_positive(float x) { return isfinite(x) && x > 0.0f; }
+
+}  // namespace
+
+bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
+  if (B < 1 || T < 1 || H < 1) return false;
+  const int C = chunk == 0 ? kDefaultChunk : chunk;
+  if (C != 64) return false;
+  const int64_t bh = (int64_t)B * H;
+  const int64_t nchunks = ((int64_t)T + C - 1) / C;
+  int64_t cps = (bh * nchunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  if (cps < 1) cps = 1;
+  if (cps > nchunks) cps = nchunks;
+  const int64_t nseg = (nchunks + cps - 1) / cps;
+  if (bh * nseg > kMaxWorkgroups || bh > ((int64_t)1 << 20)) return false;
+  plan->C = C;
+  plan->nchunks = (int)nchunks;
+  plan->cps = (int)cps;
+  plan->nseg = (int)nseg;
+  plan->ws_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
+  return true;
+}
+
+}  // namespace la
+
+using namespace la;
+
+extern "C" {
+
+int la_version(void) { return 100; }
+
+const char* la_status_string(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL_PTR: return "LA_ERR_NULL_PTR: a required pointer is NULL";
+    case LA_ERR_BAD_SHAPE: return "LA_ERR_BAD_SHAPE: B, T and H must be >= 1 and the launch must fit";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: need D == 128, chunk in {0, 64}, rope_base > 0, rms_eps >= 0";
+    case LA_ERR_ALIGNMENT: return "LA_ERR_ALIGNMENT: pointers must be 16-byte aligned";
+    case LA_ERR_ALIASING: return "LA_ERR_ALIASING: an output overlaps another argument";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+    case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
+  }
+  return "unknown la_status";
+}
+
+size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk) {
+  PrefillPlan plan;
+  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan)) return 0;
+  return plan.ws_bytes;
+}
+
+static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                              const la_bf16* gate_logits, const float* S_in, float* S_out,
+                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
+                              float rope_base, float rms_eps, const float* q_norm_w,
+                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream, hipEvent_t const* events) {
+  if (!q || !k || !v || !gate_logits || !S_out || !o || !workspace) return LA_ERR_NULL_PTR;
+  if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64)) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+
+  const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
+  const void* ins[] = {q, k, v, gate_logits};
+  for (const void* in : ins) {
+    if (overlaps(o, act, in, act) || overlaps(S_out, st, in, act)) return LA_ERR_ALIASING;
+  }
+  if (overlaps(o, act, S_out, st) || overlaps(o, act, S_in, st)) return LA_ERR_ALIASING;
+  if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;
+  const void* all[] = {q, k, v, gate_logits, S_in, S_out, o};
+  for (const void* x : all)
+    if (overlaps(workspace, plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
+  if (workspace_bytes < plan.ws_bytes) return LA_ERR_WORKSPACE;
+
+  PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = gate_logits;
+  p.o = o;
+  p.ws = static_cast<float*>(workspace);
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.qw = q_norm_w;
+  p.kw = k_norm_w;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.nseg = plan.nseg;
+  p.cps = plan.cps;
+  p.pos0 = pos0;
+  p.eps = rms_eps;
+  rope_freqs(rope_base, &p.freqs);
+  return launch_prefill(p, plan, static_cast<hipStream_t>(stream), events) == hipSuccess ? LA_OK
+                                                                                     : LA_ERR_HIP;
+}
+
+la_status la_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                     const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
+                     int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
+                     float rms_eps, const float* q_norm_w, const float* k_norm_w,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
+                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream, nullptr);
+}
+
+la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                              const la_bf16* gate_logits, const float* S_in, float* S_out,
+                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
+                              float rope_base, float rms_eps, const float* q_norm_w,
+                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events) {
+  if (!events || n_events != 4) return LA_ERR_NULL_PTR;
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return LA_ERR_NULL_PTR;
+  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
+                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t const*>(events));
+}
+
+la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                         const la_bf16* gate_logits, float* S, la_bf16* o, int B, int H, int D,
+                         int64_t pos, float rope_base, float rms_eps, const float* q_norm_w,
+                         const float* k_norm_w, void* stream) {
+  if (!q || !k || !v || !gate_logits || !S || !o) return LA_ERR_NULL_PTR;
+  if (B < 1 || H < 1 || (int64_t)B * H > ((int64_t)1 << 30)) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  const void* ptrs[] = {q, k, v, gate_logits, S, o, q_norm_w, k_norm_w};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const uint64_t act = (uint64_t)B * H * D * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
+  const void* ins[] = {q, k, v, gate_logits};
+  for (const void* in : ins)
+    if (overlaps(o, act, in, act) || overlaps(S, st, in, act)) return LA_ERR_ALIASING;
+  if (overlaps(o, act, S, st)) return LA_ERR_ALIASING;
+
+  DecodeParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = gate_logits;
+  p.o = o;
+  p.S = S;
+  p.qw = q_norm_w;
+  p.kw = k_norm_w;
+  p.B = B;
+  p.H = H;
+  p.pos = pos;
+  p.eps = rms_eps;
+  rope_freqs(rope_base, &p.freqs);
+  return launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+}  // extern "C"

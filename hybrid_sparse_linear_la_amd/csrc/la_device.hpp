@@ -1,0 +1,92 @@
+// Device-side building blocks of the gfx950 linear-attention kernels: bf16
+// conversion, the 16x16x32 bf16 MFMA, XOR-swizzled LDS tile addressing and the
+// RoPE rotation with a double-precision angle reduction.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kD = 128;     // head dimension (D_k = D_v)
+constexpr int kHalf = 64;   // RoPE frequencies per head (rotate-half pairs)
+
+typedef short bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf2f(uint32_t h16) { return __uint_as_float(h16 << 16); }
+__device__ __forceinline__ float bf2f_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bf16 (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
+// Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for
+// e = 0..7, and receives D[4 (l / 16) + r][l % 16] for r = 0..3.
+__device__ __forceinline__ f32x4 mma(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ bf16x8 as_bf16x8(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Pack two accumulator tiles (4 rows each) into one 8-element bf16 operand.
+__device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
+  return __builtin_bit_cast(bf16x8, make_uint4(pack2(a[0], a[1]), pack2(a[2], a[3]),
+                                               pack2(b[0], b[1]), pack2(b[2], b[3])));
+}
+
+// ---------------------------------------------------------------------------
+// LDS tiles, bf16, with the 16-byte block index XOR-swizzled so that both the
+// 16-byte MFMA operand reads and the staging writes spread over all banks.
+//
+// Row tile [rows][128] (q, k, gate logits, output staging): element (t, d).
+__device__ __forceinline__ int row_off(int t, int d) {
+  return t * (kD * 2) + ((((d >> 3) ^ (t & 7))) << 4) + ((d & 7) << 1);
+}
+// Transposed tile [128][C] (k^T, v^T): element (d, t); C is a multiple of 64.
+template <int C>
+__device__ __forceinline__ int col_off(int d, int t) {
+  return d * (C * 2) + ((((t >> 3) ^ ((d >> 1) & 7))) << 4) + ((t & 7) << 1);
+}
+// Score tile [C][C]: element (t, s).
+template <int C>
+__device__ __forceinline__ int score_off(int t, int s) {
+  return t * (C * 2) + ((((s >> 3) ^ (t & 7))) << 4) + ((s & 7) << 1);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const uint8_t* base, int off) {
+  return *reinterpret_cast<const T*>(base + off);
+}
+template <typename T>
+__device__ __forceinline__ void lds_st(uint8_t* base, int off, T v) {
+  *reinterpret_cast<T*>(base + off) = v;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE rotation e^{i p theta} for an integer position p: the angle p * theta is
+// formed and reduced modulo 2 pi in double precision (error ~1e-10 rad for p up
+// to millions), then cos/sin of the reduced angle are taken in float.
+__device__ __forceinline__ float2 rope_rotation(int64_t p, double theta) {
+  const double a = (double)p * theta;
+  const double kk = rint(a * 0.15915494309189535);       // round(a / 2 pi)
+  const double r = fma(-kk, 6.283185307179586, a);        // a - 2 pi kk, |r| <= pi
+  float s, c;
+  sincosf((float)r, &s, &c);
+  return make_float2(c, s);
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace la

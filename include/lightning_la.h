@@ -1,0 +1,134 @@
+/*
+ * lightning_la.h -- C ABI of the MI355X (gfx950) causal linear-attention
+ * ("Lightning Attention") layer: chunked prefill and single-token decode.
+ *
+ * The layer (per batch element b and head h, tokens t at absolute positions
+ * pos0 + t):
+ *   qh_t = RoPE(RMSNorm(q_t)), kh_t = RoPE(RMSNorm(k_t))     (v is not normalized)
+ *   S_t  = S_{t-1} + kh_t v_t^T                               (fp32 state, D x D)
+ *   o_t  = sigmoid(g_t) * (qh_t S_t)                          (elementwise gate)
+ *
+ * Sources (pages cited by title and section):
+ *   - State update S_t = S_{t-1} + k_t v_t^T: "MiniCPM-SALA: Hybridizing Sparse and
+ *     Linear Attention for Efficient Long-Context Modeling" (paper digest),
+ *     前置知识 > 线性注意力 (Linear Attention).
+ *   - QK-normalization, MHA heads (GQA converted to MHA), output gating on the
+ *     linear layers: "創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B模型"
+ *     (MiniCPM-SALA technical-report rendering), 04 技術報告 > 02 模型架構 >
+ *     (3) 線性注意力模塊; also "9B端側開源模型跑通百萬上下文，面壁全新稀疏-線性混合
+ *     注意力" (QbitAI article), architecture section.
+ *   - RoPE kept on the linear layers (HyPE): technical-report rendering,
+ *     02 模型架構 > (4) 混合位置編碼.
+ * Readings where the pages are silent: the readout o_t = q_t S_t sees token t
+ * itself; no decay, feature map, normalizing denominator or 1/sqrt(D) scale;
+ * RMSNorm n_i = w_i x_i / sqrt(mean(x^2) + eps) over the head dimension;
+ * rotate-half RoPE pairing (i, i + D/2) with theta_i = rope_base^(-2i/D) applied
+ * after the norm; the gate is sigmoid of per-element logits of o's shape and
+ * never touches S.
+ *
+ * Layouts (row-major, no padding):
+ *   q, k, v, gate logits, o : bf16 [B, T, H, D]   (decode: [B, H, D])
+ *   S_in, S_out, S          : fp32 [B, H, D, D], S[i][j] = sum_t kh_t[i] v_t[j]
+ *   q_norm_w, k_norm_w      : fp32 [D], or NULL for all-ones weights
+ * Supported: D == 128, B, H >= 1, T >= 1, chunk in {0 (= default), 64}.
+ *
+ * Ownership and asynchrony: every pointer (except where noted) is a device
+ * pointer owned by the caller.  The library allocates no memory and keeps no
+ * mutable global state; calls are re-entrant.  A call validates its arguments,
+ * enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = the
+ * null stream) and returns; results are valid once the caller synchronizes
+ * that stream.
+ *
+ * Errors: all validation happens before anything is enqueued; on any status
+ * other than LA_OK nothing was launched and no output was touched (except
+ * LA_ERR_HIP, returned when a launch itself fails; device faults surface at
+ * the caller's synchronization).  No C++ exception crosses this interface.
+ */
+#ifndef LIGHTNING_LA_H
+#define LIGHTNING_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                              */
+  LA_ERR_BAD_SHAPE = 2,   /* B, T or H < 1, or a size product overflows               */
+  LA_ERR_UNSUPPORTED = 3, /* D != 128, or chunk not in {0, 64}                        */
+  LA_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned                          */
+  LA_ERR_ALIASING = 5,    /* o overlaps an input, or S_out overlaps an activation      */
+  LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_prefill_workspace_bytes */
+  LA_ERR_HIP = 7          /* a kernel launch failed                                    */
+} la_status;
+
+typedef uint16_t la_bf16; /* raw bfloat16 bits */
+
+/* Version of this interface (major * 10000 + minor * 100 + patch). */
+int la_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* la_status_string(la_status s);
+
+/*
+ * Bytes of device workspace la_prefill needs for this shape and chunk (0 for an
+ * invalid shape).  The workspace holds one fp32 D x D state per (b, h, segment),
+ * where a segment is a run of consecutive chunks handled by one workgroup.
+ */
+size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk);
+
+/*
+ * Chunked prefill over T tokens starting at absolute position pos0.
+ *   q, k, v, gate_logits : [B, T, H, D] bf16 inputs.
+ *   S_in  : [B, H, D, D] fp32 initial state, or NULL for zeros.  May equal S_out
+ *           (in-place carry between segments of a long sequence).
+ *   S_out : [B, H, D, D] fp32 final state (the state after token T - 1).
+ *   o     : [B, T, H, D] bf16 gated output; must not overlap any input.
+ *   chunk : tokens per chunk of the chunked evaluation (0 = default, 64).
+ *   rope_base : RoPE base (10000 in the workloads); rms_eps : RMSNorm epsilon.
+ *   workspace : device buffer of at least la_prefill_workspace_bytes(...) bytes;
+ *               its contents on entry are irrelevant and are clobbered.
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; fp32 state; RMSNorm,
+ * RoPE and gate in fp32 with RoPE angles reduced in double precision.
+ */
+la_status la_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                     const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
+                     int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
+                     float rms_eps, const float* q_norm_w, const float* k_norm_w,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * la_prefill that also records caller-created HIP events (hipEvent_t passed as
+ * void*) on `stream` at its kernel boundaries, for per-kernel timing:
+ *   events[0] before the chunk-state kernel, events[1] before the state scan,
+ *   events[2] before the output kernel, events[3] after the output kernel.
+ * n_events must be 4 and every event non-NULL (else LA_ERR_NULL_PTR); the
+ * results are identical to la_prefill's.
+ */
+la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                              const la_bf16* gate_logits, const float* S_in, float* S_out,
+                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
+                              float rope_base, float rms_eps, const float* q_norm_w,
+                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events);
+
+/*
+ * One decode step: one token per sequence at absolute position pos.
+ *   q, k, v, gate_logits : [B, H, D] bf16.
+ *   S : [B, H, D, D] fp32 state, updated in place (S += kh v^T).
+ *   o : [B, H, D] bf16 gated output, o = sigmoid(g) * (qh S_new).
+ * Arithmetic: fp32 throughout (no rounding of qh, kh or S to bf16).
+ */
+la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                         const la_bf16* gate_logits, float* S, la_bf16* o, int B, int H, int D,
+                         int64_t pos, float rope_base, float rms_eps, const float* q_norm_w,
+                         const float* k_norm_w, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_LA_H */

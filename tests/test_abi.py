@@ -1,0 +1,113 @@
+"""The C-ABI library loads, exports every function include/lightning_la.h declares,
+and rejects bad arguments before touching the GPU.  CPU only: every call here
+fails validation, so no kernel is launched and no pointer is dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lightning_la.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import hybrid_sparse_linear_la_amd as la
+    return la.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
+         "la_decode_step"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.la_version() == 100
+
+
+def test_status_strings(lib):
+    for s, name in ((0, b"LA_OK"), (1, b"LA_ERR_NULL_PTR"), (2, b"LA_ERR_BAD_SHAPE"), (3, b"LA_ERR_UNSUPPORTED"),
+                    (4, b"LA_ERR_ALIGNMENT"), (5, b"LA_ERR_ALIASING"), (6, b"LA_ERR_WORKSPACE"), (7, b"LA_ERR_HIP")):
+        assert lib.la_status_string(s).startswith(name)
+    assert lib.la_status_string(99) == b"unknown la_status"
+
+
+def test_workspace_bytes(lib):
+    # one fp32 128x128 state per (b, h, segment); segments target ~1024 workgroups
+    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 0) == 32 * 32 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 32768, 32, 128, 64) == 32 * 32 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 0) == 2 * 5 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 64, 0) == 0
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 96) == 0
+    assert lib.la_prefill_workspace_bytes(0, 300, 2, 128, 0) == 0
+
+
+# fake, never-dereferenced device addresses (validation fails before any use)
+A = 1 << 40
+MB = 1 << 20
+
+
+def _prefill(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, g=A + 192 * MB, S_in=None, S_out=A + 256 * MB,
+             o=A + 320 * MB, B=1, T=64, H=2, D=128, pos0=0, chunk=0, base=10000.0, eps=1e-6, qw=None,
+             kw=None, ws=A + 384 * MB, ws_bytes=1 << 30):
+    vp = ctypes.c_void_p
+    return lib.la_prefill(vp(q), vp(k), vp(v), vp(g), vp(S_in), vp(S_out), vp(o), B, T, H, D, pos0, chunk,
+                          base, eps, vp(qw), vp(kw), vp(ws), ws_bytes, None)
+
+
+def test_prefill_validation(lib):
+    import hybrid_sparse_linear_la_amd  # noqa: F401  (argtypes set by library())
+    assert _prefill(lib, q=None) == 1
+    assert _prefill(lib, ws=None) == 1
+    assert _prefill(lib, S_out=None) == 1
+    assert _prefill(lib, B=0) == 2
+    assert _prefill(lib, T=0) == 2
+    assert _prefill(lib, H=-1) == 2
+    assert _prefill(lib, D=64) == 3
+    assert _prefill(lib, chunk=32) == 3
+    assert _prefill(lib, base=0.0) == 3
+    assert _prefill(lib, eps=-1.0) == 3
+    assert _prefill(lib, eps=float("nan")) == 3
+    assert _prefill(lib, q=A + 8) == 4
+    assert _prefill(lib, qw=A + 1000 * MB + 4) == 4
+    assert _prefill(lib, o=A + 32) == 5                  # o overlaps q
+    assert _prefill(lib, S_out=A + 64 * MB + 1024) == 5  # S_out overlaps k
+    assert _prefill(lib, S_in=A + 256 * MB + 16, S_out=A + 256 * MB) == 5  # partial overlap
+    assert _prefill(lib, ws=A + 320 * MB + 64) == 5      # workspace overlaps o
+    assert _prefill(lib, ws_bytes=1024) == 6
+
+
+def _decode(lib, q=A, k=A + MB, v=A + 2 * MB, g=A + 3 * MB, S=A + 4 * MB, o=A + 512 * MB, B=2, H=2,
+            D=128, pos=0, base=10000.0, eps=1e-6):
+    vp = ctypes.c_void_p
+    return lib.la_decode_step(vp(q), vp(k), vp(v), vp(g), vp(S), vp(o), B, H, D, pos, base, eps, None, None,
+                              None)
+
+
+def test_decode_validation(lib):
+    import hybrid_sparse_linear_la_amd  # noqa: F401
+    assert _decode(lib, S=None) == 1
+    assert _decode(lib, B=0) == 2
+    assert _decode(lib, D=256) == 3
+    assert _decode(lib, base=-2.0) == 3
+    assert _decode(lib, v=A + 2 * MB + 2) == 4
+    assert _decode(lib, o=A + 256) == 5        # o overlaps q
+    assert _decode(lib, S=A + 3 * MB) == 5     # S overlaps g
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    import hybrid_sparse_linear_la_amd as la
+    monkeypatch.setattr(la, "_lib", None)
+    monkeypatch.setattr(la, "lib_path", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        la.library()

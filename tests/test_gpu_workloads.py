@@ -1,0 +1,124 @@
+"""GPU parity at the layer's full workload sizes, in the launch configuration the
+benchmark times (default chunk, B = 1, 32 heads x 128):
+
+  * 32K-token prefill: every output and the final state against the oracle;
+  * 256K-token prefill: all outputs and states of sampled heads against the oracle
+    (the oracle is chunk independent, so it runs once);
+  * 1M tokens streamed as 16 segments of 65536 with S carried in place: equal to
+    one single-shot call, and sampled heads against the oracle streamed segment by
+    segment;
+  * batched decode (64 sequences x 32 heads, 1000 steps from position 262144):
+    o at every step and S after steps 1, 10 and 1000 against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_o_close, assert_S_close, o_row_errors, s_errors, to_np, to_np32
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def la():
+    import hybrid_sparse_linear_la_amd as la
+    la.library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return la
+
+
+def _head(t, h):
+    """[B, T, H, D] GPU tensor -> float32 numpy [B, T, 1, D] of head h."""
+    return to_np32(t[:, :, h:h + 1])
+
+
+def test_prefill_32k_all_heads(la):
+    w = workloads.PREFILL_32K
+    print(f"workload {w.name}", flush=True)
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, D, w.seed, "cuda")
+    o, S = la.prefill(q, k, v, g)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.forward(to_np32(q), to_np32(k), to_np32(v), to_np32(g))
+    eo = assert_o_close(to_np(o), o_ref)
+    es = assert_S_close(to_np(S), S_ref)
+    print(f"32K parity o {eo} S {es}", flush=True)
+
+
+def test_prefill_256k_sampled_heads(la):
+    w = workloads.PREFILL_256K
+    print(f"workload {w.name}", flush=True)
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, D, w.seed, "cuda")
+    o, S = la.prefill(q, k, v, g)
+    torch.cuda.synchronize()
+    for h in (0, 21):
+        o_ref, S_ref = oracle.forward(_head(q, h), _head(k, h), _head(v, h), _head(g, h))
+        eo = assert_o_close(to_np(o[:, :, h:h + 1]), o_ref, what=f"o head {h}")
+        es = assert_S_close(to_np(S[:, h:h + 1]), S_ref, what=f"S head {h}")
+        print(f"256K head {h} parity o {eo} S {es}", flush=True)
+
+
+def test_stream_1m_segmented_equals_single_shot(la):
+    w = workloads.STREAM_1M
+    print(f"workload {w.name}", flush=True)
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, D, w.seed, "cuda")
+    o1, S1 = la.prefill(q, k, v, g)
+    seg = w.T // w.segments
+    S = torch.zeros((w.B, w.H, D, D), dtype=torch.float32, device="cuda")
+    o2 = torch.empty_like(q)
+    ws = torch.empty(la.prefill_workspace_bytes(w.B, seg, w.H), dtype=torch.uint8, device="cuda")
+    for s in range(w.segments):
+        sl = slice(s * seg, (s + 1) * seg)
+        la.prefill(q[:, sl], k[:, sl], v[:, sl], g[:, sl], S_in=S, S_out=S, pos0=s * seg, out=o2[:, sl],
+                   workspace=ws)
+    torch.cuda.synchronize()
+    # segmented and single-shot differ only in fp32 summation order of the carried state
+    e = o_row_errors(to_np(o2[:, -seg:]), to_np(o1[:, -seg:]))
+    assert e["max"] <= 2e-2, e
+    es = s_errors(to_np(S), to_np(S1))
+    assert es["fro"] <= 1e-3, es
+    print(f"1M segmented vs single-shot: o {e} S {es}", flush=True)
+    # sampled head against the oracle, streamed segment by segment (host memory bounded)
+    h = 5
+    S_ref = None
+    worst = 0.0
+    for s in range(w.segments):
+        sl = slice(s * seg, (s + 1) * seg)
+        o_ref, S_ref = oracle.forward(to_np32(q[:, sl, h:h + 1]), to_np32(k[:, sl, h:h + 1]),
+                                      to_np32(v[:, sl, h:h + 1]), to_np32(g[:, sl, h:h + 1]),
+                                      S=S_ref, pos0=s * seg)
+        eo = assert_o_close(to_np(o2[:, sl, h:h + 1]), o_ref, what=f"o segment {s}")
+        worst = max(worst, eo["max"])
+    es = assert_S_close(to_np(S[:, h:h + 1]), S_ref, what="S after 1M tokens")
+    print(f"1M head {h} vs oracle: worst segment o row error {worst:.3e}, S {es}", flush=True)
+
+
+def test_decode_b64_1000_steps(la):
+    w = workloads.DECODE_B64
+    print(f"workload {w.name}", flush=True)
+    S0, q, k, v, g = workloads.decode_inputs(w, device="cuda")
+    S = S0.clone()
+    outs = torch.empty_like(q)
+    snaps = {}
+    for n in range(w.steps):
+        la.decode_step(q[n], k[n], v[n], g[n], S, w.pos0 + n, out=outs[n])
+        if n + 1 in (1, 10):
+            snaps[n + 1] = to_np(S)
+    torch.cuda.synchronize()
+    snaps[w.steps] = None
+    S0_np = to_np(S0)
+    # S after 1 and 10 steps: every sequence
+    for n in (1, 10):
+        _, S_ref = oracle.forward(to_np32(q[:n].transpose(0, 1)), to_np32(k[:n].transpose(0, 1)),
+                                  to_np32(v[:n].transpose(0, 1)), to_np32(g[:n].transpose(0, 1)),
+                                  S=S0_np, pos0=w.pos0)
+        assert_S_close(snaps[n], S_ref, what=f"S after step {n}")
+    # o at every step and S after 1000 steps: sampled sequences
+    bs = [0, 31, 63]
+    sel = lambda t: to_np32(t[:, bs].transpose(0, 1))  # noqa: E731  [3, steps, H, D]
+    o_ref, S_ref = oracle.forward(sel(q), sel(k), sel(v), sel(g), S=S0_np[bs], pos0=w.pos0)
+    eo = assert_o_close(to_np(outs[:, bs].transpose(0, 1)), o_ref, what="o over 1000 steps")
+    es = assert_S_close(to_np(S[bs]), S_ref, what="S after 1000 steps")
+    print(f"decode parity o {eo} S {es}", flush=True)
