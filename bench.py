@@ -237,6 +237,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one plain device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer's path runs on a single MI355X "
@@ -253,6 +256,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hip = HipEvents()
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w, tps, step_s, roofline, detail, tensors = bench_prefill(la, torch, workloads, hip, args)
     decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)

@@ -36,7 +36,9 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 void rope_freqs(float base, RopeFreqs* f) {
-  for (int i = 0; i < kFreqs; ++i) f->theta[i] = pow((double)base, -2.0 * (double)i / (double)kHeadDim);
+  const double two_pi = 6.283185307179586476925287;
+  for (int i = 0; i < kFreqs; ++i)
+    f->rev[i] = pow((double)base, -2.0 * (double)i / (double)kHeadDim) / two_pi;
 }
 
 bool finite_positive(float x) { return isfinite(x) && x > 0.0f; }

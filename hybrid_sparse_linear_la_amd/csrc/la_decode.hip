@@ -50,12 +50,12 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
       ssq += __shfl_xor(ssq, off);
       ssk += __shfl_xor(ssk, off);
     }
-    const float iq = rsqrtf(ssq * (1.0f / kD) + p.eps), ik = rsqrtf(ssk * (1.0f / kD) + p.eps);
+    const float iq = rsqrt_(ssq * (1.0f / kD) + p.eps), ik = rsqrt_(ssk * (1.0f / kD) + p.eps);
     q0 *= iq * (p.qw ? p.qw[i] : 1.f);
     q1 *= iq * (p.qw ? p.qw[i + kHalf] : 1.f);
     k0 *= ik * (p.kw ? p.kw[i] : 1.f);
     k1 *= ik * (p.kw ? p.kw[i + kHalf] : 1.f);
-    const float2 rot = rope_rotation(p.pos, p.freqs.theta[i]);
+    const float2 rot = rope_rotation(p.pos, p.freqs.rev[i]);
     sq[i] = q0 * rot.x - q1 * rot.y;
     sq[i + kHalf] = q1 * rot.x + q0 * rot.y;
     sk[i] = k0 * rot.x - k1 * rot.y;

@@ -71,22 +71,27 @@ __device__ __forceinline__ void lds_st(uint8_t* base, int off, T v) {
 }
 
 // ---------------------------------------------------------------------------
-// RoPE rotation e^{i p theta} for an integer position p: the angle p * theta is
-// formed and reduced modulo 2 pi in double precision (error ~1e-10 rad for p up
-// to millions), then cos/sin of the reduced angle are taken in float.
-__device__ __forceinline__ float2 rope_rotation(int64_t p, double theta) {
-  const double a = (double)p * theta;
-  const double kk = rint(a * 0.15915494309189535);       // round(a / 2 pi)
-  const double r = fma(-kk, 6.283185307179586, a);        // a - 2 pi kk, |r| <= pi
-  float s, c;
-  sincosf((float)r, &s, &c);
-  return make_float2(c, s);
+// RoPE rotation e^{i p theta} for an integer position p.  The angle is carried in
+// revolutions: rev = p * (theta / 2 pi) is formed in double precision and reduced
+// to [-1/2, 1/2] (error ~1e-11 revolutions for p up to millions); the hardware
+// sine/cosine (argument in revolutions) then act on the small reduced value.
+__device__ __forceinline__ float2 rope_rotation(int64_t p, double rev_per_pos) {
+  double rev = (double)p * rev_per_pos;
+  rev -= rint(rev);
+  const float r = (float)rev;
+  return make_float2(__builtin_amdgcn_cosf(r), __builtin_amdgcn_sinf(r));
 }
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.y * b.x + a.x * b.y);
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// sigmoid(x) = 1 / (1 + e^{-x}) with the hardware exp and reciprocal (~1 ulp each).
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// 1 / sqrt(x) (hardware reciprocal square root, ~1 ulp).
+__device__ __forceinline__ float rsqrt_(float x) { return __builtin_amdgcn_rsqf(x); }
 
 }  // namespace la

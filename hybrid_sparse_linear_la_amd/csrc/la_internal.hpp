@@ -11,9 +11,10 @@ namespace la {
 constexpr int kHeadDim = 128;
 constexpr int kFreqs = 64;
 
-// RoPE inverse frequencies theta_i = base^(-2i/D), computed on the host in double.
+// RoPE frequencies in revolutions per position, rev_i = base^(-2i/D) / (2 pi),
+// computed on the host in double.
 struct RopeFreqs {
-  double theta[kFreqs];
+  double rev[kFreqs];
 };
 
 // How one prefill call is cut up: T tokens -> chunks of C tokens -> segments of
