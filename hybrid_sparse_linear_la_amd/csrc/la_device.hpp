@@ -22,7 +22,26 @@ __device__ __forceinline__ float bf2f_hi(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ uint32_t f2bf(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
-__device__ __forceinline__ uint32_t pack2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs, fp32 accumulate.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc,
+                                         false);
+}
+
+// Two floats -> packed f16 (round toward zero), and back.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
 
 // D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
 // Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for

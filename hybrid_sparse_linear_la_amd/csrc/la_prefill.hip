@@ -14,18 +14,25 @@
 //   2. la_state_scan_kernel  : per state element, exclusive prefix over segments
 //      (plus S_in) in place, and the final state -> S_out.
 //   3. la_chunk_output_kernel: one workgroup per (b, h, segment) starts from its
-//      segment's prefix state and walks the chunks: QK-RMSNorm + RoPE prologue
-//      into LDS, masked scores, O^T = S^T Qh^T + V^T P^T, sigmoid gate, coalesced
-//      bf16 store, then S += Kh^T V.
+//      segment's prefix state and walks the chunks.  Four producer waves load
+//      chunk c+1, apply QK-RMSNorm + RoPE to q, k and the sigmoid to the gate,
+//      and stage the tiles into one half of a ping-pong LDS buffer, while four
+//      consumer waves run all the MFMA work of chunk c from the other half:
+//      O^T = S^T Qh^T + V^T P^T with P^T = masked Kh Qh^T, the gate multiply,
+//      the bf16 store of o, and S += Kh^T V.  One barrier per chunk.
 //
-// Workgroup: 512 threads = 8 waves (two per SIMD).  Wave w owns value columns
-// [16w, 16w + 16) of S and of the chunk output.  S stays in MFMA accumulators:
-// an accumulator tile pair is the A operand of S^T Qh^T directly, with the key
-// dims of the contraction taken in the order pi(8g + e) = 32kk + 4g + 16(e/4) +
-// e%4 (lane group g = lane / 16, operand element e), and Qh read in that order.
-// The token contractions (Kh^T V and V^T P^T) use the same order over tokens, and
-// their "transposed" operands come straight from the row-major tiles through
-// ds_read_b64_tr_b16, so no tile is ever written transposed.
+// MFMA layouts (v_mfma_f32_16x16x32_bf16; lane l = 16 g + n16 supplies
+// A[n16][8g + e], B[8g + e][n16] and holds D[4g + r][n16]):
+//   * a consumer wave owns value columns [32w, 32w + 32) of S; S stays in
+//     accumulators, and an accumulator tile pair is the A operand of S^T Qh^T
+//     directly when the key dims of the contraction are taken in the order
+//     pi(8g + e) = 32kk + 4g + 16(e/4) + e%4, with Qh read in that order;
+//   * the score tiles P^T (lane holds 4 consecutive keys of one query) pair up
+//     into the B operand of V^T P^T with the same order over keys, so P never
+//     goes through LDS;
+//   * the token contractions take their "transposed" operands (V^T, Kh^T)
+//     straight from the row-major tiles through ds_read_b64_tr_b16, so no tile
+//     is ever written transposed.
 #include "la_device.hpp"
 #include "la_internal.hpp"
 
@@ -35,20 +42,17 @@ namespace {
 constexpr int kC = 64;      // tokens per chunk
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTileBytes = kC * kD * 2;  // one [64][128] bf16 tile
-constexpr int kExactRows = 16;           // rows whose scores use the hi/lo split
+constexpr int kRowBytes = kD * 2 + 16;     // 128 bf16 + 16 bytes of padding
+constexpr int kTileBytes = kC * kRowBytes;  // one [64][128] bf16 tile
+constexpr int kExactRows = 16;              // rows whose scores use the hi/lo split
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
-// [64][128] bf16 row tile, 256-byte rows; the 16-byte block index is XORed with
-// t & 15, which spreads every access pattern below over all banks.
-__device__ __forceinline__ int tile_off(int t, int d) {
-  return t * (kD * 2) + ((((d >> 3) ^ (t & 15))) << 4) + ((d & 7) << 1);
-}
-// [64][64] bf16 score tile, 128-byte rows; block index XORed with (t >> 1) & 7.
-__device__ __forceinline__ int score_off(int t, int s) {
-  return t * (kC * 2) + ((((s >> 3) ^ ((t >> 1) & 7))) << 4) + ((s & 7) << 1);
-}
+// [64][128] bf16 row tile with 272-byte rows: consecutive rows start 16 bytes
+// apart in the bank space, so the 8-byte operand reads (16 rows x 4 lane
+// groups), the transposed reads (4 rows x 4 groups) and the staging writes all
+// spread over the banks, and every offset is linear (immediate offsets).
+__device__ __forceinline__ int tile_off(int t, int d) { return t * kRowBytes + 2 * d; }
 
 // Transposed read: within each 16-lane group, lane L supplies the address of 4
 // bf16 and receives element L of each of the 4 rows formed by lanes 4r..4r+3.
@@ -69,110 +73,152 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-// Staging coordinates: thread (rg = tid / 16, j = tid % 16) holds rows rg and
-// rg + 32 of a chunk, dims {4j..4j+3} U {64+4j..64+4j+3}: each RoPE pair (i,
-// i + 64) sits in one thread, and 16 lanes cover a row.
+// Staging coordinates: a thread (rg, j) holds rows rg + kStep m (m < M) of a
+// chunk and dims {4j..4j+3} U {64+4j..64+4j+3}: each RoPE pair (i, i + 64) sits
+// in one thread, and 16 consecutive lanes cover a row.
+template <int M>
 struct Rows {
-  uint2 lo[2];  // dims 4j..4j+3, four bf16
-  uint2 hi[2];  // dims 64+4j..64+4j+3
+  uint2 lo[M];  // dims 4j..4j+3, four bf16
+  uint2 hi[M];  // dims 64+4j..64+4j+3
 };
 
 // Unmasked, branch-free loads: rows at or beyond nvalid (>= 1) re-read the last
 // valid row, keeping every address inside the tensor.  Such rows of q, k and the
 // gate only reach masked scores and unstored outputs; v's are zeroed when staged.
+template <int M, int kStep>
 __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, int64_t rs, int nvalid,
-                                          int rg, int j, Rows& R) {
+                                          int rg, int j, Rows<M>& R) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const uint16_t* src = base + (int64_t)min(rg + 32 * m, nvalid - 1) * rs;
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* src = base + (int64_t)min(rg + kStep * m, nvalid - 1) * rs;
     R.lo[m] = *reinterpret_cast<const uint2*>(src + 4 * j);
     R.hi[m] = *reinterpret_cast<const uint2*>(src + kHalf + 4 * j);
   }
 }
 
-__device__ __forceinline__ void store_rows(uint8_t* tile, const Rows& R, int rg, int j) {
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    lds_st<uint2>(tile, tile_off(rg + 32 * m, 4 * j), R.lo[m]);
-    lds_st<uint2>(tile, tile_off(rg + 32 * m, kHalf + 4 * j), R.hi[m]);
-  }
-}
-
-__device__ __forceinline__ void store_rows_masked(uint8_t* tile, const Rows& R, int nvalid, int rg,
+template <int M, int kStep>
+__device__ __forceinline__ void store_rows_masked(uint8_t* tile, const Rows<M>& R, int nvalid, int rg,
                                                   int j) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const bool ok = rg + 32 * m < nvalid;
-    lds_st<uint2>(tile, tile_off(rg + 32 * m, 4 * j), ok ? R.lo[m] : make_uint2(0u, 0u));
-    lds_st<uint2>(tile, tile_off(rg + 32 * m, kHalf + 4 * j), ok ? R.hi[m] : make_uint2(0u, 0u));
+  for (int m = 0; m < M; ++m) {
+    const bool ok = rg + kStep * m < nvalid;
+    lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), ok ? R.lo[m] : make_uint2(0u, 0u));
+    lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), ok ? R.hi[m] : make_uint2(0u, 0u));
   }
 }
 
-// RoPE per thread: A[e] = e^{i rg theta}, Z[e] = e^{i 32 theta} for the thread's
-// frequencies 4j+e; row rg + 32m of a chunk at position p0 is rotated by
-// base(p0) * A * Z^m.  base_rev is the frequency of pair tid (tid < 64), for the
-// per-chunk base rotation, kept in a register so the loop loads nothing for it.
+// sigmoid of the gate logits, staged as f16 (the value lies in (0, 1); f16 keeps
+// 11 significant bits, round toward zero).
+template <int M, int kStep>
+__device__ __forceinline__ void sigmoid_stage(uint8_t* tile, const Rows<M>& R, int rg, int j) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint2 a = R.lo[m], b = R.hi[m];
+    const uint2 lo = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(a.x)), sigmoidf_(bf2f_hi(a.x))),
+                                pack_f16x2(sigmoidf_(bf2f_lo(a.y)), sigmoidf_(bf2f_hi(a.y))));
+    const uint2 hi = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(b.x)), sigmoidf_(bf2f_hi(b.x))),
+                                pack_f16x2(sigmoidf_(bf2f_lo(b.y)), sigmoidf_(bf2f_hi(b.y))));
+    lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), lo);
+    lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), hi);
+  }
+}
+
+// RoPE per thread: A[e] = e^{i rg theta}, Z[e] = e^{i kStep theta} for the
+// thread's frequencies 4j+e; row rg + kStep m of a chunk at position p0 is
+// rotated by base(p0) * A * Z^m.  base_rev is the frequency of pair i = tid % 64,
+// for the per-chunk base rotation, kept in a register so the loop loads nothing.
 struct Rope {
   float2 A[4];
   float2 Z[4];
   double base_rev;
 };
 
+template <int kStep>
 __device__ __forceinline__ void rope_init(const PrefillParams& p, int tid, int rg, int j, Rope& L) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const double rv = p.freqs.rev[4 * j + e];
     L.A[e] = rope_rotation(rg, rv);
-    L.Z[e] = rope_rotation(32, rv);
+    L.Z[e] = rope_rotation(kStep, rv);
   }
   L.base_rev = p.freqs.rev[tid & (kHalf - 1)];
 }
 
-// QK-normalization (RMSNorm over the 128 dims of a row, weights w) followed by
-// rotate-half RoPE, in fp32; the bf16 result goes to `tile`.  With `lo` set, rows
-// below kExactRows also store lo = bf16(y - bf16(y)) into `lo`, for the scores
-// of the first rows of a call.
+// QK-normalization (RMSNorm over the 128 dims of row t, weights w) followed by
+// rotate-half RoPE with rotations E, in fp32; the bf16 result goes to `tile`.
+// With `lo` set, rows below kExactRows also store lo = bf16(y - bf16(y)) into
+// `lo`, for the scores of the first rows of a call.
 template <bool kWeights>
-__device__ __forceinline__ void norm_rope_stage(const Rows& R, const float (&w)[8], float eps,
-                                                const float2* sRot, const Rope& L, int rg, int j,
-                                                uint8_t* tile, uint8_t* lo) {
-  float2 E[4];
+__device__ __forceinline__ void norm_rope_row(uint2 rl, uint2 rh, const float (&w)[8], float eps,
+                                              const float2 (&E)[4], int t, int j, uint8_t* tile,
+                                              uint8_t* lo) {
+  const float ss = dot2_bf16(rh.y, rh.y, dot2_bf16(rh.x, rh.x, dot2_bf16(rl.y, rl.y, dot2_bf16(rl.x, rl.x, 0.f))));
+  const float inv = rsqrt_(row16_sum(ss) * (1.0f / kD) + eps);
+  const float x[8] = {bf2f_lo(rl.x), bf2f_hi(rl.x), bf2f_lo(rl.y), bf2f_hi(rl.y),
+                      bf2f_lo(rh.x), bf2f_hi(rh.x), bf2f_lo(rh.y), bf2f_hi(rh.y)};
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = kWeights ? x[e] * w[e] : x[e];
+    const float b = kWeights ? x[4 + e] * w[4 + e] : x[4 + e];
+    const float c = E[e].x * inv, s = E[e].y * inv;
+    y[e] = fmaf(a, c, -b * s);
+    y[4 + e] = fmaf(b, c, a * s);
+  }
+  const uint2 hlo = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
+  const uint2 hhi = make_uint2(pack2(y[4], y[5]), pack2(y[6], y[7]));
+  lds_st<uint2>(tile, tile_off(t, 4 * j), hlo);
+  lds_st<uint2>(tile, tile_off(t, kHalf + 4 * j), hhi);
+  if (lo != nullptr && t < kExactRows) {
+    const uint2 llo = make_uint2(pack2(y[0] - bf2f_lo(hlo.x), y[1] - bf2f_hi(hlo.x)),
+                                 pack2(y[2] - bf2f_lo(hlo.y), y[3] - bf2f_hi(hlo.y)));
+    const uint2 lhi = make_uint2(pack2(y[4] - bf2f_lo(hhi.x), y[5] - bf2f_hi(hhi.x)),
+                                 pack2(y[6] - bf2f_lo(hhi.y), y[7] - bf2f_hi(hhi.y)));
+    lds_st<uint2>(lo, tile_off(t, 4 * j), llo);
+    lds_st<uint2>(lo, tile_off(t, kHalf + 4 * j), lhi);
+  }
+}
+
+// Rotations of the thread's rows rg + kStep m at its frequencies 4j + e, from the
+// chunk's base rotations sRot: E_0 = sRot * A, E_m = E_{m-1} * Z.
+template <int kStep>
+__device__ __forceinline__ void first_rotation(const float2* sRot, const Rope& L, int j, float2 (&E)[4]) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) E[e] = cmul(sRot[4 * j + e], L.A[e]);
+}
+__device__ __forceinline__ void next_rotation(const Rope& L, float2 (&E)[4]) {
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    if (m == 1) {
+  for (int e = 0; e < 4; ++e) E[e] = cmul(E[e], L.Z[e]);
+}
+
+// One tensor (k in the state kernel).
+template <bool kWeights, int M, int kStep>
+__device__ __forceinline__ void norm_rope_stage(const Rows<M>& R, const float (&w)[8], float eps,
+                                                const float2* sRot, const Rope& L, int rg, int j,
+                                                uint8_t* tile) {
+  float2 E[4];
+  first_rotation<kStep>(sRot, L, j, E);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) E[e] = cmul(E[e], L.Z[e]);
-    }
-    float x[8] = {bf2f_lo(R.lo[m].x), bf2f_hi(R.lo[m].x), bf2f_lo(R.lo[m].y), bf2f_hi(R.lo[m].y),
-                  bf2f_lo(R.hi[m].x), bf2f_hi(R.hi[m].x), bf2f_lo(R.hi[m].y), bf2f_hi(R.hi[m].y)};
-    float ss = 0.f;
+  for (int m = 0; m < M; ++m) {
+    if (m > 0) next_rotation(L, E);
+    norm_rope_row<kWeights>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, nullptr);
+  }
+}
+
+// q and k of the same rows share one rotation chain.
+template <bool kWeights, int M, int kStep>
+__device__ __forceinline__ void norm_rope_stage_qk(const Rows<M>& Qr, const Rows<M>& Kr, const float (&wq)[8],
+                                                   const float (&wk)[8], float eps, const float2* sRot,
+                                                   const Rope& L, int rg, int j, uint8_t* tq, uint8_t* tk,
+                                                   uint8_t* lq, uint8_t* lk) {
+  float2 E[4];
+  first_rotation<kStep>(sRot, L, j, E);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-    const float inv = rsqrt_(row16_sum(ss) * (1.0f / kD) + eps);
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float a = kWeights ? x[e] * w[e] : x[e];
-      const float b = kWeights ? x[4 + e] * w[4 + e] : x[4 + e];
-      const float c = E[e].x * inv, s = E[e].y * inv;
-      y[e] = fmaf(a, c, -b * s);
-      y[4 + e] = fmaf(b, c, a * s);
-    }
-    const uint2 hlo = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
-    const uint2 hhi = make_uint2(pack2(y[4], y[5]), pack2(y[6], y[7]));
-    const int t = rg + 32 * m;
-    lds_st<uint2>(tile, tile_off(t, 4 * j), hlo);
-    lds_st<uint2>(tile, tile_off(t, kHalf + 4 * j), hhi);
-    if (lo != nullptr && t < kExactRows) {
-      const uint2 llo = make_uint2(pack2(y[0] - bf2f_lo(hlo.x), y[1] - bf2f_hi(hlo.x)),
-                                   pack2(y[2] - bf2f_lo(hlo.y), y[3] - bf2f_hi(hlo.y)));
-      const uint2 lhi = make_uint2(pack2(y[4] - bf2f_lo(hhi.x), y[5] - bf2f_hi(hhi.x)),
-                                   pack2(y[6] - bf2f_lo(hhi.y), y[7] - bf2f_hi(hhi.y)));
-      lds_st<uint2>(lo, tile_off(t, 4 * j), llo);
-      lds_st<uint2>(lo, tile_off(t, kHalf + 4 * j), lhi);
-    }
+  for (int m = 0; m < M; ++m) {
+    if (m > 0) next_rotation(L, E);
+    const int t = rg + kStep * m;
+    norm_rope_row<kWeights>(Qr.lo[m], Qr.hi[m], wq, eps, E, t, j, tq, lq);
+    norm_rope_row<kWeights>(Kr.lo[m], Kr.hi[m], wk, eps, E, t, j, tk, lk);
   }
 }
 
@@ -209,9 +255,9 @@ __device__ __forceinline__ int64_t state_elem(int rtk, int r, int w, int g4, int
   return (int64_t)(16 * rtk + 4 * g4 + r) * kD + 16 * w + n16;
 }
 
-// Token-contraction operand of V: lane n16 gets V[32kk + 4g + 16(e/4) + e%4][16w + n16].
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int kk, int w, int g4, int n16) {
-  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = 16 * w + 4 * (n16 & 3);
+// Token-contraction operand of V: lane n16 gets V[32kk + 4g + 16(e/4) + e%4][c0 + n16].
+__device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int kk, int c0, int g4, int n16) {
+  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
   return as_bf16x8(lds_tr(sV, tile_off(t0, c)), lds_tr(sV, tile_off(t0 + 16, c)));
 }
 
@@ -248,17 +294,17 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
   float wk[8];
   load_norm_weights(p.kw, j, wk);
   Rope L;
-  rope_init(p, tid, rg, j, L);
+  rope_init<32>(p, tid, rg, j, L);
 
   f32x4 Sacc[8];
 #pragma unroll
   for (int a = 0; a < 8; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Rows Kr, Vr;
+  Rows<2> Kr, Vr;
   {
     const int nv = min(kC, tl.t_end - tl.t_begin);
-    load_rows(p.k + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Kr);
-    load_rows(p.v + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Vr);
+    load_rows<2, 32>(p.k + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Kr);
+    load_rows<2, 32>(p.v + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Vr);
   }
   if (tid < kHalf) sRot[0][tid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
   __syncthreads();
@@ -268,19 +314,19 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
     const int nv = min(kC, tl.t_end - t0);
     uint8_t* bK = sK[c & 1];
     uint8_t* bV = sV[c & 1];
-    norm_rope_stage<kWeights>(Kr, wk, p.eps, sRot[c & 1], L, rg, j, bK, nullptr);
-    store_rows_masked(bV, Vr, nv, rg, j);
+    norm_rope_stage<kWeights, 2, 32>(Kr, wk, p.eps, sRot[c & 1], L, rg, j, bK);
+    store_rows_masked<2, 32>(bV, Vr, nv, rg, j);
     if (c + 1 < tl.nch) {
       const int t1 = t0 + kC;
       const int nv1 = min(kC, tl.t_end - t1);
-      load_rows(p.k + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Kr);
-      load_rows(p.v + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Vr);
+      load_rows<2, 32>(p.k + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Kr);
+      load_rows<2, 32>(p.v + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Vr);
       if (tid < kHalf) sRot[(c + 1) & 1][tid] = rope_rotation(p.pos0 + t1, L.base_rev);
     }
     __syncthreads();
     bf16x8 Vop[2];
-    Vop[0] = v_operand(bV, 0, w, g4, n16);
-    Vop[1] = v_operand(bV, 1, w, g4, n16);
+    Vop[0] = v_operand(bV, 0, 16 * w, g4, n16);
+    Vop[1] = v_operand(bV, 1, 16 * w, g4, n16);
     accumulate_state(Sacc, bK, Vop, g4, n16);
   }
 
@@ -313,169 +359,213 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
 }
 
 // --------------------------------------------------------------------------
-// Score tiles (row block rt, column block st <= rt) of a chunk, dealt to the 8
-// waves (waves 0 and 1 take two): tile idx has rt = (kTileRT >> 2 idx) & 3 and
-// st = (kTileST >> 2 idx) & 3 for the order (0,0) (1,1) (2,2) (3,3) (1,0) (2,1)
-// (3,2) (2,0) (3,1) (3,0).  Packed in immediates so no table is loaded.
-constexpr uint32_t kTileRT = 0xfb9e4;
-constexpr uint32_t kTileST = 0x124e4;
+// Output kernel.  Threads 0..255 are the consumer waves (wave w owns value
+// columns [32w, 32w + 32)); threads 256..511 are the producer waves (thread
+// (rg, j) stages rows rg + 16m, m < 4).  Both roles run their own loop with the
+// same number of barriers: one before the loop, one after the first staging and
+// one per chunk.
+constexpr int kConsumers = 256;
+
+// Consumer operand in key order pi: lane n16 gets X[row][32kk + 4g + 16(e/4) + e%4].
+__device__ __forceinline__ bf16x8 pi_operand(const uint8_t* tile, int row, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint2>(tile, tile_off(row, 32 * kk + 4 * g4)),
+                   lds_ld<uint2>(tile, tile_off(row, 32 * kk + 16 + 4 * g4)));
+}
 
 template <bool kWeights>
-__global__ __launch_bounds__(kThreads) void la_chunk_output_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sK[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sG[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sO[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kC * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kD * 2];
-  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kD * 2];
-  __shared__ float2 sRot[2][kHalf];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
-  const int j = tid & 15, rg = tid >> 4;
-  const Tile tl = decode_tile(p);
+__device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, uint8_t (*sQ)[kTileBytes],
+                                        uint8_t (*sK)[kTileBytes], uint8_t (*sV)[kTileBytes],
+                                        uint8_t (*sG)[kTileBytes], uint8_t* sQl, uint8_t* sKl,
+                                        float2 (*sRot)[kHalf]) {
+  const int ptid = threadIdx.x - kConsumers;
+  const int j = ptid & 15, rg = ptid >> 4;
   const int64_t rs = (int64_t)p.H * kD;
-
   float wq[8], wk[8];
   load_norm_weights(p.qw, j, wq);
   load_norm_weights(p.kw, j, wk);
   Rope L;
-  rope_init(p, tid, rg, j, L);
+  rope_init<16>(p, ptid, rg, j, L);
+  Rows<4> Qr, Kr, Vr, Gr;
+  auto load_chunk = [&](int c) {
+    const int t = tl.t_begin + c * kC;
+    const int nv = min(kC, tl.t_end - t);
+    const int64_t off = tl.base + (int64_t)t * rs;
+    load_rows<4, 16>(p.q + off, rs, nv, rg, j, Qr);
+    load_rows<4, 16>(p.k + off, rs, nv, rg, j, Kr);
+    load_rows<4, 16>(p.v + off, rs, nv, rg, j, Vr);
+    load_rows<4, 16>(p.g + off, rs, nv, rg, j, Gr);
+  };
+  auto stage_chunk = [&](int c) {
+    const int b = c & 1;
+    const int nv = min(kC, tl.t_end - (tl.t_begin + c * kC));
+    const bool exact = tl.seg == 0 && c == 0;
+    norm_rope_stage_qk<kWeights, 4, 16>(Qr, Kr, wq, wk, p.eps, sRot[b], L, rg, j, sQ[b], sK[b],
+                                        exact ? sQl : nullptr, exact ? sKl : nullptr);
+    store_rows_masked<4, 16>(sV[b], Vr, nv, rg, j);
+    sigmoid_stage<4, 16>(sG[b], Gr, rg, j);
+  };
 
-  // prefix state of this segment
-  f32x4 Sacc[8];
+  load_chunk(0);
+  if (ptid < kHalf) {
+    sRot[0][ptid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
+    if (tl.nch > 1) sRot[1][ptid] = rope_rotation(p.pos0 + tl.t_begin + kC, L.base_rev);
+  }
+  __syncthreads();
+  stage_chunk(0);
+  if (tl.nch > 1) load_chunk(1);
+  __syncthreads();
+  for (int c = 0; c < tl.nch; ++c) {
+    if (c + 1 < tl.nch) {
+      stage_chunk(c + 1);
+      if (c + 2 < tl.nch) {
+        load_chunk(c + 2);
+        if (ptid < kHalf)
+          sRot[c & 1][ptid] = rope_rotation(p.pos0 + tl.t_begin + (c + 2) * kC, L.base_rev);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, uint8_t (*sQ)[kTileBytes],
+                                        uint8_t (*sK)[kTileBytes], uint8_t (*sV)[kTileBytes],
+                                        uint8_t (*sG)[kTileBytes], const uint8_t* sQl,
+                                        const uint8_t* sKl) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int64_t rs = (int64_t)p.H * kD;
+
+  // prefix state of this segment: S[:, 32w + 16 dt .. + 16) in accumulator tiles
+  f32x4 Sacc[2][8];
   {
     const float* src = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
 #pragma unroll
-    for (int rtk = 0; rtk < 8; ++rtk)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[rtk][r] = src[state_elem(rtk, r, w, g4, n16)];
+      for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sacc[dt][rtk][r] = src[state_elem(rtk, r, 2 * w + dt, g4, n16)];
   }
-  // score tiles above the diagonal are never written: zero them once
-  for (int i = tid; i < kC * kC * 2 / 16; i += kThreads)
-    reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
-
-  Rows Qr, Kr, Vr, Gr;
-  {
-    const int nv = min(kC, tl.t_end - tl.t_begin);
-    const int64_t off = tl.base + (int64_t)tl.t_begin * rs;
-    load_rows(p.q + off, rs, nv, rg, j, Qr);
-    load_rows(p.k + off, rs, nv, rg, j, Kr);
-    load_rows(p.v + off, rs, nv, rg, j, Vr);
-    load_rows(p.g + off, rs, nv, rg, j, Gr);
-  }
-  if (tid < kHalf) sRot[0][tid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
+  // this lane's output pointer at chunk-relative row n16, column 32 w + 4 g
+  uint16_t* const obase = p.o + tl.base + (int64_t)n16 * rs + 32 * w + 4 * g4;
+  __syncthreads();
   __syncthreads();
 
   for (int c = 0; c < tl.nch; ++c) {
+    const int b = c & 1;
+    const uint8_t* Q = sQ[b];
+    const uint8_t* K = sK[b];
+    const uint8_t* V = sV[b];
+    const uint8_t* G = sG[b];
     const int t0 = tl.t_begin + c * kC;
     const int nv = min(kC, tl.t_end - t0);
-    // The first chunk of a call forms the scores of its first rows from a hi/lo
-    // split of qh and kh: those rows sum only a few scores, so the bf16 rounding
-    // of qh, kh would otherwise dominate their error.
-    const bool exact = (tl.seg == 0 && c == 0);
+    // The first chunk of a call forms the scores of its first 16 rows from a
+    // hi/lo split of qh and kh: those rows sum only a few scores, so the bf16
+    // rounding of qh, kh would otherwise dominate their error.
+    const bool exact = tl.seg == 0 && c == 0;
 
-    // ---- prologue: RMSNorm + RoPE of q and k, staging of all four inputs
-    norm_rope_stage<kWeights>(Qr, wq, p.eps, sRot[c & 1], L, rg, j, sQ, exact ? sQl : nullptr);
-    norm_rope_stage<kWeights>(Kr, wk, p.eps, sRot[c & 1], L, rg, j, sK, exact ? sKl : nullptr);
-    store_rows_masked(sV, Vr, nv, rg, j);
-    store_rows(sG, Gr, rg, j);
-    if (c + 1 < tl.nch) {
-      const int t1 = t0 + kC;
-      const int nv1 = min(kC, tl.t_end - t1);
-      const int64_t off = tl.base + (int64_t)t1 * rs;
-      load_rows(p.q + off, rs, nv1, rg, j, Qr);
-      load_rows(p.k + off, rs, nv1, rg, j, Kr);
-      load_rows(p.v + off, rs, nv1, rg, j, Vr);
-      load_rows(p.g + off, rs, nv1, rg, j, Gr);
-      if (tid < kHalf) sRot[(c + 1) & 1][tid] = rope_rotation(p.pos0 + t1, L.base_rev);
-    }
-    __syncthreads();
+    bf16x8 SA[2][4];  // S_pre^T as A operand (bf16), key dims in order pi
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) SA[dt][kk] = pack8(Sacc[dt][2 * kk], Sacc[dt][2 * kk + 1]);
+    bf16x8 Vf[2][2];  // V^T (token order pi), columns 32w + 16 dt + n16
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) Vf[dt][kk] = v_operand(V, kk, 32 * w + 16 * dt, g4, n16);
 
-    // ---- masked scores P^T = Kh Qh^T (lane holds 4 consecutive keys s of one
-    // query t), stored as P[t][s] in bf16
-    for (int idx = w; idx < 10; idx += kWaves) {
-      const int rt = (kTileRT >> (2 * idx)) & 3, st = (kTileST >> (2 * idx)) & 3;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kD / 32; ++ks) {
-        const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
-        const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
-        const bf16x8 kh = as_bf16x8(lds_ld<uint4>(sK, ka));
-        const bf16x8 qh = as_bf16x8(lds_ld<uint4>(sQ, qa));
-        if (exact && idx == 0) {  // tile (0, 0): add the lo cross terms
-          acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qh, acc);
-          acc = mma(kh, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
-        }
-        acc = mma(kh, qh, acc);
-      }
-      if (st == rt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g4 + r > n16) acc[r] = 0.f;
-      }
-      lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
-                    make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
-    }
-
-    // ---- inter-chunk term O^T = S_pre^T Qh^T (S_pre in bf16, key dims in order pi)
-    f32x4 Oacc[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < kD / 32; ++kk) {
-      const bf16x8 a = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int t = 16 * rt + n16;
-        const bf16x8 b = as_bf16x8(lds_ld<uint2>(sQ, tile_off(t, 32 * kk + 4 * g4)),
-                                   lds_ld<uint2>(sQ, tile_off(t, 32 * kk + 16 + 4 * g4)));
-        Oacc[rt] = mma(a, b, Oacc[rt]);
-      }
-    }
-    __syncthreads();  // scores complete
-
-    // ---- intra-chunk term O^T += V^T P^T (tokens in order pi)
-    bf16x8 Vop[2];
-    Vop[0] = v_operand(sV, 0, w, g4, n16);
-    Vop[1] = v_operand(sV, 1, w, g4, n16);
+    f32x4 Oacc[2][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       const int t = 16 * rt + n16;
+      bf16x8 Qf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) Qf[kk] = pi_operand(Q, t, kk, g4);
+      // inter-chunk term O^T = S_pre^T Qh^T
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        Oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Oacc[dt][rt] = mma(SA[dt][kk], Qf[kk], Oacc[dt][rt]);
+      }
+      // masked scores P^T = Kh Qh^T for key blocks st <= rt
+      f32x4 Pt[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        Pt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (st > rt) continue;
+        const int s = 16 * st + n16;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 kf = pi_operand(K, s, kk, g4);
+          if (rt == 0 && exact) {  // tile (0, 0) of the first chunk: add the lo cross terms
+            Pt[st] = mma(pi_operand(sKl, s, kk, g4), Qf[kk], Pt[st]);
+            Pt[st] = mma(kf, pi_operand(sQl, t, kk, g4), Pt[st]);
+          }
+          Pt[st] = mma(kf, Qf[kk], Pt[st]);
+        }
+        if (st == rt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (4 * g4 + r > n16) Pt[st][r] = 0.f;
+        }
+      }
+      // intra-chunk term O^T += V^T P^T; score tiles pair up into B operands
 #pragma unroll
       for (int kk = 0; kk <= rt / 2; ++kk) {
-        const bf16x8 b = as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
-                                   lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
-        Oacc[rt] = mma(Vop[kk], b, Oacc[rt]);
+        const bf16x8 pb = pack8(Pt[2 * kk], Pt[2 * kk + 1]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) Oacc[dt][rt] = mma(Vf[dt][kk], pb, Oacc[dt][rt]);
       }
     }
 
-    // ---- state carry S_pre += Kh^T V
-    accumulate_state(Sacc, sK, Vop, g4, n16);
+    // state carry S_pre += Kh^T V
+#pragma unroll
+    for (int kk = 0; kk < kC / 32; ++kk) {
+      const int tr0 = 32 * kk + 4 * g4 + (n16 >> 2);
+#pragma unroll
+      for (int rtk = 0; rtk < 8; ++rtk) {
+        const int col = 16 * rtk + 4 * (n16 & 3);
+        const bf16x8 a = as_bf16x8(lds_tr(K, tile_off(tr0, col)), lds_tr(K, tile_off(tr0 + 16, col)));
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) Sacc[dt][rtk] = mma(a, Vf[dt][kk], Sacc[dt][rtk]);
+      }
+    }
 
-    // ---- gate epilogue: lane holds o[t = 16 rt + n16][16 w + 4 g .. + 3]
+    // gate and store: lane holds o[16 rt + n16][32 w + 16 dt + 4 g .. + 3]
+    uint16_t* orow = obase + (int64_t)t0 * rs;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const int off = tile_off(16 * rt + n16, 16 * w + 4 * g4);
-      const uint2 gl = lds_ld<uint2>(sG, off);
-      const float o0 = Oacc[rt][0] * sigmoidf_(bf2f_lo(gl.x));
-      const float o1 = Oacc[rt][1] * sigmoidf_(bf2f_hi(gl.x));
-      const float o2 = Oacc[rt][2] * sigmoidf_(bf2f_lo(gl.y));
-      const float o3 = Oacc[rt][3] * sigmoidf_(bf2f_hi(gl.y));
-      lds_st<uint2>(sO, off, make_uint2(pack2(o0, o1), pack2(o2, o3)));
-    }
-    __syncthreads();
+      const int t = 16 * rt + n16;
+      uint16_t* dst = orow + (int64_t)(16 * rt) * rs;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int row = (tid >> 4) + 32 * pass, blk = tid & 15;
-      if (row < nv) {
-        const uint4 val = lds_ld<uint4>(sO, tile_off(row, 8 * blk));
-        *reinterpret_cast<uint4*>(p.o + tl.base + (int64_t)(t0 + row) * rs + 8 * blk) = val;
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint2 sg = lds_ld<uint2>(G, tile_off(t, 32 * w + 16 * dt + 4 * g4));
+        const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * f16_lo(sg.x), Oacc[dt][rt][1] * f16_hi(sg.x)),
+                                     pack2(Oacc[dt][rt][2] * f16_lo(sg.y), Oacc[dt][rt][3] * f16_hi(sg.y)));
+        if (t < nv) *reinterpret_cast<uint2*>(dst + 16 * dt) = out;
       }
     }
+    __syncthreads();
   }
+}
+
+template <bool kWeights>
+__global__ __launch_bounds__(kThreads) void la_chunk_output_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), f16
+  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
+  __shared__ float2 sRot[2][kHalf];
+
+  const Tile tl = decode_tile(p);
+  if (threadIdx.x >= kConsumers)
+    produce<kWeights>(p, tl, sQ, sK, sV, sG, sQl, sKl, sRot);
+  else
+    consume(p, tl, sQ, sK, sV, sG, sQl, sKl);
 }
 
 }  // namespace
