@@ -364,7 +364,9 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
 // (rg, j) stages rows rg + 16m, m < 4).  Both roles run their own loop with the
 // same number of barriers: one before the loop, one after the first staging and
 // one per chunk.
-constexpr int kConsumers = 256;
+constexpr int kConsumers = 256;               // 4 consumer waves
+constexpr int kProducers = 512;               // 8 producer waves
+constexpr int kOutThreads = kConsumers + kProducers;
 
 // Consumer operand in key order pi: lane n16 gets X[row][32kk + 4g + 16(e/4) + e%4].
 __device__ __forceinline__ bf16x8 pi_operand(const uint8_t* tile, int row, int kk, int g4) {
@@ -384,25 +386,29 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   load_norm_weights(p.qw, j, wq);
   load_norm_weights(p.kw, j, wk);
   Rope L;
-  rope_init<16>(p, ptid, rg, j, L);
-  Rows<4> Qr, Kr, Vr, Gr;
+  rope_init<32>(p, ptid, rg, j, L);
+  Rows<2> Qr, Kr, Vr, Gr;
   auto load_chunk = [&](int c) {
     const int t = tl.t_begin + c * kC;
     const int nv = min(kC, tl.t_end - t);
     const int64_t off = tl.base + (int64_t)t * rs;
-    load_rows<4, 16>(p.q + off, rs, nv, rg, j, Qr);
-    load_rows<4, 16>(p.k + off, rs, nv, rg, j, Kr);
-    load_rows<4, 16>(p.v + off, rs, nv, rg, j, Vr);
-    load_rows<4, 16>(p.g + off, rs, nv, rg, j, Gr);
+    load_rows<2, 32>(p.q + off, rs, nv, rg, j, Qr);
+    load_rows<2, 32>(p.k + off, rs, nv, rg, j, Kr);
+    load_rows<2, 32>(p.v + off, rs, nv, rg, j, Vr);
+    load_rows<2, 32>(p.g + off, rs, nv, rg, j, Gr);
   };
-  auto stage_chunk = [&](int c) {
+  // phase A of a chunk's staging: qh, kh; phase B: v, sigmoid(gate)
+  auto stage_qk = [&](int c) {
+    const int b = c & 1;
+    const bool exact = tl.seg == 0 && c == 0;
+    norm_rope_stage_qk<kWeights, 2, 32>(Qr, Kr, wq, wk, p.eps, sRot[b], L, rg, j, sQ[b], sK[b],
+                                        exact ? sQl : nullptr, exact ? sKl : nullptr);
+  };
+  auto stage_vg = [&](int c) {
     const int b = c & 1;
     const int nv = min(kC, tl.t_end - (tl.t_begin + c * kC));
-    const bool exact = tl.seg == 0 && c == 0;
-    norm_rope_stage_qk<kWeights, 4, 16>(Qr, Kr, wq, wk, p.eps, sRot[b], L, rg, j, sQ[b], sK[b],
-                                        exact ? sQl : nullptr, exact ? sKl : nullptr);
-    store_rows_masked<4, 16>(sV[b], Vr, nv, rg, j);
-    sigmoid_stage<4, 16>(sG[b], Gr, rg, j);
+    store_rows_masked<2, 32>(sV[b], Vr, nv, rg, j);
+    sigmoid_stage<2, 32>(sG[b], Gr, rg, j);
   };
 
   load_chunk(0);
@@ -411,12 +417,16 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
     if (tl.nch > 1) sRot[1][ptid] = rope_rotation(p.pos0 + tl.t_begin + kC, L.base_rev);
   }
   __syncthreads();
-  stage_chunk(0);
+  stage_qk(0);
+  stage_vg(0);
   if (tl.nch > 1) load_chunk(1);
   __syncthreads();
   for (int c = 0; c < tl.nch; ++c) {
-    if (c + 1 < tl.nch) {
-      stage_chunk(c + 1);
+    const bool next = c + 1 < tl.nch;
+    if (next) stage_qk(c + 1);
+    __syncthreads();
+    if (next) {
+      stage_vg(c + 1);
       if (c + 2 < tl.nch) {
         load_chunk(c + 2);
         if (ptid < kHalf)
@@ -427,10 +437,111 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   }
 }
 
+// Score tiles (row block rt, key block st <= rt) of a chunk dealt to the 4 consumer
+// waves (3/3/2/2): tile idx has rt = (kTileRT >> 2 idx) & 3, st = (kTileST >> 2 idx)
+// & 3 for the order (0,0) (1,1) (2,2) (3,3) (1,0) (2,1) (3,2) (2,0) (3,1) (3,0).
+constexpr uint32_t kTileRT = 0xfb9e4;
+constexpr uint32_t kTileST = 0x124e4;
+constexpr int kScoreRowBytes = kC * 2 + 16;  // [64][64] bf16 score tile, padded rows
+
+__device__ __forceinline__ int score_off(int t, int s) { return t * kScoreRowBytes + 2 * s; }
+
+// Phase A of a consumer chunk: this wave's share of the masked scores P = Qh Kh^T
+// (computed as P^T tiles, lane holding 4 consecutive keys of one query) into the
+// score tile, and the inter-chunk term O^T = S_pre^T Qh^T for all 64 queries.
+__device__ __forceinline__ void consume_phase_a(const uint8_t* Q, const uint8_t* K, const uint8_t* sQl,
+                                                const uint8_t* sKl, uint8_t* sP, const f32x4 (&Sacc)[2][8],
+                                                f32x4 (&Oacc)[2][4], bool exact, int w, int g4, int n16) {
+  for (int idx = w; idx < 10; idx += 4) {
+    const int rt = (kTileRT >> (2 * idx)) & 3, st = (kTileST >> (2 * idx)) & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ++ks) {
+      const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
+      const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
+      const bf16x8 kf = as_bf16x8(lds_ld<uint4>(K, ka));
+      const bf16x8 qf = as_bf16x8(lds_ld<uint4>(Q, qa));
+      if (exact && idx == 0) {  // tile (0, 0) of a call's first chunk: hi/lo cross terms
+        acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qf, acc);
+        acc = mma(kf, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
+      }
+      acc = mma(kf, qf, acc);
+    }
+    if (st == rt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (4 * g4 + r > n16) acc[r] = 0.f;
+    }
+    lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
+                  make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
+  }
+  bf16x8 SA[2][4];  // S_pre^T as A operand (bf16), key dims in order pi
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) SA[dt][kk] = pack8(Sacc[dt][2 * kk], Sacc[dt][2 * kk + 1]);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    bf16x8 Qf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Qf[kk] = pi_operand(Q, 16 * rt + n16, kk, g4);
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      Oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) Oacc[dt][rt] = mma(SA[dt][kk], Qf[kk], Oacc[dt][rt]);
+    }
+  }
+}
+
+// Phase B: O^T += V^T P^T (scores read from the shared tile in key order pi),
+// gate and store each row block, then S_pre += Kh^T V.
+__device__ __forceinline__ void consume_phase_b(const uint8_t* K, const uint8_t* V, const uint8_t* G,
+                                                const uint8_t* sP, f32x4 (&Sacc)[2][8], f32x4 (&Oacc)[2][4],
+                                                int nv, uint16_t* orow, int64_t rs, int w, int g4, int n16) {
+  bf16x8 Vf[2][2];  // V^T (token order pi), columns 32w + 16 dt + n16
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) Vf[dt][kk] = v_operand(V, kk, 32 * w + 16 * dt, g4, n16);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int t = 16 * rt + n16;
+#pragma unroll
+    for (int kk = 0; kk <= rt / 2; ++kk) {
+      const bf16x8 pb = as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
+                                  lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) Oacc[dt][rt] = mma(Vf[dt][kk], pb, Oacc[dt][rt]);
+    }
+    // gate and store: lane holds o[16 rt + n16][32 w + 16 dt + 4 g .. + 3]
+    uint16_t* dst = orow + (int64_t)(16 * rt) * rs;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const uint2 sg = lds_ld<uint2>(G, tile_off(t, 32 * w + 16 * dt + 4 * g4));
+      const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * f16_lo(sg.x), Oacc[dt][rt][1] * f16_hi(sg.x)),
+                                   pack2(Oacc[dt][rt][2] * f16_lo(sg.y), Oacc[dt][rt][3] * f16_hi(sg.y)));
+      if (t < nv) *reinterpret_cast<uint2*>(dst + 16 * dt) = out;
+    }
+  }
+  // state carry S_pre += Kh^T V
+#pragma unroll
+  for (int kk = 0; kk < kC / 32; ++kk) {
+    const int tr0 = 32 * kk + 4 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk) {
+      const int col = 16 * rtk + 4 * (n16 & 3);
+      const bf16x8 a = as_bf16x8(lds_tr(K, tile_off(tr0, col)), lds_tr(K, tile_off(tr0 + 16, col)));
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) Sacc[dt][rtk] = mma(a, Vf[dt][kk], Sacc[dt][rtk]);
+    }
+  }
+}
+
 __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, uint8_t (*sQ)[kTileBytes],
                                         uint8_t (*sK)[kTileBytes], uint8_t (*sV)[kTileBytes],
                                         uint8_t (*sG)[kTileBytes], const uint8_t* sQl,
-                                        const uint8_t* sKl) {
+                                        const uint8_t* sKl, uint8_t* sP) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
   const int64_t rs = (int64_t)p.H * kD;
@@ -448,6 +559,9 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
   }
   // this lane's output pointer at chunk-relative row n16, column 32 w + 4 g
   uint16_t* const obase = p.o + tl.base + (int64_t)n16 * rs + 32 * w + 4 * g4;
+  // score tiles above the diagonal are never written: zero the tile once
+  for (int i = tid; i < kC * kScoreRowBytes / 16; i += kConsumers)
+    reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();
   __syncthreads();
 
@@ -463,109 +577,30 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
     // hi/lo split of qh and kh: those rows sum only a few scores, so the bf16
     // rounding of qh, kh would otherwise dominate their error.
     const bool exact = tl.seg == 0 && c == 0;
-
-    bf16x8 SA[2][4];  // S_pre^T as A operand (bf16), key dims in order pi
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) SA[dt][kk] = pack8(Sacc[dt][2 * kk], Sacc[dt][2 * kk + 1]);
-    bf16x8 Vf[2][2];  // V^T (token order pi), columns 32w + 16 dt + n16
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[dt][kk] = v_operand(V, kk, 32 * w + 16 * dt, g4, n16);
-
     f32x4 Oacc[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int t = 16 * rt + n16;
-      bf16x8 Qf[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) Qf[kk] = pi_operand(Q, t, kk, g4);
-      // inter-chunk term O^T = S_pre^T Qh^T
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        Oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) Oacc[dt][rt] = mma(SA[dt][kk], Qf[kk], Oacc[dt][rt]);
-      }
-      // masked scores P^T = Kh Qh^T for key blocks st <= rt
-      f32x4 Pt[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        Pt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (st > rt) continue;
-        const int s = 16 * st + n16;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 kf = pi_operand(K, s, kk, g4);
-          if (rt == 0 && exact) {  // tile (0, 0) of the first chunk: add the lo cross terms
-            Pt[st] = mma(pi_operand(sKl, s, kk, g4), Qf[kk], Pt[st]);
-            Pt[st] = mma(kf, pi_operand(sQl, t, kk, g4), Pt[st]);
-          }
-          Pt[st] = mma(kf, Qf[kk], Pt[st]);
-        }
-        if (st == rt) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * g4 + r > n16) Pt[st][r] = 0.f;
-        }
-      }
-      // intra-chunk term O^T += V^T P^T; score tiles pair up into B operands
-#pragma unroll
-      for (int kk = 0; kk <= rt / 2; ++kk) {
-        const bf16x8 pb = pack8(Pt[2 * kk], Pt[2 * kk + 1]);
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) Oacc[dt][rt] = mma(Vf[dt][kk], pb, Oacc[dt][rt]);
-      }
-    }
-
-    // state carry S_pre += Kh^T V
-#pragma unroll
-    for (int kk = 0; kk < kC / 32; ++kk) {
-      const int tr0 = 32 * kk + 4 * g4 + (n16 >> 2);
-#pragma unroll
-      for (int rtk = 0; rtk < 8; ++rtk) {
-        const int col = 16 * rtk + 4 * (n16 & 3);
-        const bf16x8 a = as_bf16x8(lds_tr(K, tile_off(tr0, col)), lds_tr(K, tile_off(tr0 + 16, col)));
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) Sacc[dt][rtk] = mma(a, Vf[dt][kk], Sacc[dt][rtk]);
-      }
-    }
-
-    // gate and store: lane holds o[16 rt + n16][32 w + 16 dt + 4 g .. + 3]
-    uint16_t* orow = obase + (int64_t)t0 * rs;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const int t = 16 * rt + n16;
-      uint16_t* dst = orow + (int64_t)(16 * rt) * rs;
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const uint2 sg = lds_ld<uint2>(G, tile_off(t, 32 * w + 16 * dt + 4 * g4));
-        const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * f16_lo(sg.x), Oacc[dt][rt][1] * f16_hi(sg.x)),
-                                     pack2(Oacc[dt][rt][2] * f16_lo(sg.y), Oacc[dt][rt][3] * f16_hi(sg.y)));
-        if (t < nv) *reinterpret_cast<uint2*>(dst + 16 * dt) = out;
-      }
-    }
+    consume_phase_a(Q, K, sQl, sKl, sP, Sacc, Oacc, exact, w, g4, n16);
+    __syncthreads();
+    consume_phase_b(K, V, G, sP, Sacc, Oacc, nv, obase + (int64_t)t0 * rs, rs, w, g4, n16);
     __syncthreads();
   }
 }
 
 template <bool kWeights>
-__global__ __launch_bounds__(kThreads) void la_chunk_output_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kOutThreads) void la_chunk_output_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sQ[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), f16
   __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
   __shared__ float2 sRot[2][kHalf];
 
   const Tile tl = decode_tile(p);
   if (threadIdx.x >= kConsumers)
     produce<kWeights>(p, tl, sQ, sK, sV, sG, sQl, sKl, sRot);
   else
-    consume(p, tl, sQ, sK, sV, sG, sQl, sKl);
+    consume(p, tl, sQ, sK, sV, sG, sQl, sKl, sP);
 }
 
 }  // namespace
@@ -589,9 +624,9 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
                      stream, p);
   mark(2);
   if (weights)
-    hipLaunchKernelGGL(la_chunk_output_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(la_chunk_output_kernel<true>, grid, dim3(kOutThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(la_chunk_output_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL(la_chunk_output_kernel<false>, grid, dim3(kOutThreads), 0, stream, p);
   mark(3);
   const hipError_t launch = hipGetLastError();
   return err != hipSuccess ? err : launch;
