@@ -80,6 +80,13 @@ __device__ __forceinline__ int score_off(int t, int s) {
   return t * (C * 2) + ((((s >> 3) ^ (t & 7))) << 4) + ((s & 7) << 1);
 }
 
+// Global load of 8 bytes that are read once (non-temporal hint).
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 ld_stream(const void* p) {
+  const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(x.x, x.y);
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_ld(const uint8_t* base, int off) {
   return *reinterpret_cast<const T*>(base + off);

@@ -14,12 +14,14 @@
 //   2. la_state_scan_kernel  : per state element, exclusive prefix over segments
 //      (plus S_in) in place, and the final state -> S_out.
 //   3. la_chunk_output_kernel: one workgroup per (b, h, segment) starts from its
-//      segment's prefix state and walks the chunks.  Four producer waves load
-//      chunk c+1, apply QK-RMSNorm + RoPE to q, k and the sigmoid to the gate,
-//      and stage the tiles into one half of a ping-pong LDS buffer, while four
-//      consumer waves run all the MFMA work of chunk c from the other half:
-//      O^T = S^T Qh^T + V^T P^T with P^T = masked Kh Qh^T, the gate multiply,
-//      the bf16 store of o, and S += Kh^T V.  One barrier per chunk.
+//      segment's prefix state and walks the chunks.  Eight producer waves apply
+//      QK-RMSNorm + RoPE to q, k and the sigmoid to the gate of chunk c+1 and
+//      stage the tiles into one half of a ping-pong LDS buffer (their global
+//      loads run two chunks further ahead), while four consumer waves run all
+//      the MFMA work of chunk c from the other half: the masked scores
+//      P = Qh Kh^T into a shared LDS tile and O^T = S^T Qh^T, then
+//      O^T += V^T P^T, the gate multiply, the bf16 store of o and S += Kh^T V.
+//      Two barriers per chunk.
 //
 // MFMA layouts (v_mfma_f32_16x16x32_bf16; lane l = 16 g + n16 supplies
 // A[n16][8g + e], B[8g + e][n16] and holds D[4g + r][n16]):
@@ -91,8 +93,8 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, int
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint16_t* src = base + (int64_t)min(rg + kStep * m, nvalid - 1) * rs;
-    R.lo[m] = *reinterpret_cast<const uint2*>(src + 4 * j);
-    R.hi[m] = *reinterpret_cast<const uint2*>(src + kHalf + 4 * j);
+    R.lo[m] = ld_stream(src + 4 * j);
+    R.hi[m] = ld_stream(src + kHalf + 4 * j);
   }
 }
 
@@ -360,10 +362,9 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
 
 // --------------------------------------------------------------------------
 // Output kernel.  Threads 0..255 are the consumer waves (wave w owns value
-// columns [32w, 32w + 32)); threads 256..511 are the producer waves (thread
-// (rg, j) stages rows rg + 16m, m < 4).  Both roles run their own loop with the
-// same number of barriers: one before the loop, one after the first staging and
-// one per chunk.
+// columns [32w, 32w + 32)); threads 256..767 are the producer waves (thread
+// (rg, j) stages rows rg and rg + 32).  Both roles run their own loop with the
+// same number of barriers: two before the loop and two per chunk.
 constexpr int kConsumers = 256;               // 4 consumer waves
 constexpr int kProducers = 512;               // 8 producer waves
 constexpr int kOutThreads = kConsumers + kProducers;
@@ -387,53 +388,55 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   load_norm_weights(p.kw, j, wk);
   Rope L;
   rope_init<32>(p, ptid, rg, j, L);
-  Rows<2> Qr, Kr, Vr, Gr;
-  auto load_chunk = [&](int c) {
+  struct Chunk {
+    Rows<2> q, k, v, g;
+  };
+  Chunk X, Y;
+  auto load_chunk = [&](int c, Chunk& R) {
     const int t = tl.t_begin + c * kC;
     const int nv = min(kC, tl.t_end - t);
     const int64_t off = tl.base + (int64_t)t * rs;
-    load_rows<2, 32>(p.q + off, rs, nv, rg, j, Qr);
-    load_rows<2, 32>(p.k + off, rs, nv, rg, j, Kr);
-    load_rows<2, 32>(p.v + off, rs, nv, rg, j, Vr);
-    load_rows<2, 32>(p.g + off, rs, nv, rg, j, Gr);
+    load_rows<2, 32>(p.q + off, rs, nv, rg, j, R.q);
+    load_rows<2, 32>(p.k + off, rs, nv, rg, j, R.k);
+    load_rows<2, 32>(p.v + off, rs, nv, rg, j, R.v);
+    load_rows<2, 32>(p.g + off, rs, nv, rg, j, R.g);
   };
-  // phase A of a chunk's staging: qh, kh; phase B: v, sigmoid(gate)
-  auto stage_qk = [&](int c) {
+  auto stage = [&](int c, const Chunk& R) {
     const int b = c & 1;
     const bool exact = tl.seg == 0 && c == 0;
-    norm_rope_stage_qk<kWeights, 2, 32>(Qr, Kr, wq, wk, p.eps, sRot[b], L, rg, j, sQ[b], sK[b],
-                                        exact ? sQl : nullptr, exact ? sKl : nullptr);
-  };
-  auto stage_vg = [&](int c) {
-    const int b = c & 1;
     const int nv = min(kC, tl.t_end - (tl.t_begin + c * kC));
-    store_rows_masked<2, 32>(sV[b], Vr, nv, rg, j);
-    sigmoid_stage<2, 32>(sG[b], Gr, rg, j);
+    norm_rope_stage_qk<kWeights, 2, 32>(R.q, R.k, wq, wk, p.eps, sRot[b], L, rg, j, sQ[b], sK[b],
+                                        exact ? sQl : nullptr, exact ? sKl : nullptr);
+    store_rows_masked<2, 32>(sV[b], R.v, nv, rg, j);
+    sigmoid_stage<2, 32>(sG[b], R.g, rg, j);
+  };
+  // One step of the pipeline while the consumers work on chunk c: stage chunk
+  // c + 1 from R, then reuse R for chunk c + 3 (chunk c + 2 is in flight in the
+  // other register set).
+  auto step = [&](int c, Chunk& R) {
+    if (c + 1 < tl.nch) {
+      stage(c + 1, R);
+      if (c + 3 < tl.nch) load_chunk(c + 3, R);
+      if (c + 2 < tl.nch && ptid < kHalf)
+        sRot[c & 1][ptid] = rope_rotation(p.pos0 + tl.t_begin + (c + 2) * kC, L.base_rev);
+    }
+    __syncthreads();
+    __syncthreads();
   };
 
-  load_chunk(0);
+  load_chunk(0, Y);
   if (ptid < kHalf) {
     sRot[0][ptid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
     if (tl.nch > 1) sRot[1][ptid] = rope_rotation(p.pos0 + tl.t_begin + kC, L.base_rev);
   }
   __syncthreads();
-  stage_qk(0);
-  stage_vg(0);
-  if (tl.nch > 1) load_chunk(1);
+  stage(0, Y);
+  if (tl.nch > 1) load_chunk(1, X);
+  if (tl.nch > 2) load_chunk(2, Y);
   __syncthreads();
-  for (int c = 0; c < tl.nch; ++c) {
-    const bool next = c + 1 < tl.nch;
-    if (next) stage_qk(c + 1);
-    __syncthreads();
-    if (next) {
-      stage_vg(c + 1);
-      if (c + 2 < tl.nch) {
-        load_chunk(c + 2);
-        if (ptid < kHalf)
-          sRot[c & 1][ptid] = rope_rotation(p.pos0 + tl.t_begin + (c + 2) * kC, L.base_rev);
-      }
-    }
-    __syncthreads();
+  for (int c = 0; c < tl.nch; c += 2) {
+    step(c, X);
+    if (c + 1 < tl.nch) step(c + 1, Y);
   }
 }
 
