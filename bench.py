@@ -14,6 +14,7 @@ Prints one JSON line (rank 0, N = 1):
   roofline  the dominant kernel (the chunk-output kernel) against HBM bandwidth,
             from HIP events recorded on the library's stream around each kernel
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample
+  prefill_detail.chunk_sweep  the same prefill at chunk 64, 128 and 256
 """
 from __future__ import annotations
 
@@ -128,10 +129,10 @@ def bench_prefill(la, torch, workloads, hip, args):
     scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
     flops = (4 * D * D + 2 * D * (chunk + 1)) * B * T * H
     out_s = per["chunk_output"] / 1e3
-    traffic = measured_traffic(tokens)
+    traffic = measured_traffic(tokens) if chunk == la.DEFAULT_CHUNK else None
     roofline = {
         "bound": "hbm",
-        "kernel": "la_chunk_output_kernel",
+        "kernel": "la_chunk_output_kernel" if chunk == la.DEFAULT_CHUNK else "la_chunk_output_wide_kernel",
         "achieved": round(out_bytes / out_s / 1e9, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
@@ -157,7 +158,33 @@ def bench_prefill(la, torch, workloads, hip, args):
         "segments_per_head": plan_nseg,
         "chunk": chunk,
     }
+    if not args.no_chunk_sweep:
+        detail["chunk_sweep"] = chunk_sweep(la, torch, hip, (q, k, v, g), o, S_out)
     return w, tokens * args.steps / wall, step_s, roofline, detail, (q, k, v, g)
+
+
+def chunk_sweep(la, torch, hip, tensors, o, S_out, steps=3):
+    """GPU time of the same 256K prefill at every supported chunk size (events
+    around each kernel, one warm-up call, `steps` timed calls)."""
+    q, k, v, g = tensors
+    B, T, H, D = q.shape
+    res = {}
+    for c in (64, 128, 256):
+        ws = torch.empty(la.prefill_workspace_bytes(B, T, H, D, c), dtype=torch.uint8, device="cuda")
+        la.prefill(q, k, v, g, chunk=c, out=o, S_out=S_out, workspace=ws)
+        evs = [hip.create(4) for _ in range(steps)]
+        for e in evs:
+            la.prefill(q, k, v, g, chunk=c, out=o, S_out=S_out, workspace=ws, events=e)
+        torch.cuda.synchronize()
+        ms = sum(hip.ms(e[0], e[3]) for e in evs) / steps
+        out_ms = sum(hip.ms(e[2], e[3]) for e in evs) / steps
+        for e in evs:
+            hip.destroy(e)
+        del ws
+        res[str(c)] = {"gpu_ms": round(ms, 4), "output_kernel_ms": round(out_ms, 4),
+                       "tokens_per_s": round(B * T / (ms / 1e3), 1),
+                       "kernel": "la_chunk_output_kernel" if c == 64 else "la_chunk_output_wide_kernel"}
+    return res
 
 
 def bench_decode(la, torch, workloads, hip, args):
@@ -237,6 +264,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")

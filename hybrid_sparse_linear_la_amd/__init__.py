@@ -25,7 +25,7 @@ lib_path = os.path.join(_PKG, "liblightning_la.so")
 
 HEAD_DIM = 128
 DEFAULT_CHUNK = 64
-SUPPORTED_CHUNKS = (0, 64)
+SUPPORTED_CHUNKS = (0, 64, 128, 256)
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
     4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",

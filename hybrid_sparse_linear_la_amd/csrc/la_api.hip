@@ -48,12 +48,15 @@ bool finite_positive(float x) { return isfinite(x) && x > 0.0f; }
 bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   if (B < 1 || T < 1 || H < 1) return false;
   const int C = chunk == 0 ? kDefaultChunk : chunk;
-  if (C != 64) return false;
+  if (C != 64 && C != 128 && C != 256) return false;
+  // Work is counted in 64-token sub-chunks; a segment holds whole C-chunks.
+  const int64_t sub = C / 64;
   const int64_t bh = (int64_t)B * H;
-  const int64_t nchunks = ((int64_t)T + C - 1) / C;
+  const int64_t nchunks = ((int64_t)T + 63) / 64;
   int64_t cps = (bh * nchunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  if (cps < 1) cps = 1;
-  if (cps > nchunks) cps = nchunks;
+  cps = (cps + sub - 1) / sub * sub;
+  if (cps < sub) cps = sub;
+  if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
   if (bh * nseg > kMaxWorkgroups || bh > ((int64_t)1 << 20)) return false;
   plan->C = C;
@@ -77,7 +80,7 @@ const char* la_status_string(la_status s) {
     case LA_OK: return "LA_OK";
     case LA_ERR_NULL_PTR: return "LA_ERR_NULL_PTR: a required pointer is NULL";
     case LA_ERR_BAD_SHAPE: return "LA_ERR_BAD_SHAPE: B, T and H must be >= 1 and the launch must fit";
-    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: need D == 128, chunk in {0, 64}, rope_base > 0, rms_eps >= 0";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: need D == 128, chunk in {0, 64, 128, 256}, rope_base > 0 and finite, rms_eps >= 0 and finite";
     case LA_ERR_ALIGNMENT: return "LA_ERR_ALIGNMENT: pointers must be 16-byte aligned";
     case LA_ERR_ALIASING: return "LA_ERR_ALIASING: an output overlaps another argument";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
@@ -100,7 +103,7 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
                               void* stream, hipEvent_t const* events) {
   if (!q || !k || !v || !gate_logits || !S_out || !o || !workspace) return LA_ERR_NULL_PTR;
   if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
-  if (D != kHeadDim || (chunk != 0 && chunk != 64)) return LA_ERR_UNSUPPORTED;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
   if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
   PrefillPlan plan;
   if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;

@@ -62,24 +62,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x4& a, const f32x4& b) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS tiles, bf16, with the 16-byte block index XOR-swizzled so that both the
-// 16-byte MFMA operand reads and the staging writes spread over all banks.
-//
-// Row tile [rows][128] (q, k, gate logits, output staging): element (t, d).
-__device__ __forceinline__ int row_off(int t, int d) {
-  return t * (kD * 2) + ((((d >> 3) ^ (t & 7))) << 4) + ((d & 7) << 1);
-}
-// Transposed tile [128][C] (k^T, v^T): element (d, t); C is a multiple of 64.
-template <int C>
-__device__ __forceinline__ int col_off(int d, int t) {
-  return d * (C * 2) + ((((t >> 3) ^ ((d >> 1) & 7))) << 4) + ((t & 7) << 1);
-}
-// Score tile [C][C]: element (t, s).
-template <int C>
-__device__ __forceinline__ int score_off(int t, int s) {
-  return t * (C * 2) + ((((s >> 3) ^ (t & 7))) << 4) + ((s & 7) << 1);
-}
-
 // Global load of 8 bytes that are read once (non-temporal hint).
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 ld_stream(const void* p) {

@@ -17,12 +17,13 @@ struct RopeFreqs {
   double rev[kFreqs];
 };
 
-// How one prefill call is cut up: T tokens -> chunks of C tokens -> segments of
-// `cps` consecutive chunks.  One workgroup walks one (b, h, segment).
+// How one prefill call is cut up: T tokens -> sub-chunks of 64 tokens ->
+// segments of `cps` consecutive sub-chunks (a multiple of C / 64, so a segment
+// holds whole chunks of C tokens).  One workgroup walks one (b, h, segment).
 struct PrefillPlan {
-  int C = 0;        // chunk length
-  int nchunks = 0;  // ceil(T / C)
-  int cps = 0;      // chunks per segment
+  int C = 0;        // chunk length: 64, 128 or 256
+  int nchunks = 0;  // ceil(T / 64)
+  int cps = 0;      // 64-token sub-chunks per segment
   int nseg = 0;     // segments per (b, h)
   size_t ws_bytes = 0;
 };

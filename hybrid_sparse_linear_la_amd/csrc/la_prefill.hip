@@ -207,6 +207,17 @@ __device__ __forceinline__ void norm_rope_stage(const Rows<M>& R, const float (&
   }
 }
 
+// One tensor, with the first row's rotations E already formed (advanced in place).
+template <bool kWeights, int M, int kStep>
+__device__ __forceinline__ void norm_rope_rows(const Rows<M>& R, const float (&w)[8], float eps, float2 (&E)[4],
+                                               const Rope& L, int rg, int j, uint8_t* tile, uint8_t* lo) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (m > 0) next_rotation(L, E);
+    norm_rope_row<kWeights>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, lo);
+  }
+}
+
 // q and k of the same rows share one rotation chain.
 template <bool kWeights, int M, int kStep>
 __device__ __forceinline__ void norm_rope_stage_qk(const Rows<M>& Qr, const Rows<M>& Kr, const float (&wq)[8],
@@ -606,6 +617,167 @@ __global__ __launch_bounds__(kOutThreads) void la_chunk_output_kernel(PrefillPar
     consume(p, tl, sQ, sK, sV, sG, sQl, sKl, sP);
 }
 
+
+// --------------------------------------------------------------------------
+// Wide-chunk output kernel, C = 64 kSub (kSub = 2 or 4).  The chunked form with
+// chunk C: query sub-block i (64 rows) of a chunk takes its scores against key
+// sub-blocks jj <= i (causally masked at jj = i) and its inter-chunk term from the
+// state at the chunk start; the chunk's Kh^T V joins the state after the chunk.
+// Tiles are single-buffered and k, v of sub-block jj are staged again for every
+// i >= jj, so a wider chunk costs more work and more reads than C = 64.  Eight
+// waves; wave w owns value columns [16 w, 16 w + 16) of S and o.  Three barriers
+// per (i, jj): after staging, after the scores, after the intra-chunk product.
+constexpr int kWideThreads = 512;
+
+template <bool kWeights, int kSub>
+__global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int j = tid & 15, rg = tid >> 4;
+  const Tile tl = decode_tile(p);
+  const int64_t rs = (int64_t)p.H * kD;
+
+  float wq[8], wk[8];
+  load_norm_weights(p.qw, j, wq);
+  load_norm_weights(p.kw, j, wk);
+  Rope L;
+  rope_init<32>(p, tid, rg, j, L);
+  double rev[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) rev[e] = p.freqs.rev[4 * j + e];
+  // rotations of row rg of a sub-block starting at token t
+  auto first_rows = [&](int t, float2 (&E)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(p.pos0 + t, rev[e]), L.A[e]);
+  };
+
+  // prefix state of this segment: S[:, 16 w .. 16 w + 16)
+  f32x4 Sacc[8];
+  {
+    const float* src = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Sacc[rtk][r] = src[state_elem(rtk, r, w, g4, n16)];
+  }
+  // this lane's output (and gate) columns 16 w + 4 g .. + 3 of (b, h)
+  const int64_t col_off = tl.base + 16 * w + 4 * g4;
+
+  for (int t0 = tl.t_begin; t0 < tl.t_end; t0 += kSub * kC) {
+    f32x4 Dacc[8];
+#pragma unroll
+    for (int a = 0; a < 8; ++a) Dacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kSub; ++i) {
+      const int ti = t0 + i * kC;
+      if (ti >= tl.t_end) break;
+      const int nvi = min(kC, tl.t_end - ti);
+      // scores of the first 16 rows of a call use the hi/lo split (see the C = 64 kernel)
+      const bool exact = tl.seg == 0 && t0 == tl.t_begin && i == 0;
+      // gate logits of the lane's rows ti + 16 rt + n16 (clamped to the sub-block's last valid row)
+      uint2 graw[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        graw[rt] = ld_stream(p.g + col_off + (int64_t)(ti + min(16 * rt + n16, nvi - 1)) * rs);
+      f32x4 Oacc[4];
+      for (int jj = 0; jj <= i; ++jj) {
+        const int tj = t0 + jj * kC;
+        const int nvj = min(kC, tl.t_end - tj);
+        {
+          Rows<2> Kr, Vr;
+          load_rows<2, 32>(p.k + tl.base + (int64_t)tj * rs, rs, nvj, rg, j, Kr);
+          load_rows<2, 32>(p.v + tl.base + (int64_t)tj * rs, rs, nvj, rg, j, Vr);
+          if (jj == 0) {
+            Rows<2> Qr;
+            load_rows<2, 32>(p.q + tl.base + (int64_t)ti * rs, rs, nvi, rg, j, Qr);
+            float2 E[4];
+            first_rows(ti, E);
+            norm_rope_rows<kWeights, 2, 32>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
+          }
+          float2 E[4];
+          first_rows(tj, E);
+          norm_rope_rows<kWeights, 2, 32>(Kr, wk, p.eps, E, L, rg, j, sK, exact && jj == 0 ? sKl : nullptr);
+          store_rows_masked<2, 32>(sV, Vr, nvj, rg, j);
+        }
+        __syncthreads();
+        if (jj == 0) {
+          // inter-chunk term O^T = S^T Qh^T (key dims in order pi)
+          bf16x8 SA[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) SA[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) Oacc[rt] = mma(SA[kk], pi_operand(sQ, 16 * rt + n16, kk, g4), Oacc[rt]);
+          }
+        }
+        // scores of query sub-block i against key sub-block jj, two 16x16 tiles per wave
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int idx = w + 8 * u;
+          const int rt = idx >> 2, st = idx & 3;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < kD / 32; ++ks) {
+            const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
+            const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
+            const bf16x8 kf = as_bf16x8(lds_ld<uint4>(sK, ka));
+            const bf16x8 qf = as_bf16x8(lds_ld<uint4>(sQ, qa));
+            if (exact && idx == 0) {
+              acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qf, acc);
+              acc = mma(kf, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
+            }
+            acc = mma(kf, qf, acc);
+          }
+          if (jj == i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (st > rt || (st == rt && 4 * g4 + r > n16)) acc[r] = 0.f;
+          }
+          lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
+                        make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
+        }
+        bf16x8 Vf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) Vf[kk] = v_operand(sV, kk, 16 * w, g4, n16);
+        if (jj == i) accumulate_state(Dacc, sK, Vf, g4, n16);
+        __syncthreads();
+        // O^T += V^T P^T
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const int t = 16 * rt + n16;
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const bf16x8 pb = as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
+                                        lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
+            Oacc[rt] = mma(Vf[kk], pb, Oacc[rt]);
+          }
+        }
+        __syncthreads();
+      }
+      // gate and store: lane holds o[ti + 16 rt + n16][16 w + 4 g .. + 3]
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (16 * rt + n16 < nvi) {
+          const uint2 gr = graw[rt];
+          const uint2 out = make_uint2(pack2(Oacc[rt][0] * sigmoidf_(bf2f_lo(gr.x)), Oacc[rt][1] * sigmoidf_(bf2f_hi(gr.x))),
+                                       pack2(Oacc[rt][2] * sigmoidf_(bf2f_lo(gr.y)), Oacc[rt][3] * sigmoidf_(bf2f_hi(gr.y))));
+          *reinterpret_cast<uint2*>(p.o + col_off + (int64_t)(ti + 16 * rt + n16) * rs) = out;
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 8; ++a) Sacc[a] += Dacc[a];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipStream_t stream,
@@ -626,10 +798,22 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
   hipLaunchKernelGGL(la_state_scan_kernel, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
                      stream, p);
   mark(2);
-  if (weights)
-    hipLaunchKernelGGL(la_chunk_output_kernel<true>, grid, dim3(kOutThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(la_chunk_output_kernel<false>, grid, dim3(kOutThreads), 0, stream, p);
+  if (plan.C == kC) {
+    if (weights)
+      hipLaunchKernelGGL(la_chunk_output_kernel<true>, grid, dim3(kOutThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(la_chunk_output_kernel<false>, grid, dim3(kOutThreads), 0, stream, p);
+  } else if (plan.C == 2 * kC) {
+    if (weights)
+      hipLaunchKernelGGL((la_chunk_output_wide_kernel<true, 2>), grid, dim3(kWideThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((la_chunk_output_wide_kernel<false, 2>), grid, dim3(kWideThreads), 0, stream, p);
+  } else {
+    if (weights)
+      hipLaunchKernelGGL((la_chunk_output_wide_kernel<true, 4>), grid, dim3(kWideThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((la_chunk_output_wide_kernel<false, 4>), grid, dim3(kWideThreads), 0, stream, p);
+  }
   mark(3);
   const hipError_t launch = hipGetLastError();
   return err != hipSuccess ? err : launch;

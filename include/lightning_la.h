@@ -30,7 +30,8 @@
  *   q, k, v, gate logits, o : bf16 [B, T, H, D]   (decode: [B, H, D])
  *   S_in, S_out, S          : fp32 [B, H, D, D], S[i][j] = sum_t kh_t[i] v_t[j]
  *   q_norm_w, k_norm_w      : fp32 [D], or NULL for all-ones weights
- * Supported: D == 128, B, H >= 1, T >= 1, chunk in {0 (= default), 64}.
+ * Supported: D == 128, B, H >= 1, T >= 1, chunk in {0 (= default = 64), 64, 128,
+ * 256}, rope_base finite and > 0, rms_eps finite and >= 0.
  *
  * Ownership and asynchrony: every pointer (except where noted) is a device
  * pointer owned by the caller.  The library allocates no memory and keeps no
@@ -58,7 +59,8 @@ typedef enum {
   LA_OK = 0,
   LA_ERR_NULL_PTR = 1,    /* a required pointer is NULL                              */
   LA_ERR_BAD_SHAPE = 2,   /* B, T or H < 1, or a size product overflows               */
-  LA_ERR_UNSUPPORTED = 3, /* D != 128, or chunk not in {0, 64}                        */
+  LA_ERR_UNSUPPORTED = 3, /* D != 128, chunk not in {0, 64, 128, 256}, or a bad
+                             rope_base / rms_eps                                     */
   LA_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned                          */
   LA_ERR_ALIASING = 5,    /* o overlaps an input, or S_out overlaps an activation      */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_prefill_workspace_bytes */
@@ -87,7 +89,12 @@ size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk);
  *           (in-place carry between segments of a long sequence).
  *   S_out : [B, H, D, D] fp32 final state (the state after token T - 1).
  *   o     : [B, T, H, D] bf16 gated output; must not overlap any input.
- *   chunk : tokens per chunk of the chunked evaluation (0 = default, 64).
+ *   chunk : tokens per chunk of the chunked evaluation: 0 (= 64), 64, 128 or 256.
+ *           The result is the same closed form for every chunk; the chunk only
+ *           decides which token pairs go through the bf16 score products and
+ *           which through the bf16 state operand.  64 is the fast path; 128
+ *           and 256 run a single-buffered kernel that stages k and v of a
+ *           chunk's earlier 64-row blocks again for every later block.
  *   rope_base : RoPE base (10000 in the workloads); rms_eps : RMSNorm epsilon.
  *   workspace : device buffer of at least la_prefill_workspace_bytes(...) bytes;
  *               its contents on entry are irrelevant and are clobbered.

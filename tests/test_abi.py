@@ -49,6 +49,10 @@ def test_workspace_bytes(lib):
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 0) == 2 * 5 * 128 * 128 * 4
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 64, 0) == 0
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 96) == 0
+    # wider chunks: segments hold whole chunks (5 sub-chunks of 64 -> 3 or 2 segments)
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 128) == 2 * 3 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 256) == 2 * 2 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 256) == 32 * 32 * 128 * 128 * 4
     assert lib.la_prefill_workspace_bytes(0, 300, 2, 128, 0) == 0
 
 
@@ -75,6 +79,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, H=-1) == 2
     assert _prefill(lib, D=64) == 3
     assert _prefill(lib, chunk=32) == 3
+    assert _prefill(lib, chunk=96) == 3
+    assert _prefill(lib, chunk=512) == 3
     assert _prefill(lib, base=0.0) == 3
     assert _prefill(lib, eps=-1.0) == 3
     assert _prefill(lib, eps=float("nan")) == 3

@@ -63,6 +63,49 @@ def test_prefill_matches_oracle(la, B, T, H, pos0, S_std, weights):
     assert_S_close(to_np(S), S_ref)
 
 
+WIDE_CASES = [
+    # chunk, B, T, H, pos0, S_std, weights
+    (128, 1, 1, 1, 0, 0.0, False),
+    (128, 1, 63, 3, 0, 0.0, False),       # one partial sub-block
+    (128, 2, 200, 2, 5, 0.5, False),      # second chunk ragged inside its first sub-block
+    (128, 1, 700, 4, 262144, 1.0, True),
+    (128, 1, 4096, 32, 0, 0.0, False),    # several segments per head
+    (256, 1, 100, 2, 0, 0.0, False),
+    (256, 2, 300, 3, 1000, 0.2, False),   # second chunk: one full and a partial sub-block
+    (256, 1, 1000, 4, 7, 0.0, True),      # last chunk: three sub-blocks, the last ragged
+    (256, 1, 4096, 32, 0, 0.0, False),
+]
+
+
+@pytest.mark.parametrize("chunk,B,T,H,pos0,S_std,weights", WIDE_CASES)
+def test_wide_chunk_matches_oracle(la, chunk, B, T, H, pos0, S_std, weights):
+    print(f"wide-chunk case C={chunk} B={B} T={T} H={H} pos0={pos0}", flush=True)
+    q, k, v, g, S_in, qw, kw = _inputs(B, T, H, seed=21 + T + chunk, S_std=S_std, weights=weights)
+    o, S = la.prefill(q, k, v, g, S_in=S_in, pos0=pos0, chunk=chunk, q_norm_w=qw, k_norm_w=kw)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(q, k, v, g, S_in, pos0, qw, kw)
+    assert_o_close(to_np(o), o_ref)
+    assert_S_close(to_np(S), S_ref)
+
+
+def test_chunk_sizes_agree(la):
+    """Every chunk size evaluates the same closed form: the outputs agree with each
+    other within the tolerance to the oracle (the typical row far inside it), and
+    the final state (the same fp32 sums, grouped into segments of whole chunks)
+    agrees to rounding."""
+    q, k, v, g, S_in, _, _ = _inputs(1, 2000, 4, seed=31, S_std=0.1)
+    outs = {c: la.prefill(q, k, v, g, S_in=S_in, pos0=123, chunk=c) for c in (64, 128, 256)}
+    torch.cuda.synchronize()
+    o64, S64 = outs[64]
+    for c in (128, 256):
+        o, S = outs[c]
+        e = o_row_errors(to_np(o), to_np(o64))
+        # each side carries ~1e-3 of bf16 output rounding per row
+        assert e["max"] <= 2e-2 and e["median"] <= 5e-3 and e["fro"] <= 5e-3, (c, e)
+        rel = float(torch.linalg.norm(S - S64) / torch.linalg.norm(S64))
+        assert rel <= 1e-5, (c, rel)
+
+
 def test_prefill_in_place_state_carry(la):
     q, k, v, g, S, _, _ = _inputs(1, 200, 4, seed=3, S_std=0.3)
     S_ref_in = to_np(S)
