@@ -15,6 +15,8 @@ Prints one JSON line (rank 0, N = 1):
             from HIP events recorded on the library's stream around each kernel
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample
   prefill_detail.chunk_sweep  the same prefill at chunk 64, 128 and 256
+  varlen    a packed serving batch (4 x 16K-token prompts + 60 decode steps) in
+            one la_prefill_varlen call, beside the same work as two calls
 """
 from __future__ import annotations
 
@@ -253,6 +255,61 @@ def cpu_baseline(tensors, args):
                       f"(fp64 token-by-token recurrence, {dt:.1f} s)"}
 
 
+def bench_varlen(la, torch, workloads, hip, args, steps=5):
+    """The serving mix as one la_prefill_varlen call, and the same work as one
+    equal-length la_prefill over the prompts plus one la_decode_step."""
+    w = workloads.SERVING_MIX
+    q, k, v, g, S_in, cu = workloads.mixed_inputs(w, "cuda")
+    n_pre = sum(1 for n in w.lengths if n > 1)
+    T_pre = w.lengths[0]
+    o = torch.empty_like(q)
+    S_out = torch.empty_like(S_in)
+    ws = torch.empty(la.prefill_varlen_workspace_bytes(cu, w.H), dtype=torch.uint8, device="cuda")
+
+    def one_call():
+        la.prefill_varlen(q, k, v, g, cu, pos0=list(w.pos0), S_in=S_in, out=o, S_out=S_out, workspace=ws)
+
+    # the same work as two calls: prompts [n_pre, T_pre] and decode rows [n_dec]
+    pre = [x[:n_pre * T_pre].view(n_pre, T_pre, w.H, w.D) for x in (q, k, v, g)]
+    dec = [x[n_pre * T_pre:] for x in (q, k, v, g)]
+    S_pre_in, S_dec = S_in[:n_pre].contiguous(), S_in[n_pre:].clone()
+    ws2 = torch.empty(la.prefill_workspace_bytes(n_pre, T_pre, w.H), dtype=torch.uint8, device="cuda")
+    o_pre = torch.empty_like(pre[0])
+    S_pre_out = torch.empty_like(S_pre_in)
+
+    def two_calls():
+        la.prefill(*pre, S_in=S_pre_in, pos0=0, out=o_pre, S_out=S_pre_out, workspace=ws2)
+        la.decode_step(*dec, S_dec, w.pos0[-1])
+
+    res = {}
+    for name, fn in (("varlen_one_call", one_call), ("prefill_plus_decode_calls", two_calls)):
+        fn()
+        e = hip.create(2)
+        stream = torch.cuda.current_stream().cuda_stream
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        hip.record(e[0], stream)
+        for _ in range(steps):
+            fn()
+        hip.record(e[1], stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        ms = hip.ms(e[0], e[1]) / steps
+        hip.destroy(e)
+        res[name] = {"gpu_ms": round(ms, 4), "wall_ms": round(wall * 1e3, 4)}
+    tokens = sum(w.lengths)
+    n_dec = len(w.lengths) - n_pre
+    # compulsory bytes: activations in/out of every token-head, plus each sequence's
+    # state read and written once
+    comp = 1280 * tokens * w.H + 2 * 65536 * len(w.lengths) * w.H
+    ms = res["varlen_one_call"]["gpu_ms"]
+    return {"workload": w.name, "sequences": len(w.lengths), "prefill_sequences": n_pre,
+            "decode_sequences": n_dec, "tokens": tokens, "steps": steps,
+            "tokens_per_s": round(tokens / (ms / 1e3), 1),
+            "compulsory_bytes": comp, "achieved_GBps": round(comp / (ms / 1e3) / 1e9, 1),
+            "hbm_roof_frac": round(comp / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), **res}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -264,6 +321,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the mixed prefill/decode batch")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -294,6 +352,7 @@ def main():
         del src, dst
     w, tps, step_s, roofline, detail, tensors = bench_prefill(la, torch, workloads, hip, args)
     decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
+    varlen = None if args.no_varlen else bench_varlen(la, torch, workloads, hip, args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
@@ -314,6 +373,7 @@ def main():
         "cpu_baseline": cpu,
         "prefill_detail": detail,
         "decode": decode,
+        "varlen": varlen,
     }
     print(json.dumps(line), flush=True)
 

@@ -9,6 +9,7 @@ is missing, every call raises.
 
     o, S_out = prefill(q, k, v, gate, S_in=None, pos0=0)
     o = decode_step(q, k, v, gate, S, pos)        # S updated in place
+    o, S_out = prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None)
 """
 from __future__ import annotations
 
@@ -17,7 +18,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "prefill_workspace_bytes", "LAError", "library", "lib_path",
+__all__ = ["prefill", "decode_step", "prefill_varlen", "prefill_workspace_bytes",
+           "prefill_varlen_workspace_bytes", "LAError", "library", "lib_path",
            "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +62,12 @@ def library():
         lib.la_prefill_profiled.restype = ctypes.c_int
         lib.la_prefill_profiled.argtypes = lib.la_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p),
                                                                       ctypes.c_int]
+        lib.la_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_prefill_varlen_workspace_bytes.argtypes = [ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int,
+                                                          ctypes.c_int]
+        lib.la_prefill_varlen.restype = ctypes.c_int
+        lib.la_prefill_varlen.argtypes = [_vp] * 9 + [ctypes.c_int] * 5 + [
+            ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
             ctypes.c_int64, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
@@ -143,6 +151,62 @@ def prefill(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: 
     else:
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib.la_prefill_profiled(*args, arr, len(events)))
+    return out, S_out
+
+
+def _host_array(name, values, ctype, n):
+    """Host copy of a length-n integer sequence as a ctypes array."""
+    if isinstance(values, torch.Tensor):
+        values = values.detach().cpu().tolist()
+    values = [int(x) for x in values]
+    if len(values) != n:
+        raise ValueError(f"{name} must have {n} entries, got {len(values)}")
+    return (ctype * n)(*values)
+
+
+def prefill_varlen_workspace_bytes(cu_seqlens, H: int, D: int = HEAD_DIM, chunk: int = 0) -> int:
+    cu = _host_array("cu_seqlens", cu_seqlens, ctypes.c_int32, len(cu_seqlens))
+    return int(library().la_prefill_varlen_workspace_bytes(len(cu) - 1, cu, H, D, chunk))
+
+
+def prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None, chunk: int = 0,
+                   rope_base: float = 10000.0, rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None,
+                   out=None, S_out=None, workspace=None):
+    """Variable-length batch.  q, k, v, gate: bf16 [total_T, H, 128] holding the
+    sequences back to back; cu_seqlens: nseq + 1 offsets (host list or CPU tensor);
+    pos0: nseq start positions or None; S_in/S_out: fp32 [nseq, H, 128, 128].
+
+    Returns (o bf16 [total_T, H, 128], S_out)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+        _act(n, t, 3)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    total_T, H, D = q.shape
+    nseq = len(cu_seqlens) - 1
+    cu = _host_array("cu_seqlens", cu_seqlens, ctypes.c_int32, nseq + 1)
+    p0 = None if pos0 is None else _host_array("pos0", pos0, ctypes.c_int64, nseq)
+    _f32("S_in", S_in, (nseq, H, D, D))
+    _f32("q_norm_w", q_norm_w, (D,))
+    _f32("k_norm_w", k_norm_w, (D,))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _act("out", out, 3)
+    if S_out is None:
+        S_out = torch.empty((nseq, H, D, D), dtype=torch.float32, device=q.device)
+    else:
+        _f32("S_out", S_out, (nseq, H, D, D))
+    need = int(lib.la_prefill_varlen_workspace_bytes(nseq, cu, H, D, chunk))
+    if need == 0:
+        status = 3 if (D != HEAD_DIM or chunk not in SUPPORTED_CHUNKS) else 2
+        raise LAError(status, lib.la_status_string(status).decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.la_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), cu, p0, _ptr(S_in), _ptr(S_out),
+                                 _ptr(out), nseq, total_T, H, D, int(chunk), float(rope_base),
+                                 float(rms_eps), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out, S_out
 
 

@@ -3,6 +3,10 @@
 // error status leaves the outputs untouched.
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
 
 #include "la_internal.hpp"
 #include "lightning_la.h"
@@ -17,6 +21,7 @@ constexpr int kDefaultChunk = 64;
 constexpr int64_t kTargetWorkgroups = 1024;
 // Launch-size limits (grid.x * block.x must stay below 2^32 work-items).
 constexpr int64_t kMaxWorkgroups = (int64_t)1 << 23;
+constexpr int64_t kMaxHeads = (int64_t)1 << 20;  // sequences x heads of one call
 
 struct Range {
   uintptr_t lo, hi;
@@ -58,13 +63,75 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   if (cps < sub) cps = sub;
   if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
-  if (bh * nseg > kMaxWorkgroups || bh > ((int64_t)1 << 20)) return false;
+  if (bh * nseg > kMaxWorkgroups || bh > kMaxHeads) return false;
   plan->C = C;
   plan->nchunks = (int)nchunks;
   plan->cps = (int)cps;
   plan->nseg = (int)nseg;
+  plan->nwork = (int64_t)B * nseg;
   plan->ws_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
   return true;
+}
+
+// Host plan of a variable-length batch: the segment, sequence and single-token
+// tables and where they and the segment states sit in the workspace.
+struct VarlenPlan {
+  PrefillPlan plan;
+  std::vector<SegDesc> segs;
+  std::vector<SeqDesc> seqs;
+  std::vector<DecDesc> decs;
+  size_t seq_off = 0, dec_off = 0, table_bytes = 0, state_off = 0;
+};
+
+static size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+la_status plan_varlen(int nseq, const int32_t* cu, const int64_t* pos0, int H, int chunk, VarlenPlan* vp) {
+  if (nseq < 1 || H < 1 || cu == nullptr) return cu == nullptr ? LA_ERR_NULL_PTR : LA_ERR_BAD_SHAPE;
+  if (nseq > (1 << 24) || (int64_t)nseq * H > kMaxHeads) return LA_ERR_BAD_SHAPE;
+  const int C = chunk == 0 ? kDefaultChunk : chunk;
+  if (C != 64 && C != 128 && C != 256) return LA_ERR_UNSUPPORTED;
+  if (cu[0] != 0) return LA_ERR_BAD_SHAPE;
+  int64_t sub_chunks = 0;
+  for (int b = 0; b < nseq; ++b) {
+    const int64_t len = (int64_t)cu[b + 1] - cu[b];
+    if (len < 0) return LA_ERR_BAD_SHAPE;
+    if (len >= 2) sub_chunks += (len + 63) / 64;
+  }
+  const int64_t sub = C / 64;
+  int64_t cps = ((int64_t)H * sub_chunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  cps = std::max<int64_t>(sub, (cps + sub - 1) / sub * sub);
+  vp->segs.clear();
+  vp->seqs.assign(nseq, SeqDesc{0, 0, 0, 0});
+  vp->decs.clear();
+  bool scan = false;
+  for (int b = 0; b < nseq; ++b) {
+    const int32_t t0 = cu[b], t1 = cu[b + 1];
+    const int64_t p0 = pos0 ? pos0[b] : 0;
+    if (t1 - t0 == 1) {
+      vp->seqs[b].decode = 1;
+      vp->decs.push_back(DecDesc{b, t0, p0});
+      continue;
+    }
+    scan = true;
+    vp->seqs[b].first_seg = (int32_t)vp->segs.size();
+    for (int64_t t = t0, s = 0; t < t1; t += cps * 64, ++s) {
+      vp->segs.push_back(SegDesc{b, (int32_t)t, (int32_t)std::min<int64_t>(t1, t + cps * 64), (int32_t)s, p0 - t0});
+      vp->seqs[b].nseg += 1;
+    }
+  }
+  const int64_t nsegs = (int64_t)vp->segs.size();
+  if (nsegs * H > kMaxWorkgroups || (int64_t)vp->decs.size() * H > ((int64_t)1 << 30)) return LA_ERR_BAD_SHAPE;
+  vp->plan = PrefillPlan{};
+  vp->plan.C = C;
+  vp->plan.cps = (int)cps;
+  vp->plan.nwork = nsegs;
+  vp->plan.scan = scan;
+  vp->seq_off = round_up(nsegs * sizeof(SegDesc), 16);
+  vp->dec_off = round_up(vp->seq_off + nseq * sizeof(SeqDesc), 16);
+  vp->table_bytes = vp->dec_off + vp->decs.size() * sizeof(DecDesc);
+  vp->state_off = round_up(vp->table_bytes, 256);
+  vp->plan.ws_bytes = vp->state_off + (size_t)nsegs * H * kHeadDim * kHeadDim * sizeof(float);
+  return LA_OK;
 }
 
 }  // namespace la
@@ -131,6 +198,8 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
   p.g = gate_logits;
   p.o = o;
   p.ws = static_cast<float*>(workspace);
+  p.segs = nullptr;
+  p.seqs = nullptr;
   p.S_in = S_in;
   p.S_out = S_out;
   p.qw = q_norm_w;
@@ -195,6 +264,9 @@ la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
   p.g = gate_logits;
   p.o = o;
   p.S = S;
+  p.S_in = nullptr;
+  p.S_zero = false;
+  p.rows = nullptr;
   p.qw = q_norm_w;
   p.kw = k_norm_w;
   p.B = B;
@@ -203,6 +275,100 @@ la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
   p.eps = rms_eps;
   rope_freqs(rope_base, &p.freqs);
   return launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+size_t la_prefill_varlen_workspace_bytes(int nseq, const int32_t* cu_seqlens, int H, int D, int chunk) {
+  VarlenPlan vp;
+  if (D != kHeadDim || plan_varlen(nseq, cu_seqlens, nullptr, H, chunk, &vp) != LA_OK) return 0;
+  return vp.plan.ws_bytes;
+}
+
+la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                            const la_bf16* gate_logits, const int32_t* cu_seqlens, const int64_t* pos0,
+                            const float* S_in, float* S_out, la_bf16* o, int nseq, int total_T, int H,
+                            int D, int chunk, float rope_base, float rms_eps, const float* q_norm_w,
+                            const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!S_out || !workspace || !cu_seqlens) return LA_ERR_NULL_PTR;
+  if (total_T > 0 && (!q || !k || !v || !gate_logits || !o)) return LA_ERR_NULL_PTR;
+  if (nseq < 1 || H < 1 || total_T < 0) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  VarlenPlan vp;
+  const la_status planned = plan_varlen(nseq, cu_seqlens, pos0, H, chunk, &vp);
+  if (planned != LA_OK) return planned;
+  if (cu_seqlens[nseq] != total_T) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const uint64_t act = (uint64_t)total_T * H * D * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)nseq * H * D * D * sizeof(float);
+  const void* ins[] = {q, k, v, gate_logits};
+  for (const void* in : ins) {
+    if (overlaps(o, act, in, act) || overlaps(S_out, st, in, act)) return LA_ERR_ALIASING;
+  }
+  if (overlaps(o, act, S_out, st) || overlaps(o, act, S_in, st)) return LA_ERR_ALIASING;
+  if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;
+  const void* all[] = {q, k, v, gate_logits, S_in, S_out, o};
+  for (const void* x : all)
+    if (overlaps(workspace, vp.plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
+  if (workspace_bytes < vp.plan.ws_bytes) return LA_ERR_WORKSPACE;
+
+  // the tables go to the front of the workspace, in stream order
+  std::vector<uint8_t> tables(vp.table_bytes, 0);
+  if (!vp.segs.empty()) memcpy(tables.data(), vp.segs.data(), vp.segs.size() * sizeof(SegDesc));
+  memcpy(tables.data() + vp.seq_off, vp.seqs.data(), vp.seqs.size() * sizeof(SeqDesc));
+  if (!vp.decs.empty()) memcpy(tables.data() + vp.dec_off, vp.decs.data(), vp.decs.size() * sizeof(DecDesc));
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(ws, tables.data(), tables.size(), hipMemcpyHostToDevice, s) != hipSuccess) return LA_ERR_HIP;
+
+  RopeFreqs freqs;
+  rope_freqs(rope_base, &freqs);
+  if (vp.plan.scan || vp.plan.nwork > 0) {
+    PrefillParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = gate_logits;
+    p.o = o;
+    p.ws = reinterpret_cast<float*>(ws + vp.state_off);
+    p.segs = reinterpret_cast<const SegDesc*>(ws);
+    p.seqs = reinterpret_cast<const SeqDesc*>(ws + vp.seq_off);
+    p.S_in = S_in;
+    p.S_out = S_out;
+    p.qw = q_norm_w;
+    p.kw = k_norm_w;
+    p.B = nseq;
+    p.T = total_T;
+    p.H = H;
+    p.nseg = 0;
+    p.cps = vp.plan.cps;
+    p.pos0 = 0;
+    p.eps = rms_eps;
+    p.freqs = freqs;
+    if (launch_prefill(p, vp.plan, s) != hipSuccess) return LA_ERR_HIP;
+  }
+  if (!vp.decs.empty()) {
+    DecodeParams d;
+    d.q = q;
+    d.k = k;
+    d.v = v;
+    d.g = gate_logits;
+    d.o = o;
+    d.S = S_out;
+    d.S_in = S_in;
+    d.S_zero = S_in == nullptr;
+    d.rows = reinterpret_cast<const DecDesc*>(ws + vp.dec_off);
+    d.qw = q_norm_w;
+    d.kw = k_norm_w;
+    d.B = (int)vp.decs.size();
+    d.H = H;
+    d.pos = 0;
+    d.eps = rms_eps;
+    d.freqs = freqs;
+    if (launch_decode(d, s) != hipSuccess) return LA_ERR_HIP;
+  }
+  return LA_OK;
 }
 
 }  // extern "C"

@@ -28,16 +28,27 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
 
   const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;  // b * H + h
-  const int64_t tok = bh * kD;     // [B, H, D] offset of this (b, h)
+  // token row and state of this (b, h): row b of [B, H, D] inputs and state b, or
+  // for a packed batch the row and sequence of single-token sequence b
+  int64_t tok = bh * kD, sbh = bh, pos = p.pos;
+  if (p.rows != nullptr) {
+    const DecDesc d = p.rows[bh / p.H];
+    const int64_t h = bh % p.H;
+    tok = ((int64_t)d.t * p.H + h) * kD;
+    sbh = (int64_t)d.seq * p.H + h;
+    pos = d.pos;
+  }
 
   const int cg = tid & 31;  // value columns 4cg .. 4cg + 3
   const int rgp = tid >> 5; // key rows rgp + 8 m
-  float4* Sbh = reinterpret_cast<float4*>(p.S + bh * kD * kD);
+  float4* Sbh = reinterpret_cast<float4*>(p.S + sbh * kD * kD);
+  const float4* Sin = reinterpret_cast<const float4*>((p.S_in ? p.S_in : p.S) + sbh * kD * kD);
 
   // Issue the state loads first; the prologue overlaps their latency.
   float4 sreg[kRowsPerThread];
 #pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m) sreg[m] = Sbh[(rgp + kRowGroups * m) * (kD / 4) + cg];
+  for (int m = 0; m < kRowsPerThread; ++m)
+    sreg[m] = p.S_zero ? make_float4(0.f, 0.f, 0.f, 0.f) : Sin[(rgp + kRowGroups * m) * (kD / 4) + cg];
 
   if (tid < 64) {
     // wave 0: RMSNorm + RoPE of q and k; lane i holds the rotate-half pair (i, i + 64)
@@ -55,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void la_decode_kernel(DecodeParams p) {
     q1 *= iq * (p.qw ? p.qw[i + kHalf] : 1.f);
     k0 *= ik * (p.kw ? p.kw[i] : 1.f);
     k1 *= ik * (p.kw ? p.kw[i + kHalf] : 1.f);
-    const float2 rot = rope_rotation(p.pos, p.freqs.rev[i]);
+    const float2 rot = rope_rotation(pos, p.freqs.rev[i]);
     sq[i] = q0 * rot.x - q1 * rot.y;
     sq[i + kHalf] = q1 * rot.x + q0 * rot.y;
     sk[i] = k0 * rot.x - k1 * rot.y;

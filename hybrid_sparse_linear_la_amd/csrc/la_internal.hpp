@@ -24,11 +24,35 @@ struct PrefillPlan {
   int C = 0;        // chunk length: 64, 128 or 256
   int nchunks = 0;  // ceil(T / 64)
   int cps = 0;      // 64-token sub-chunks per segment
-  int nseg = 0;     // segments per (b, h)
+  int nseg = 0;     // segments per (b, h) (equal-length batches)
+  int64_t nwork = 0;  // segment workgroups per head: B * nseg, or the table's segments
+  bool scan = true;   // launch the state scan
   size_t ws_bytes = 0;
 };
 
 bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan);
+
+// Variable-length batches (packed [total_T, H, D] activations).  The host cuts
+// every sequence of two or more tokens into segments and sends the tables below
+// to the device in the workspace; single-token sequences take the decode kernel.
+struct SegDesc {      // one segment: its workgroups are blockIdx = h + H * (index)
+  int32_t seq;        // sequence
+  int32_t t_begin;    // packed token range [t_begin, t_end)
+  int32_t t_end;
+  int32_t seg_local;  // segment number within the sequence
+  int64_t pos_base;   // absolute position of packed token 0 for this sequence
+};
+struct SeqDesc {      // one sequence, for the state scan
+  int32_t first_seg;  // index of its first segment
+  int32_t nseg;       // 0 for an empty sequence (S_out = S_in)
+  int32_t decode;     // 1: a single-token sequence handled by the decode kernel
+  int32_t pad;
+};
+struct DecDesc {      // one single-token sequence
+  int32_t seq;
+  int32_t t;          // its packed token
+  int64_t pos;        // absolute position
+};
 
 struct PrefillParams {
   const uint16_t* q;
@@ -36,7 +60,9 @@ struct PrefillParams {
   const uint16_t* v;
   const uint16_t* g;
   uint16_t* o;
-  float* ws;          // [B][H][nseg][D][D] fp32 segment states
+  float* ws;          // fp32 segment states: [B][H][nseg][D][D], or [segment][H][D][D] with segs
+  const SegDesc* segs;  // nullptr: B sequences of T tokens; else one entry per segment
+  const SeqDesc* seqs;  // with segs: one entry per sequence
   const float* S_in;  // [B][H][D][D] or nullptr
   float* S_out;       // [B][H][D][D]
   const float* qw;    // [D] or nullptr
@@ -53,7 +79,10 @@ struct DecodeParams {
   const uint16_t* v;
   const uint16_t* g;
   uint16_t* o;
-  float* S;
+  float* S;             // state written (and read when S_in is nullptr)
+  const float* S_in;    // nullptr: update S in place
+  bool S_zero;          // the state before the step is zero (S_in and S are not read)
+  const DecDesc* rows;  // nullptr: B rows [B][H][D]; else B entries into packed [*, H, D] rows
   const float* qw;
   const float* kw;
   int B, H;

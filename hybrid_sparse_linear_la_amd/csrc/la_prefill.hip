@@ -245,20 +245,38 @@ __device__ __forceinline__ void load_norm_weights(const float* w, int j, float (
 
 struct Tile {
   int b, h, seg, t_begin, t_end, nch;
-  int64_t base;  // element offset of (b, t = 0, h, d = 0)
+  int64_t base;      // element offset of (row 0, h, d = 0) for the rows of this tile's sequence
+  int64_t pos_base;  // absolute position of row 0 in those rows
+  float* state;      // this (b, h, segment)'s D x D state in the workspace
 };
 
+// Workgroup -> (b, h, segment).  Equal-length batches: blockIdx = h + H (seg +
+// nseg b), rows t of sequence b.  Variable-length batches: blockIdx = h + H s for
+// segment s of the table, rows t of the packed activations.
 __device__ __forceinline__ Tile decode_tile(const PrefillParams& p) {
   Tile tl;
   int bid = blockIdx.x;
   tl.h = bid % p.H;
   bid /= p.H;
-  tl.seg = bid % p.nseg;
-  tl.b = bid / p.nseg;
-  tl.t_begin = tl.seg * p.cps * kC;
-  tl.t_end = min(p.T, tl.t_begin + p.cps * kC);
+  if (p.segs != nullptr) {
+    const SegDesc d = p.segs[bid];
+    tl.b = d.seq;
+    tl.seg = d.seg_local;
+    tl.t_begin = d.t_begin;
+    tl.t_end = d.t_end;
+    tl.base = (int64_t)tl.h * kD;
+    tl.pos_base = d.pos_base;
+    tl.state = p.ws + ((int64_t)bid * p.H + tl.h) * kD * kD;
+  } else {
+    tl.seg = bid % p.nseg;
+    tl.b = bid / p.nseg;
+    tl.t_begin = tl.seg * p.cps * kC;
+    tl.t_end = min(p.T, tl.t_begin + p.cps * kC);
+    tl.base = ((int64_t)tl.b * p.T * p.H + tl.h) * kD;
+    tl.pos_base = p.pos0;
+    tl.state = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
+  }
   tl.nch = (tl.t_end - tl.t_begin + kC - 1) / kC;
-  tl.base = ((int64_t)tl.b * p.T * p.H + tl.h) * kD;
   return tl;
 }
 
@@ -319,7 +337,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
     load_rows<2, 32>(p.k + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Kr);
     load_rows<2, 32>(p.v + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Vr);
   }
-  if (tid < kHalf) sRot[0][tid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
+  if (tid < kHalf) sRot[0][tid] = rope_rotation(tl.pos_base + tl.t_begin, L.base_rev);
   __syncthreads();
 
   for (int c = 0; c < tl.nch; ++c) {
@@ -334,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
       const int nv1 = min(kC, tl.t_end - t1);
       load_rows<2, 32>(p.k + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Kr);
       load_rows<2, 32>(p.v + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Vr);
-      if (tid < kHalf) sRot[(c + 1) & 1][tid] = rope_rotation(p.pos0 + t1, L.base_rev);
+      if (tid < kHalf) sRot[(c + 1) & 1][tid] = rope_rotation(tl.pos_base + t1, L.base_rev);
     }
     __syncthreads();
     bf16x8 Vop[2];
@@ -343,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
     accumulate_state(Sacc, bK, Vop, g4, n16);
   }
 
-  float* dst = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
+  float* dst = tl.state;
 #pragma unroll
   for (int rtk = 0; rtk < 8; ++rtk)
 #pragma unroll
@@ -353,16 +371,27 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
 // --------------------------------------------------------------------------
 // Exclusive prefix of the per-segment states, in place, seeded with S_in; the
 // inclusive total is the final state.  One thread per 4 consecutive elements.
+// A variable-length batch walks each sequence's own run of segments (none for an
+// empty sequence, whose final state is S_in) and skips single-token sequences.
 __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
   constexpr int64_t per = kD * kD / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)p.B * p.H * per) return;
   const int64_t bh = idx / per, e = idx - bh * per;
-  float4 run = p.S_in ? reinterpret_cast<const float4*>(p.S_in)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+  int nseg = p.nseg;
   float4* ws = reinterpret_cast<float4*>(p.ws) + bh * p.nseg * per + e;
-  for (int s = 0; s < p.nseg; ++s) {
-    const float4 d = ws[s * per];
-    ws[s * per] = run;
+  int64_t stride = per;
+  if (p.seqs != nullptr) {
+    const SeqDesc d = p.seqs[bh / p.H];
+    if (d.decode) return;
+    nseg = d.nseg;
+    ws = reinterpret_cast<float4*>(p.ws) + ((int64_t)d.first_seg * p.H + bh % p.H) * per + e;
+    stride = (int64_t)p.H * per;
+  }
+  float4 run = p.S_in ? reinterpret_cast<const float4*>(p.S_in)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nseg; ++s) {
+    const float4 d = ws[s * stride];
+    ws[s * stride] = run;
     run.x += d.x;
     run.y += d.y;
     run.z += d.z;
@@ -429,7 +458,7 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
       stage(c + 1, R);
       if (c + 3 < tl.nch) load_chunk(c + 3, R);
       if (c + 2 < tl.nch && ptid < kHalf)
-        sRot[c & 1][ptid] = rope_rotation(p.pos0 + tl.t_begin + (c + 2) * kC, L.base_rev);
+        sRot[c & 1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + (c + 2) * kC, L.base_rev);
     }
     __syncthreads();
     __syncthreads();
@@ -437,8 +466,8 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
 
   load_chunk(0, Y);
   if (ptid < kHalf) {
-    sRot[0][ptid] = rope_rotation(p.pos0 + tl.t_begin, L.base_rev);
-    if (tl.nch > 1) sRot[1][ptid] = rope_rotation(p.pos0 + tl.t_begin + kC, L.base_rev);
+    sRot[0][ptid] = rope_rotation(tl.pos_base + tl.t_begin, L.base_rev);
+    if (tl.nch > 1) sRot[1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + kC, L.base_rev);
   }
   __syncthreads();
   stage(0, Y);
@@ -563,7 +592,7 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
   // prefix state of this segment: S[:, 32w + 16 dt .. + 16) in accumulator tiles
   f32x4 Sacc[2][8];
   {
-    const float* src = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
+    const float* src = tl.state;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -655,13 +684,13 @@ __global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(P
   // rotations of row rg of a sub-block starting at token t
   auto first_rows = [&](int t, float2 (&E)[4]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(p.pos0 + t, rev[e]), L.A[e]);
+    for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t, rev[e]), L.A[e]);
   };
 
   // prefix state of this segment: S[:, 16 w .. 16 w + 16)
   f32x4 Sacc[8];
   {
-    const float* src = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
+    const float* src = tl.state;
 #pragma unroll
     for (int rtk = 0; rtk < 8; ++rtk)
 #pragma unroll
@@ -782,7 +811,7 @@ __global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(P
 
 hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipStream_t stream,
                           hipEvent_t const* events) {
-  const dim3 grid((unsigned)((int64_t)p.B * p.H * plan.nseg));
+  const dim3 grid((unsigned)(plan.nwork * p.H));
   const int64_t scan_threads = (int64_t)p.B * p.H * kD * kD / 4;
   const bool weights = p.qw != nullptr || p.kw != nullptr;
   hipError_t err = hipSuccess;
@@ -790,25 +819,28 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
     if (events && err == hipSuccess) err = hipEventRecord(events[i], stream);
   };
   mark(0);
-  if (weights)
-    hipLaunchKernelGGL(la_chunk_state_kernel<true>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(la_chunk_state_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  if (plan.nwork > 0) {
+    if (weights)
+      hipLaunchKernelGGL(la_chunk_state_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL(la_chunk_state_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+  }
   mark(1);
-  hipLaunchKernelGGL(la_state_scan_kernel, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
-                     stream, p);
+  if (plan.scan)
+    hipLaunchKernelGGL(la_state_scan_kernel, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
+                       stream, p);
   mark(2);
-  if (plan.C == kC) {
+  if (plan.nwork > 0 && plan.C == kC) {
     if (weights)
       hipLaunchKernelGGL(la_chunk_output_kernel<true>, grid, dim3(kOutThreads), 0, stream, p);
     else
       hipLaunchKernelGGL(la_chunk_output_kernel<false>, grid, dim3(kOutThreads), 0, stream, p);
-  } else if (plan.C == 2 * kC) {
+  } else if (plan.nwork > 0 && plan.C == 2 * kC) {
     if (weights)
       hipLaunchKernelGGL((la_chunk_output_wide_kernel<true, 2>), grid, dim3(kWideThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((la_chunk_output_wide_kernel<false, 2>), grid, dim3(kWideThreads), 0, stream, p);
-  } else {
+  } else if (plan.nwork > 0) {
     if (weights)
       hipLaunchKernelGGL((la_chunk_output_wide_kernel<true, 4>), grid, dim3(kWideThreads), 0, stream, p);
     else

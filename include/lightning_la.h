@@ -123,6 +123,41 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
                               void* stream, void* const* events, int n_events);
 
 /*
+ * Variable-length batch ("varlen"): nseq sequences packed along the token axis,
+ * for ragged prefill batches and for mixed batches of prefill chunks and decode
+ * steps.  Sequence b owns packed tokens [cu_seqlens[b], cu_seqlens[b + 1]) of
+ * q, k, v, gate_logits and o ([total_T, H, D] bf16), starts at absolute
+ * position pos0[b] and carries its own state S_in[b] -> S_out[b] ([nseq, H, D, D]
+ * fp32).  Each sequence gets what la_prefill (or, for one token, la_decode_step)
+ * gives it alone; the length mix only changes how the work is cut up.  The pages
+ * time prefill (time to first token) and prefill plus decode ("創新Transformer！
+ * 面壁基於稀疏-線性混合架構SALA訓練9B模型，端側跑通百萬上下文", 05 計算效率測試) and
+ * name batching and concurrent requests as unstudied ("MiniCPM-SALA: Hybridizing
+ * Sparse and Linear Attention for Efficient Long-Context Modeling", 独立分析的弱点);
+ * this entry point is the batched form of the same layer.
+ *   cu_seqlens : HOST int32 [nseq + 1]: cu_seqlens[0] = 0, nondecreasing,
+ *                cu_seqlens[nseq] = total_T.  A sequence may be empty (its
+ *                S_out[b] = S_in[b]) or a single token (a decode step: the
+ *                decode kernel serves it).
+ *   pos0       : HOST int64 [nseq], or NULL for all zeros.
+ *   q, k, v, gate_logits, o may be NULL when total_T == 0.
+ *   S_in       : device [nseq, H, D, D] or NULL (zeros); may equal S_out.
+ *   chunk, rope_base, rms_eps, q_norm_w, k_norm_w : as for la_prefill.
+ *   workspace  : at least la_prefill_varlen_workspace_bytes(...) bytes.
+ * The call builds its work tables on the host and copies them into the front
+ * of the workspace with hipMemcpyAsync on `stream` before the kernels, so it
+ * returns once that (pageable) copy has been staged.  Errors as for la_prefill;
+ * LA_ERR_BAD_SHAPE also covers malformed cu_seqlens.
+ */
+size_t la_prefill_varlen_workspace_bytes(int nseq, const int32_t* cu_seqlens, int H, int D, int chunk);
+
+la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                            const la_bf16* gate_logits, const int32_t* cu_seqlens, const int64_t* pos0,
+                            const float* S_in, float* S_out, la_bf16* o, int nseq, int total_T, int H,
+                            int D, int chunk, float rope_base, float rms_eps, const float* q_norm_w,
+                            const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: one token per sequence at absolute position pos.
  *   q, k, v, gate_logits : [B, H, D] bf16.
  *   S : [B, H, D, D] fp32 state, updated in place (S += kh v^T).

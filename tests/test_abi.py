@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
-         "la_decode_step"])
+         "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -91,6 +91,58 @@ def test_prefill_validation(lib):
     assert _prefill(lib, S_in=A + 256 * MB + 16, S_out=A + 256 * MB) == 5  # partial overlap
     assert _prefill(lib, ws=A + 320 * MB + 64) == 5      # workspace overlaps o
     assert _prefill(lib, ws_bytes=1024) == 6
+
+
+def _cu(values):
+    return (ctypes.c_int32 * len(values))(*values)
+
+
+def _varlen(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, g=A + 192 * MB, cu=(0, 5, 5, 70), pos0=None,
+            S_in=None, S_out=A + 256 * MB, o=A + 320 * MB, nseq=None, total_T=None, H=2, D=128, chunk=0,
+            base=10000.0, eps=1e-6, qw=None, ws=A + 1024 * MB, ws_bytes=1 << 30):
+    vp = ctypes.c_void_p
+    cu_arr = None if cu is None else _cu(list(cu))
+    nseq = len(cu) - 1 if nseq is None else nseq
+    total_T = cu[-1] if total_T is None else total_T
+    p0 = None if pos0 is None else (ctypes.c_int64 * len(pos0))(*pos0)
+    return lib.la_prefill_varlen(vp(q), vp(k), vp(v), vp(g), cu_arr, p0, vp(S_in), vp(S_out), vp(o), nseq,
+                                 total_T, H, D, chunk, base, eps, vp(qw), None, vp(ws), ws_bytes, None)
+
+
+def test_varlen_workspace_bytes(lib):
+    import hybrid_sparse_linear_la_amd as la
+    f = lib.la_prefill_varlen_workspace_bytes
+    # one 2-token sequence: one segment per head after a 256-byte table area
+    assert f(1, _cu([0, 2]), 2, 128, 0) == 256 + 2 * 128 * 128 * 4
+    # single-token and empty sequences need no segment states
+    assert f(3, _cu([0, 1, 1, 2]), 2, 128, 0) == 256
+    # equal lengths: the same 10 segments as la_prefill, after 10 x 24 + 2 x 16 bytes of
+    # tables rounded up to 512
+    assert f(2, _cu([0, 300, 600]), 2, 128, 0) - 512 == lib.la_prefill_workspace_bytes(2, 300, 2, 128, 0)
+    assert f(2, _cu([0, 3, 2]), 2, 128, 0) == 0   # decreasing offsets
+    assert f(1, _cu([1, 3]), 2, 128, 0) == 0      # does not start at 0
+    assert f(1, _cu([0, 3]), 2, 64, 0) == 0
+    assert f(1, _cu([0, 3]), 2, 128, 96) == 0
+    assert la.prefill_varlen_workspace_bytes([0, 1, 300, 300, 5000], 32) > 0
+
+
+def test_varlen_validation(lib):
+    import hybrid_sparse_linear_la_amd  # noqa: F401
+    assert _varlen(lib, q=None) == 1
+    assert _varlen(lib, cu=None, nseq=3, total_T=70) == 1
+    assert _varlen(lib, ws=None) == 1
+    assert _varlen(lib, nseq=0, total_T=0) == 2
+    assert _varlen(lib, cu=(0, 5, 4, 70)) == 2          # decreasing
+    assert _varlen(lib, cu=(2, 5, 5, 70)) == 2          # first offset not 0
+    assert _varlen(lib, total_T=71) == 2                # last offset != total_T
+    assert _varlen(lib, D=64) == 3
+    assert _varlen(lib, chunk=96) == 3
+    assert _varlen(lib, eps=-1.0) == 3
+    assert _varlen(lib, k=A + 64 * MB + 8) == 4
+    assert _varlen(lib, o=A + 64) == 5                  # o overlaps q
+    assert _varlen(lib, S_in=A + 256 * MB + 16) == 5    # S_in partly overlaps S_out
+    assert _varlen(lib, ws=A + 320 * MB + 256) == 5     # workspace overlaps o
+    assert _varlen(lib, ws_bytes=16) == 6
 
 
 def _decode(lib, q=A, k=A + MB, v=A + 2 * MB, g=A + 3 * MB, S=A + 4 * MB, o=A + 512 * MB, B=2, H=2,

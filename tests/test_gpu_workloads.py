@@ -8,7 +8,9 @@ benchmark times (default chunk, B = 1, 32 heads x 128):
     one single-shot call, and sampled heads against the oracle streamed segment by
     segment;
   * batched decode (64 sequences x 32 heads, 1000 steps from position 262144):
-    o at every step and S after steps 1, 10 and 1000 against the oracle.
+    o at every step and S after steps 1, 10 and 1000 against the oracle;
+  * a packed serving batch (4 prompts of 16384 tokens and 60 decode steps) in one
+    variable-length call: every decode row and sampled prompt heads.
 """
 import numpy as np
 import pytest
@@ -122,3 +124,33 @@ def test_decode_b64_1000_steps(la):
     eo = assert_o_close(to_np(outs[:, bs].transpose(0, 1)), o_ref, what="o over 1000 steps")
     es = assert_S_close(to_np(S[bs]), S_ref, what="S after 1000 steps")
     print(f"decode parity o {eo} S {es}", flush=True)
+
+
+def test_serving_mix_varlen(la):
+    """The packed serving batch the benchmark times (4 x 16384-token prompts from
+    position 0 and 60 decode steps at position 262144, one la_prefill_varlen call):
+    every decode row and its state, and sampled heads of the prompts, against the
+    oracle."""
+    w = workloads.SERVING_MIX
+    print(f"workload {w.name}", flush=True)
+    q, k, v, g, S_in, cu = workloads.mixed_inputs(w, "cuda")
+    o, S_out = la.prefill_varlen(q, k, v, g, cu, pos0=list(w.pos0), S_in=S_in)
+    torch.cuda.synchronize()
+    n_pre = sum(1 for n in w.lengths if n > 1)
+    # decode rows: all sequences and heads, one oracle step each
+    t_dec = cu[n_pre:-1]
+    row = lambda t: to_np32(t[t_dec][:, None])  # noqa: E731  [n_dec, 1, H, D]
+    S_dec = to_np(S_in[n_pre:])
+    o_ref, S_ref = oracle.forward(row(q), row(k), row(v), row(g), S=S_dec, pos0=w.pos0[-1])
+    assert_o_close(to_np(o[t_dec][:, None]), o_ref, what="decode rows")
+    assert_S_close(to_np(S_out[n_pre:]), S_ref, what="decode states")
+    # prompts: heads 0 and 21 of the first and last prompt
+    for b in (0, n_pre - 1):
+        t0, t1 = cu[b], cu[b + 1]
+        for h in (0, 21):
+            sl = lambda t: to_np32(t[t0:t1, h:h + 1][None])  # noqa: E731
+            o_ref, S_ref = oracle.forward(sl(q), sl(k), sl(v), sl(g), S=to_np(S_in[b:b + 1, h:h + 1]),
+                                          pos0=w.pos0[b])
+            eo = assert_o_close(to_np(o[t0:t1, h:h + 1][None]), o_ref, what=f"prompt {b} head {h}")
+            assert_S_close(to_np(S_out[b:b + 1, h:h + 1]), S_ref, what=f"prompt {b} head {h} state")
+            print(f"serving mix prompt {b} head {h}: o {eo}", flush=True)

@@ -49,6 +49,37 @@ DECODE_B64 = Workload("decode_b64_h32_d128_pos262144", 64, 1, 32, 128, seed=4, p
 ALL = (TINY, PREFILL_32K, PREFILL_256K, STREAM_1M, DECODE_B64)
 
 
+@dataclasses.dataclass(frozen=True)
+class MixedBatch:
+    """A packed variable-length batch: prefill sequences and single-token decode
+    steps side by side, as a serving step schedules them."""
+    name: str
+    lengths: tuple
+    pos0: tuple
+    H: int
+    D: int
+    seed: int
+    state_std: float
+
+
+# Serving mix: four 16K-token prompts being prefilled from position 0 while 60
+# sequences decode one token each at position 262144 (their states ~ N(0, 0.02^2)).
+SERVING_MIX = MixedBatch("mixed_4x16384_prefill_60x1_decode_h32_d128", (16384,) * 4 + (1,) * 60,
+                         (0,) * 4 + (262144,) * 60, 32, 128, seed=5, state_std=0.02)
+
+
+def mixed_inputs(w: MixedBatch, device="cpu"):
+    """(q, k, v, g [total_T, H, D] bf16, S_in [nseq, H, D, D] fp32, cu_seqlens list)."""
+    gen = generator(w.seed, device)
+    total = sum(w.lengths)
+    q, k, v, g = (x[0] for x in activations(1, total, w.H, w.D, w.seed, device, gen=gen))
+    S = state(len(w.lengths), w.H, w.D, w.state_std, gen, device)
+    cu = [0]
+    for n in w.lengths:
+        cu.append(cu[-1] + n)
+    return q, k, v, g, S, cu
+
+
 def generator(seed: int, device="cpu") -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
