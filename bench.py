@@ -17,6 +17,8 @@ Prints one JSON line (rank 0, N = 1):
   prefill_detail.chunk_sweep  the same prefill at chunk 64, 128 and 256
   varlen    a packed serving batch (4 x 16K-token prompts + 60 decode steps) in
             one la_prefill_varlen call, beside the same work as two calls
+  layer     one layer on a 32K-token prompt (hidden 4096): q/k/v/gate projection,
+            the layer, output projection; the projections against bf16 MFMA peak
 """
 from __future__ import annotations
 
@@ -310,6 +312,50 @@ def bench_varlen(la, torch, workloads, hip, args, steps=5):
             "hbm_roof_frac": round(comp / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4), **res}
 
 
+def bench_layer(la, torch, workloads, hip, args, steps=5):
+    """One layer on the 32K-token prompt: la_layer_forward, and its two projections
+    timed alone (la_linear with the same shapes) against the bf16 MFMA peak."""
+    w = workloads.LAYER_32K
+    x, w_qkvg, w_o = workloads.layer_inputs(w.B, w.T, w.hidden, w.H, w.D, w.seed, "cuda")
+    M, HD = w.B * w.T, w.H * w.D
+    y = torch.empty_like(x)
+    S_out = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(la.layer_workspace_bytes(w.B, w.T, w.H), dtype=torch.uint8, device="cuda")
+    proj = torch.empty((M, 4 * HD), dtype=torch.bfloat16, device="cuda")
+    o = torch.randn((M, HD), device="cuda").to(torch.bfloat16)
+    y2 = torch.empty((M, w.hidden), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
+        e = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(e[0], stream)
+        for _ in range(steps):
+            fn()
+        hip.record(e[1], stream)
+        ms = hip.ms(e[0], e[1]) / steps
+        hip.destroy(e)
+        return ms
+
+    layer_ms = timed(lambda: la.layer_forward(x, w_qkvg, w_o, out=y, S_out=S_out, workspace=ws))
+    in_ms = timed(lambda: la.linear(x.view(M, w.hidden), w_qkvg, out=proj))
+    out_ms = timed(lambda: la.linear(o, w_o, out=y2))
+    f_in, f_out = 2 * M * 4 * HD * w.hidden, 2 * M * w.hidden * HD
+    tf_in = f_in / (in_ms / 1e3) / 1e12
+    return {
+        "workload": w.name, "tokens": M, "steps": steps,
+        "layer_ms": round(layer_ms, 4), "tokens_per_s": round(M / (layer_ms / 1e3), 1),
+        "qkvg_projection": {"ms": round(in_ms, 4), "tflops": round(tf_in, 1),
+                            "roofline": {"bound": "mfma", "kernel": "la_linear_kernel", "achieved": round(tf_in, 1),
+                                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": round(tf_in / BF16_MFMA_PEAK_TFLOPS, 4)}},
+        "o_projection": {"ms": round(out_ms, 4), "tflops": round(f_out / (out_ms / 1e3) / 1e12, 1),
+                         "frac_of_bf16_peak": round(f_out / (out_ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
+        "attention_ms": round(layer_ms - in_ms - out_ms, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,6 +368,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-varlen", action="store_true", help="skip the mixed prefill/decode batch")
+    ap.add_argument("--no-layer", action="store_true", help="skip the layer forward with its projections")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -353,6 +400,7 @@ def main():
     w, tps, step_s, roofline, detail, tensors = bench_prefill(la, torch, workloads, hip, args)
     decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
     varlen = None if args.no_varlen else bench_varlen(la, torch, workloads, hip, args)
+    layer = None if args.no_layer else bench_layer(la, torch, workloads, hip, args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
@@ -374,6 +422,7 @@ def main():
         "prefill_detail": detail,
         "decode": decode,
         "varlen": varlen,
+        "layer": layer,
     }
     print(json.dumps(line), flush=True)
 

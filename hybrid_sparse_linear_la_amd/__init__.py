@@ -10,6 +10,8 @@ is missing, every call raises.
     o, S_out = prefill(q, k, v, gate, S_in=None, pos0=0)
     o = decode_step(q, k, v, gate, S, pos)        # S updated in place
     o, S_out = prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None)
+    y = linear(x, w)                              # y = x w^T
+    y, S_out = layer_forward(x, w_qkvg, w_o, S_in=None, pos0=0)
 """
 from __future__ import annotations
 
@@ -18,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "prefill_varlen", "prefill_workspace_bytes",
+__all__ = ["prefill", "decode_step", "prefill_varlen", "linear", "layer_forward", "prefill_workspace_bytes",
+           "layer_workspace_bytes",
            "prefill_varlen_workspace_bytes", "LAError", "library", "lib_path",
            "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS"]
 
@@ -68,6 +71,13 @@ def library():
         lib.la_prefill_varlen.restype = ctypes.c_int
         lib.la_prefill_varlen.argtypes = [_vp] * 9 + [ctypes.c_int] * 5 + [
             ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.la_linear.restype = ctypes.c_int
+        lib.la_linear.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, _vp]
+        lib.la_layer_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_layer_workspace_bytes.argtypes = [ctypes.c_int] * 5
+        lib.la_layer_forward.restype = ctypes.c_int
+        lib.la_layer_forward.argtypes = [_vp] * 6 + [ctypes.c_int] * 5 + [
+            ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
             ctypes.c_int64, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
@@ -207,6 +217,71 @@ def prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None, chunk: int =
                                  _ptr(out), nseq, total_T, H, D, int(chunk), float(rope_base),
                                  float(rms_eps), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out, S_out
+
+
+def _bf16_2d(name, t):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
+
+
+def linear(x, w, out=None):
+    """y = x w^T.  x: bf16 [..., K] (contiguous), w: bf16 [N, K].  Returns bf16 [..., N]."""
+    _bf16_2d("x", x)
+    _bf16_2d("w", w)
+    if w.dim() != 2 or x.shape[-1] != w.shape[1]:
+        raise ValueError(f"x [..., K] and w [N, K] do not match: {tuple(x.shape)}, {tuple(w.shape)}")
+    N, K = w.shape
+    M = x.numel() // K
+    if out is None:
+        out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
+    else:
+        _bf16_2d("out", out)
+        if out.numel() != M * N:
+            raise ValueError("out has the wrong size")
+    _check(library().la_linear(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(x.device)))
+    return out
+
+
+def layer_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, chunk: int = 0) -> int:
+    return int(library().la_layer_workspace_bytes(B, T, H, D, chunk))
+
+
+def layer_forward(x, w_qkvg, w_o, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: float = 10000.0,
+                  rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None, out=None, S_out=None, workspace=None):
+    """One layer: [q|k|v|g] = x w_qkvg^T, la_prefill, y = o w_o^T.  x: bf16 [B, T, hidden];
+    w_qkvg: bf16 [4 H 128, hidden]; w_o: bf16 [hidden, H 128].  Returns (y, S_out)."""
+    lib = library()
+    _bf16_2d("x", x)
+    _bf16_2d("w_qkvg", w_qkvg)
+    _bf16_2d("w_o", w_o)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, hidden]")
+    B, T, hidden = x.shape
+    HD = w_o.shape[1]
+    if HD % HEAD_DIM or tuple(w_qkvg.shape) != (4 * HD, hidden) or tuple(w_o.shape) != (hidden, HD):
+        raise ValueError("weights must be w_qkvg [4 H 128, hidden] and w_o [hidden, H 128]")
+    H, D = HD // HEAD_DIM, HEAD_DIM
+    _f32("S_in", S_in, (B, H, D, D))
+    _f32("q_norm_w", q_norm_w, (D,))
+    _f32("k_norm_w", k_norm_w, (D,))
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _bf16_2d("out", out)
+    if S_out is None:
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=x.device)
+    else:
+        _f32("S_out", S_out, (B, H, D, D))
+    need = int(lib.la_layer_workspace_bytes(B, T, H, D, chunk))
+    if need == 0:
+        raise LAError(2, lib.la_status_string(2).decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib.la_layer_forward(_ptr(x), _ptr(w_qkvg), _ptr(w_o), _ptr(S_in), _ptr(S_out), _ptr(out), B, T,
+                                hidden, H, D, int(pos0), int(chunk), float(rope_base), float(rms_eps),
+                                _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(x.device)))
     return out, S_out
 
 

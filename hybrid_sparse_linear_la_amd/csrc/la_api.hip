@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <utility>
 #include <vector>
 
 #include "la_internal.hpp"
@@ -369,6 +370,97 @@ la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v
     if (launch_decode(d, s) != hipSuccess) return LA_ERR_HIP;
   }
   return LA_OK;
+}
+
+la_status la_linear(const la_bf16* x, const la_bf16* w, la_bf16* y, int64_t M, int N, int K, void* stream) {
+  if (!x || !w || !y) return LA_ERR_NULL_PTR;
+  if (M < 1 || N < 1 || K < 1 || M > ((int64_t)1 << 31)) return LA_ERR_BAD_SHAPE;
+  if (K % 64 != 0 || N % 256 != 0) return LA_ERR_UNSUPPORTED;
+  if (((M + 255) / 256) * (N / 256) >= ((int64_t)1 << 31)) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {x, w, y};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const uint64_t ybytes = (uint64_t)M * N * sizeof(la_bf16);
+  if (overlaps(y, ybytes, x, (uint64_t)M * K * sizeof(la_bf16)) ||
+      overlaps(y, ybytes, w, (uint64_t)N * K * sizeof(la_bf16)))
+    return LA_ERR_ALIASING;
+  LinearParams p{};
+  p.x = x;
+  p.w = w;
+  p.y[0] = y;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.nsplit = 1;
+  return launch_linear(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+size_t la_layer_workspace_bytes(int B, int T, int H, int D, int chunk) {
+  PrefillPlan plan;
+  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan)) return 0;
+  const size_t act = (size_t)B * T * H * D * sizeof(la_bf16);
+  return 5 * round_up(act, 256) + plan.ws_bytes;
+}
+
+la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf16* w_o, const float* S_in,
+                           float* S_out, la_bf16* y, int B, int T, int hidden, int H, int D, int64_t pos0,
+                           int chunk, float rope_base, float rms_eps, const float* q_norm_w,
+                           const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !w_qkvg || !w_o || !S_out || !y || !workspace) return LA_ERR_NULL_PTR;
+  if (B < 1 || T < 1 || H < 1 || hidden < 1) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
+  if (hidden % 256 != 0 || (H * D) % 256 != 0) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {x, w_qkvg, w_o, S_in, S_out, y, workspace, q_norm_w, k_norm_w};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const int64_t M = (int64_t)B * T;
+  const int HD = H * D;
+  const uint64_t xbytes = (uint64_t)M * hidden * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
+  const size_t act = round_up((size_t)M * HD * sizeof(la_bf16), 256);
+  const size_t need = 5 * act + plan.ws_bytes;
+  if (workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const std::pair<const void*, uint64_t> regions[] = {
+      {x, xbytes}, {w_qkvg, (uint64_t)4 * HD * hidden * sizeof(la_bf16)},
+      {w_o, (uint64_t)hidden * HD * sizeof(la_bf16)}, {S_in, st}, {S_out, st}, {y, xbytes}};
+  for (const auto& r : regions)
+    if (overlaps(workspace, need, r.first, r.second)) return LA_ERR_ALIASING;
+  for (const auto& r : regions)
+    if (r.first != y && overlaps(y, xbytes, r.first, r.second)) return LA_ERR_ALIASING;
+  for (const auto& r : {regions[0], regions[1], regions[2], regions[5]})
+    if (overlaps(S_out, st, r.first, r.second)) return LA_ERR_ALIASING;
+  if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  la_bf16* qkvg[4];
+  for (int i = 0; i < 4; ++i) qkvg[i] = reinterpret_cast<la_bf16*>(ws + i * act);
+  la_bf16* o = reinterpret_cast<la_bf16*>(ws + 4 * act);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+
+  LinearParams in{};
+  in.x = x;
+  in.w = w_qkvg;
+  for (int i = 0; i < 4; ++i) in.y[i] = qkvg[i];
+  in.M = M;
+  in.N = 4 * HD;
+  in.K = hidden;
+  in.nsplit = 4;
+  if (launch_linear(in, s) != hipSuccess) return LA_ERR_HIP;
+  const la_status st_pre = la_prefill(qkvg[0], qkvg[1], qkvg[2], qkvg[3], S_in, S_out, o, B, T, H, D, pos0, chunk,
+                                      rope_base, rms_eps, q_norm_w, k_norm_w, ws + 5 * act, plan.ws_bytes, stream);
+  if (st_pre != LA_OK) return st_pre;
+  LinearParams out{};
+  out.x = o;
+  out.w = w_o;
+  out.y[0] = y;
+  out.M = M;
+  out.N = hidden;
+  out.K = HD;
+  out.nsplit = 1;
+  return launch_linear(out, s) == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -91,6 +91,18 @@ struct DecodeParams {
   RopeFreqs freqs;
 };
 
+// y = x W^T, bf16 in and out, fp32 accumulation; y split by columns into nsplit
+// tensors [M, N / nsplit].  K % 64 == 0, (N / nsplit) % 256 == 0.
+struct LinearParams {
+  const uint16_t* x;  // [M, K]
+  const uint16_t* w;  // [N, K]
+  uint16_t* y[4];
+  int64_t M;
+  int N, K, nsplit;
+};
+
+hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
+
 // events: nullptr, or 4 events recorded before each of the three kernels and after the last.
 hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipStream_t stream,
                           hipEvent_t const* events = nullptr);

@@ -158,6 +158,39 @@ la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v
                             const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Dense projection y = x W^T (the nn.Linear layout: W is [N, K]), bf16 inputs,
+ * fp32 accumulation, bf16 output; the q/k/v/gate and output projections around
+ * the layer in "創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B模型，端側跑通百萬上下文"
+ * (04 技術報告 > 02 模型架構 > (3) 線性注意力模塊: hidden 4096, 32 heads of 128).
+ *   x : [M, K], w : [N, K], y : [M, N], all row-major device buffers; y must not
+ *       overlap x or w.
+ * Supported: K % 64 == 0, N % 256 == 0, M >= 1 (LA_ERR_UNSUPPORTED otherwise).
+ */
+la_status la_linear(const la_bf16* x, const la_bf16* w, la_bf16* y, int64_t M, int N, int K, void* stream);
+
+/*
+ * Bytes of workspace la_layer_forward needs: q, k, v, gate and o buffers of
+ * B * T * H * D bf16 each (rounded to 256 bytes) plus la_prefill's workspace.
+ */
+size_t la_layer_workspace_bytes(int B, int T, int H, int D, int chunk);
+
+/*
+ * One linear-attention layer forward: [q | k | v | g] = x W_qkvg^T (one
+ * projection whose four column blocks land in four [B, T, H, D] buffers of the
+ * workspace), then la_prefill on them, then y = o W_o^T.
+ *   x        : [B, T, hidden] bf16
+ *   w_qkvg   : [4 H D, hidden] bf16, rows ordered q heads, k heads, v heads, gate
+ *   w_o      : [hidden, H D] bf16
+ *   S_in, S_out, pos0, chunk, rope_base, rms_eps, q_norm_w, k_norm_w : as la_prefill
+ *   y        : [B, T, hidden] bf16; must not overlap x, the weights or the states
+ * Supported: D == 128, hidden % 256 == 0, (H D) % 256 == 0.
+ */
+la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf16* w_o, const float* S_in,
+                           float* S_out, la_bf16* y, int B, int T, int hidden, int H, int D, int64_t pos0,
+                           int chunk, float rope_base, float rms_eps, const float* q_norm_w,
+                           const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step: one token per sequence at absolute position pos.
  *   q, k, v, gate_logits : [B, H, D] bf16.
  *   S : [B, H, D, D] fp32 state, updated in place (S += kh v^T).

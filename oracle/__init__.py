@@ -19,6 +19,14 @@ What each function follows (pages cited by title and section):
     (paper digest), 前置知识 > 线性注意力, read out as o_t = sigmoid(g_t) * (q_t S_t).
   * ``chunked`` -- the same sum regrouped by chunks (for the chunk invariance check).
   * ``decode_step`` -- ``forward`` with one token.
+  * ``linear`` / ``layer_forward`` -- the projections around the layer (one
+    fused q/k/v/gate projection and the output projection; hidden 4096, 32 heads
+    of 128, MHA): the technical-report rendering above, 02 模型架構 (3)
+    線性注意力模塊.  ``linear`` is a float64 matrix product (numpy); the layer
+    composes it with ``forward`` and, like the GPU path, rounds the projected
+    q, k, v, g and the layer output o to bfloat16 (nearest-even) where they are
+    handed on, so the comparison measures the layer's arithmetic rather than the
+    hand-over format.
 """
 from __future__ import annotations
 
@@ -171,3 +179,38 @@ def decode_step(q, k, v, g, S, pos: int, base: float = 10000.0, eps: float = 1e-
     q, k, v, g = (np.asarray(a)[:, None] for a in (q, k, v, g))
     o, S_new = forward(q, k, v, g, S=S, pos0=pos, base=base, eps=eps, q_w=q_w, k_w=k_w)
     return o[:, 0], S_new
+
+
+def linear(x, w) -> np.ndarray:
+    """y = x w^T in float64: x [..., K], w [N, K] (the nn.Linear weight layout)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return x @ w.T
+
+
+def round_bf16(a) -> np.ndarray:
+    """Round to the nearest bfloat16 (ties to even), returned as float32."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16) << 16
+    out = r.astype(np.uint32).view(np.float32).copy()
+    nan = np.isnan(a)
+    out[nan] = a[nan]
+    return out
+
+
+def layer_forward(x, w_qkvg, w_o, S=None, pos0: int = 0, base: float = 10000.0, eps: float = 1e-6,
+                  q_w=None, k_w=None):
+    """[q | k | v | g] = x w_qkvg^T (column blocks of H * D), then ``forward``, then
+    y = o w_o^T.  x [B, T, hidden]; returns (y [B, T, hidden] f64, S_out f64)."""
+    x = np.asarray(x, dtype=np.float64)
+    B, T, hidden = x.shape
+    HD = np.asarray(w_o).shape[1]
+    D = 128
+    H = HD // D
+    proj = linear(x, w_qkvg)
+    q, k, v, g = (round_bf16(proj[..., i * HD:(i + 1) * HD]).reshape(B, T, H, D) for i in range(4))
+    o, S_out = forward(q, k, v, g, S=S, pos0=pos0, base=base, eps=eps, q_w=q_w, k_w=k_w)
+    y = linear(round_bf16(o.reshape(B, T, HD)), w_o)
+    return y, S_out

@@ -26,7 +26,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
-         "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_decode_step"])
+         "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_linear", "la_layer_workspace_bytes",
+         "la_layer_forward", "la_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -169,3 +170,32 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(la, "lib_path", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         la.library()
+
+
+def test_linear_and_layer_validation(lib):
+    vp = ctypes.c_void_p
+    lin = lambda x=A, w=A + 64 * MB, y=A + 128 * MB, M=4, N=256, K=64: lib.la_linear(  # noqa: E731
+        vp(x), vp(w), vp(y), M, N, K, None)
+    assert lin(x=None) == 1
+    assert lin(M=0) == 2
+    assert lin(K=96) == 3
+    assert lin(N=384) == 3
+    assert lin(w=A + 64 * MB + 2) == 4
+    assert lin(y=A) == 5                     # y overlaps x
+    assert lin(y=A + 64 * MB) == 5           # y overlaps w
+    assert lib.la_layer_workspace_bytes(1, 300, 2, 128, 0) == 5 * 153600 + lib.la_prefill_workspace_bytes(
+        1, 300, 2, 128, 0)
+    assert lib.la_layer_workspace_bytes(1, 300, 2, 64, 0) == 0
+
+    def layer(x=A, wq=A + 64 * MB, wo=A + 128 * MB, S_in=None, S_out=A + 192 * MB, y=A + 256 * MB, B=1, T=300,
+              hidden=256, H=2, D=128, ws=A + 512 * MB, ws_bytes=1 << 30):
+        return lib.la_layer_forward(vp(x), vp(wq), vp(wo), vp(S_in), vp(S_out), vp(y), B, T, hidden, H, D, 0, 0,
+                                    10000.0, 1e-6, None, None, vp(ws), ws_bytes, None)
+    assert layer(wq=None) == 1
+    assert layer(T=0) == 2
+    assert layer(hidden=320) == 3
+    assert layer(H=3) == 3                   # H * D = 384 is not a multiple of 256
+    assert layer(y=A + 256 * MB + 8) == 4
+    assert layer(y=A + 1024) == 5            # y overlaps x
+    assert layer(ws=A + 256 * MB) == 5       # workspace overlaps y
+    assert layer(ws_bytes=4096) == 6

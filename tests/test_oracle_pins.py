@@ -243,3 +243,35 @@ def test_threads_do_not_change_results():
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(S1, S2)
     assert n >= 1
+
+
+# ---------------------------------------------------------------------------
+# Projections around the layer (oracle.linear, oracle.round_bf16, oracle.layer_forward)
+
+def test_linear_hand_example():
+    """y = x w^T with w in the nn.Linear [out, in] layout, worked by hand."""
+    x = np.array([[1.0, 2.0], [3.0, 4.0]])
+    w = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]])
+    assert np.array_equal(oracle.linear(x, w), np.array([[1.0, 2.0, 3.0], [3.0, 4.0, 7.0]]))
+
+
+def test_round_bf16_ties_to_even():
+    """bfloat16 keeps 8 significant bits: at 1.0 the spacing is 2^-7."""
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -(1 + 2 ** -8), 2 ** -8 * 3], np.float32)
+    want = np.array([1.0, 1 + 2 ** -6, 1.0, -1.0, 2 ** -8 * 3], np.float32)
+    assert np.array_equal(oracle.round_bf16(x), want)
+
+
+def test_layer_with_identity_projections_is_the_layer():
+    """w_qkvg = [I; I; I; 0] (q = k = v = x, gate logits 0) and w_o = I reduce the
+    layer to half of the bare recurrence (sigmoid(0) = 1/2), rounded to bf16."""
+    rng = np.random.default_rng(7)
+    T, HD = 40, 128
+    x = oracle.round_bf16(rng.standard_normal((1, T, HD)))
+    eye = np.eye(HD)
+    w_qkvg = np.concatenate([eye, eye, eye, np.zeros((HD, HD))])
+    y, S = oracle.layer_forward(x, w_qkvg, eye, pos0=11)
+    xs = x.reshape(1, T, 1, HD)
+    o, S_ref = oracle.forward(xs, xs, xs, np.zeros_like(xs), pos0=11)
+    np.testing.assert_allclose(y, oracle.round_bf16(o.reshape(1, T, HD)), rtol=0, atol=0)
+    np.testing.assert_allclose(S, S_ref, rtol=0, atol=0)

@@ -113,3 +113,29 @@ def decode_inputs(w: Workload, steps: int | None = None, device="cpu"):
     S0 = state(w.B, w.H, w.D, w.state_std, gen, device)
     toks = activations(steps, w.B, w.H, w.D, w.seed, device, w.dtype, gen=gen)
     return (S0,) + tuple(toks)
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerWorkload:
+    """Inputs of one layer forward: x [B, T, hidden] ~ N(0, 1) and the fused
+    q/k/v/gate and output projection weights ~ N(0, 1 / fan_in), all bf16."""
+    name: str
+    B: int
+    T: int
+    hidden: int
+    H: int
+    D: int
+    seed: int
+
+
+# One layer of the model's shape (hidden 4096, 32 heads x 128) on a 32K-token prompt.
+LAYER_32K = LayerWorkload("layer_b1_t32768_hidden4096_h32_d128", 1, 32768, 4096, 32, 128, seed=6)
+
+
+def layer_inputs(B: int, T: int, hidden: int, H: int, D: int, seed: int, device="cpu"):
+    """(x, w_qkvg [4 H D, hidden], w_o [hidden, H D]), drawn in that order."""
+    gen = generator(seed, device)
+    x = torch.randn((B, T, hidden), generator=gen, device=device).to(torch.bfloat16)
+    w_qkvg = (torch.randn((4 * H * D, hidden), generator=gen, device=device) / hidden ** 0.5).to(torch.bfloat16)
+    w_o = (torch.randn((hidden, H * D), generator=gen, device=device) / (H * D) ** 0.5).to(torch.bfloat16)
+    return x, w_qkvg, w_o
