@@ -19,6 +19,11 @@ What each function follows (pages cited by title and section):
     (paper digest), 前置知识 > 线性注意力, read out as o_t = sigmoid(g_t) * (q_t S_t).
   * ``chunked`` -- the same sum regrouped by chunks (for the chunk invariance check).
   * ``decode_step`` -- ``forward`` with one token.
+  * ``backward`` -- the gradients of ``forward`` (reverse mode of the same
+    recurrence, through the gate, RoPE and RMSNorm) for given output and
+    final-state gradients; what training the converted linear layers needs
+    (technical-report page, 03 訓練: the linear layers are trained after
+    conversion).
   * ``linear`` / ``layer_forward`` -- the projections around the layer (one
     fused q/k/v/gate projection and the output projection; hidden 4096, 32 heads
     of 128, MHA): the technical-report rendering above, 02 模型架構 (3)
@@ -67,6 +72,9 @@ def _bind(lib):
               ctypes.c_int64, ctypes.c_double, ctypes.c_double, _f32p, _f32p]
     lib.lao_forward.argtypes = common + [_f64p, _f64p]
     lib.lao_chunked.argtypes = common + [ctypes.c_int, _f64p, _f64p]
+    if hasattr(lib, "lao_backward"):
+        lib.lao_backward.argtypes = [_f32p] * 5 + [ctypes.c_int] * 4 + [
+            ctypes.c_int64, ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f64p, _f64p] + [_f64p] * 7
     return lib
 
 
@@ -109,7 +117,7 @@ def _p32(a):
 
 
 def _p64(a):
-    return a.ctypes.data_as(_f64p)
+    return None if a is None else a.ctypes.data_as(_f64p)
 
 
 def rmsnorm_row(x, eps: float = 1e-6, w=None) -> np.ndarray:
@@ -214,3 +222,29 @@ def layer_forward(x, w_qkvg, w_o, S=None, pos0: int = 0, base: float = 10000.0, 
     o, S_out = forward(q, k, v, g, S=S, pos0=pos0, base=base, eps=eps, q_w=q_w, k_w=k_w)
     y = linear(round_bf16(o.reshape(B, T, HD)), w_o)
     return y, S_out
+
+
+def backward(q, k, v, g, do, S=None, dS_out=None, pos0: int = 0, base: float = 10000.0,
+             eps: float = 1e-6, q_w=None, k_w=None) -> dict:
+    """Gradients of the loss L with dL/do = do and dL/dS_out = dS_out (None = 0).
+
+    Returns dq, dk, dv, dg ([B, T, H, D] f64), dS_in ([B, H, D, D] f64) and, when
+    weights are given, dq_w, dk_w ([D] f64)."""
+    q, k, v, g, St, (B, T, H, D) = _prep(q, k, v, g, S)
+    do = _f32(do)
+    dSo = None if dS_out is None else np.ascontiguousarray(np.asarray(dS_out, dtype=np.float64))
+    q_w = None if q_w is None else _f32(q_w)
+    k_w = None if k_w is None else _f32(k_w)
+    out = {n: np.empty((B, T, H, D), np.float64) for n in ("dq", "dk", "dv", "dg")}
+    dS_in = np.empty((B, H, D, D), np.float64)
+    dqw = np.empty((B * H, D), np.float64) if q_w is not None else None
+    dkw = np.empty((B * H, D), np.float64) if k_w is not None else None
+    _load().lao_backward(_p32(q), _p32(k), _p32(v), _p32(g), _p32(do), B, T, H, D, int(pos0), float(base),
+                         float(eps), _p32(q_w), _p32(k_w), _p64(St), _p64(dSo), _p64(out["dq"]),
+                         _p64(out["dk"]), _p64(out["dv"]), _p64(out["dg"]), _p64(dS_in), _p64(dqw), _p64(dkw))
+    out["dS_in"] = dS_in
+    if dqw is not None:
+        out["dq_w"] = dqw.sum(axis=0)
+    if dkw is not None:
+        out["dk_w"] = dkw.sum(axis=0)
+    return out

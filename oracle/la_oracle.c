@@ -198,3 +198,124 @@ void lao_chunked(const float* q, const float* k, const float* v, const float* g,
     free(kh);
   }
 }
+
+/*
+ * Gradients of the layer (reverse mode of the recurrence above), for a scalar
+ * loss L whose gradients with respect to the gated output o and the final state
+ * S_out are do and dS_out.  Per (b, h), with du_t = do_t * sigmoid(g_t):
+ *   forward, token by token:  S_t = S_{t-1} + kh_t v_t^T,  u_t = qh_t S_t,
+ *       dg_t  = do_t * u_t * sigmoid'(g_t),     dqh_t = S_t du_t;
+ *   backward, tokens in reverse:  G_t = G_{t+1} + qh_t du_t^T  (G_T = dS_out),
+ *       dkh_t = G_t v_t,   dv_t = G_t^T kh_t,   and dS_in = G_0;
+ *   then through RoPE (rotate back by the same angle) and RMSNorm:
+ *       n = w x / r,  r = sqrt(mean(x^2) + eps):
+ *       dx_i = w_i dn_i / r - x_i (sum_j w_j x_j dn_j) / (D r^3),  dw_i += dn_i x_i / r.
+ * Outputs are double.  dS_in may be NULL; dqw_part / dkw_part, when not NULL, get
+ * one [D] partial weight gradient per (b, h) task ([B*H][D]), to be summed.
+ */
+static void rope_back_row(const double* dy, int D, int64_t pos, double base, double* dn) {
+  int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    double theta = pow(base, -2.0 * (double)i / (double)D);
+    double a = (double)pos * theta;
+    double c = cos(a), s = sin(a);
+    dn[i] = dy[i] * c + dy[i + half] * s;
+    dn[i + half] = -dy[i] * s + dy[i + half] * c;
+  }
+}
+
+static void rmsnorm_back_row(const float* x, int D, double eps, const float* w, const double* dn,
+                             double* dx, double* dw) {
+  double ss = 0.0;
+  for (int i = 0; i < D; ++i) ss += (double)x[i] * (double)x[i];
+  double r = sqrt(ss / (double)D + eps);
+  double dot = 0.0;
+  for (int i = 0; i < D; ++i) dot += (w ? (double)w[i] : 1.0) * (double)x[i] * dn[i];
+  for (int i = 0; i < D; ++i) {
+    double wi = w ? (double)w[i] : 1.0;
+    dx[i] = wi * dn[i] / r - (double)x[i] * dot / ((double)D * r * r * r);
+    if (dw) dw[i] += dn[i] * (double)x[i] / r;
+  }
+}
+
+void lao_backward(const float* q, const float* k, const float* v, const float* g, const float* dout,
+                  int B, int T, int H, int D, int64_t pos0, double base, double eps, const float* q_w,
+                  const float* k_w, const double* S_in, const double* dS_out, double* dq, double* dk,
+                  double* dv, double* dg, double* dS_in, double* dqw_part, double* dkw_part) {
+  int64_t tasks = (int64_t)B * H;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(lao_get_threads())
+  for (int64_t task = 0; task < tasks; ++task) {
+    int h = (int)(task % H);
+    int b = (int)(task / H);
+    size_t DD = (size_t)D * D;
+    double* S = (double*)malloc(sizeof(double) * DD);
+    double* G = (double*)malloc(sizeof(double) * DD);
+    double* qh = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* kh = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* du = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* dqh = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* dkh = (double*)malloc(sizeof(double) * (size_t)T * D);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)D * 2);
+    double* dn = tmp + D;
+    double* dqw = dqw_part ? dqw_part + task * D : NULL;
+    double* dkw = dkw_part ? dkw_part + task * D : NULL;
+    if (dqw) memset(dqw, 0, sizeof(double) * (size_t)D);
+    if (dkw) memset(dkw, 0, sizeof(double) * (size_t)D);
+    for (size_t e = 0; e < DD; ++e) S[e] = S_in ? S_in[task * DD + e] : 0.0;
+    /* forward: u, dg, du, dqh */
+    for (int t = 0; t < T; ++t) {
+      int64_t row = (((int64_t)b * T + t) * H + h) * D;
+      prologue_row(q + row, D, pos0 + t, base, eps, q_w, tmp, qh + (int64_t)t * D);
+      prologue_row(k + row, D, pos0 + t, base, eps, k_w, tmp, kh + (int64_t)t * D);
+      for (int i = 0; i < D; ++i)
+        for (int j = 0; j < D; ++j) S[(size_t)i * D + j] += kh[(int64_t)t * D + i] * (double)v[row + j];
+      for (int j = 0; j < D; ++j) {
+        double u = 0.0;
+        for (int i = 0; i < D; ++i) u += qh[(int64_t)t * D + i] * S[(size_t)i * D + j];
+        double sg = sigmoid((double)g[row + j]);
+        dg[row + j] = (double)dout[row + j] * u * sg * (1.0 - sg);
+        du[(int64_t)t * D + j] = (double)dout[row + j] * sg;
+      }
+      for (int i = 0; i < D; ++i) {
+        double a = 0.0;
+        for (int j = 0; j < D; ++j) a += S[(size_t)i * D + j] * du[(int64_t)t * D + j];
+        dqh[(int64_t)t * D + i] = a;
+      }
+    }
+    /* backward over tokens: G, dkh, dv */
+    for (size_t e = 0; e < DD; ++e) G[e] = dS_out ? dS_out[task * DD + e] : 0.0;
+    for (int t = T - 1; t >= 0; --t) {
+      int64_t row = (((int64_t)b * T + t) * H + h) * D;
+      for (int i = 0; i < D; ++i)
+        for (int j = 0; j < D; ++j) G[(size_t)i * D + j] += qh[(int64_t)t * D + i] * du[(int64_t)t * D + j];
+      for (int i = 0; i < D; ++i) {
+        double a = 0.0;
+        for (int j = 0; j < D; ++j) a += G[(size_t)i * D + j] * (double)v[row + j];
+        dkh[(int64_t)t * D + i] = a;
+      }
+      for (int j = 0; j < D; ++j) {
+        double a = 0.0;
+        for (int i = 0; i < D; ++i) a += kh[(int64_t)t * D + i] * G[(size_t)i * D + j];
+        dv[row + j] = a;
+      }
+    }
+    if (dS_in)
+      for (size_t e = 0; e < DD; ++e) dS_in[task * DD + e] = G[e];
+    /* through RoPE and RMSNorm */
+    for (int t = 0; t < T; ++t) {
+      int64_t row = (((int64_t)b * T + t) * H + h) * D;
+      rope_back_row(dqh + (int64_t)t * D, D, pos0 + t, base, dn);
+      rmsnorm_back_row(q + row, D, eps, q_w, dn, dq + row, dqw);
+      rope_back_row(dkh + (int64_t)t * D, D, pos0 + t, base, dn);
+      rmsnorm_back_row(k + row, D, eps, k_w, dn, dk + row, dkw);
+    }
+    free(S);
+    free(G);
+    free(qh);
+    free(kh);
+    free(du);
+    free(dqh);
+    free(dkh);
+    free(tmp);
+  }
+}

@@ -1,7 +1,8 @@
 """The oracle's pins catch plausible mistakes.
 
 Each case plants one mistake (a flipped sign, a wrong index or frequency, a dropped
-term, a transposed operand, the diagonal left out of the causal mask) in a copy of
+term, a transposed operand, the diagonal left out of the causal mask, a gradient
+formula gone wrong) in a copy of
 the oracle's C source, builds it in a temporary directory, routes the oracle module
 to it and checks that at least one pin of ``test_oracle_pins`` fails.  CPU only.
 """
@@ -45,6 +46,31 @@ MUTANTS = {
     "chunk_mask_strict": ("for (int s = 0; s <= r; ++s) {", "for (int s = 0; s < r; ++s) {"),
     "chunk_prefix_term_dropped": (
         "          for (int i = 0; i < D; ++i) u += qh[(int64_t)r * D + i] * Sbh[i * D + j];\n", "\n"),
+    # gradients
+    "back_rope_not_inverted": ("dn[i] = dy[i] * c + dy[i + half] * s;", "dn[i] = dy[i] * c - dy[i + half] * s;"),
+    "back_rmsnorm_jacobian_term_dropped": (
+        "dx[i] = wi * dn[i] / r - (double)x[i] * dot / ((double)D * r * r * r);", "dx[i] = wi * dn[i] / r;"),
+    "back_sigmoid_derivative": ("dg[row + j] = (double)dout[row + j] * u * sg * (1.0 - sg);",
+                                "dg[row + j] = (double)dout[row + j] * u * sg;"),
+    "back_state_gradient_after_use": (
+        "      for (int i = 0; i < D; ++i)\n"
+        "        for (int j = 0; j < D; ++j) G[(size_t)i * D + j] += qh[(int64_t)t * D + i] * du[(int64_t)t * D + j];\n"
+        "      for (int i = 0; i < D; ++i) {\n"
+        "        double a = 0.0;\n"
+        "        for (int j = 0; j < D; ++j) a += G[(size_t)i * D + j] * (double)v[row + j];\n"
+        "        dkh[(int64_t)t * D + i] = a;\n"
+        "      }\n",
+        "      for (int i = 0; i < D; ++i) {\n"
+        "        double a = 0.0;\n"
+        "        for (int j = 0; j < D; ++j) a += G[(size_t)i * D + j] * (double)v[row + j];\n"
+        "        dkh[(int64_t)t * D + i] = a;\n"
+        "      }\n"
+        "      for (int i = 0; i < D; ++i)\n"
+        "        for (int j = 0; j < D; ++j) G[(size_t)i * D + j] += qh[(int64_t)t * D + i] * du[(int64_t)t * D + j];\n"),
+    "back_dv_uses_q": ("for (int i = 0; i < D; ++i) a += kh[(int64_t)t * D + i] * G[(size_t)i * D + j];",
+                       "for (int i = 0; i < D; ++i) a += qh[(int64_t)t * D + i] * G[(size_t)i * D + j];"),
+    "back_weight_gradient_missing_norm": ("if (dw) dw[i] += dn[i] * (double)x[i] / r;",
+                                          "if (dw) dw[i] += dn[i] * (double)x[i];"),
 }
 
 PIN_CALLS = [
@@ -59,6 +85,7 @@ PIN_CALLS = [
     (pins.test_state_closed_form_and_independence_from_q_and_gate, ()),
     (pins.test_gate_special_cases, ()),
     (pins.test_chunked_equals_recurrence_for_every_chunk_size, ()),
+    (pins.test_backward_matches_finite_differences, (True,)),
 ]
 
 

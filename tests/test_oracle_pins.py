@@ -275,3 +275,70 @@ def test_layer_with_identity_projections_is_the_layer():
     o, S_ref = oracle.forward(xs, xs, xs, np.zeros_like(xs), pos0=11)
     np.testing.assert_allclose(y, oracle.round_bf16(o.reshape(1, T, HD)), rtol=0, atol=0)
     np.testing.assert_allclose(S, S_ref, rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# Gradients (oracle.backward) against central finite differences of the forward
+
+def _loss(q, k, v, g, S, do, dSo, pos0, qw, kw):
+    o, S_out = oracle.forward(q, k, v, g, S=S, pos0=pos0, q_w=qw, k_w=kw)
+    return float(np.sum(o * do) + np.sum(S_out * dSo))
+
+
+@pytest.mark.parametrize("weights", [False, True])
+def test_backward_matches_finite_differences(weights):
+    """Every gradient element of a tiny layer (B 1, T 5, H 2, D 8) against central
+    differences of L = <o, do> + <S_out, dS_out>.  The perturbed inputs are float32,
+    so the step actually taken is used as the denominator."""
+    rng = np.random.default_rng(11)
+    B, T, H, D, pos0 = 1, 5, 2, 8, 3
+    q, k, v, g = (rng.standard_normal((B, T, H, D)).astype(np.float32) for _ in range(4))
+    S = rng.standard_normal((B, H, D, D)) * 0.3
+    do = rng.standard_normal((B, T, H, D)).astype(np.float32)  # the oracle takes do as float32
+    dSo = rng.standard_normal((B, H, D, D))
+    qw = (rng.random(D) + 0.5).astype(np.float32) if weights else None
+    kw = (rng.random(D) + 0.5).astype(np.float32) if weights else None
+    grads = oracle.backward(q, k, v, g, do, S=S, dS_out=dSo, pos0=pos0, q_w=qw, k_w=kw)
+    inputs = {"dq": q, "dk": k, "dv": v, "dg": g}
+    if weights:
+        inputs["dq_w"] = qw
+        inputs["dk_w"] = kw
+    h = 1e-3
+    for name, arr in inputs.items():
+        fd = np.zeros(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            x0 = arr[idx]
+            arr[idx] = np.float32(x0 + h)
+            xp = float(arr[idx])
+            lp = _loss(q, k, v, g, S, do, dSo, pos0, qw, kw)
+            arr[idx] = np.float32(x0 - h)
+            xm = float(arr[idx])
+            lm = _loss(q, k, v, g, S, do, dSo, pos0, qw, kw)
+            arr[idx] = x0
+            fd[idx] = (lp - lm) / (xp - xm)
+        np.testing.assert_allclose(grads[name], fd, rtol=1e-4, atol=1e-5 * np.abs(fd).max(), err_msg=name)
+    # dS_in: S is float64, so a plain central difference
+    fd = np.zeros(S.shape)
+    for idx in np.ndindex(S.shape):
+        s0 = S[idx]
+        S[idx] = s0 + h
+        lp = _loss(q, k, v, g, S, do, dSo, pos0, qw, kw)
+        S[idx] = s0 - h
+        lm = _loss(q, k, v, g, S, do, dSo, pos0, qw, kw)
+        S[idx] = s0
+        fd[idx] = (lp - lm) / (2 * h)
+    np.testing.assert_allclose(grads["dS_in"], fd, rtol=1e-6, atol=1e-9, err_msg="dS_in")
+
+
+def test_backward_is_linear_in_the_output_gradients():
+    rng = np.random.default_rng(12)
+    B, T, H, D = 1, 7, 1, 8
+    q, k, v, g = (rng.standard_normal((B, T, H, D)).astype(np.float32) for _ in range(4))
+    # dyadic values, so 2 a - b is exact in the float32 the oracle takes do in
+    do1, do2 = np.round(rng.standard_normal((2, B, T, H, D)) * 16) / 16
+    dS1, dS2 = np.round(rng.standard_normal((2, B, H, D, D)) * 16) / 16
+    a = oracle.backward(q, k, v, g, do1, dS_out=dS1)
+    b = oracle.backward(q, k, v, g, do2, dS_out=dS2)
+    c = oracle.backward(q, k, v, g, 2 * do1 - do2, dS_out=2 * dS1 - dS2)
+    for n in ("dq", "dk", "dv", "dg", "dS_in"):
+        np.testing.assert_allclose(c[n], 2 * a[n] - b[n], rtol=1e-10, atol=1e-12, err_msg=n)
