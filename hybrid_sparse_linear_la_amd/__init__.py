@@ -12,6 +12,7 @@ is missing, every call raises.
     o, S_out = prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None)
     y = linear(x, w)                              # y = x w^T
     y, S_out = layer_forward(x, w_qkvg, w_o, S_in=None, pos0=0)
+    grads = backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0=0)
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "prefill_varlen", "linear", "layer_forward", "prefill_workspace_bytes",
+__all__ = ["prefill", "decode_step", "prefill_varlen", "linear", "layer_forward", "backward",
+           "prefill_workspace_bytes", "backward_workspace_bytes",
            "layer_workspace_bytes",
            "prefill_varlen_workspace_bytes", "LAError", "library", "lib_path",
            "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS"]
@@ -77,6 +79,11 @@ def library():
         lib.la_layer_workspace_bytes.argtypes = [ctypes.c_int] * 5
         lib.la_layer_forward.restype = ctypes.c_int
         lib.la_layer_forward.argtypes = [_vp] * 6 + [ctypes.c_int] * 5 + [
+            ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.la_backward_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_backward_workspace_bytes.argtypes = [ctypes.c_int] * 5
+        lib.la_backward.restype = ctypes.c_int
+        lib.la_backward.argtypes = [_vp] * 14 + [ctypes.c_int] * 4 + [
             ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
@@ -283,6 +290,47 @@ def layer_forward(x, w_qkvg, w_o, S_in=None, pos0: int = 0, chunk: int = 0, rope
                                 _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(x.device)))
     return out, S_out
+
+
+def backward_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, chunk: int = 0) -> int:
+    return int(library().la_backward_workspace_bytes(B, T, H, D, chunk))
+
+
+def backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0: int = 0, chunk: int = 0,
+             rope_base: float = 10000.0, rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None,
+             weight_grads: bool = False, workspace=None):
+    """Gradients of la_prefill for output gradient d_o (bf16 [B, T, H, 128]) and
+    final-state gradient dS_out (fp32 [B, H, 128, 128] or None).  Returns a dict
+    with dq, dk, dv, dgate (bf16), dS_in (fp32) and, with weight_grads, dq_norm_w
+    and dk_norm_w (fp32 [128]; at weights of one when none are given)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("d_o", d_o)):
+        _act(n, t, 4)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    B, T, H, D = q.shape
+    _f32("S_in", S_in, (B, H, D, D))
+    _f32("dS_out", dS_out, (B, H, D, D))
+    _f32("q_norm_w", q_norm_w, (D,))
+    _f32("k_norm_w", k_norm_w, (D,))
+    out = {n: torch.empty_like(q) for n in ("dq", "dk", "dv", "dgate")}
+    out["dS_in"] = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+    if weight_grads:
+        out["dq_norm_w"] = torch.empty(D, dtype=torch.float32, device=q.device)
+        out["dk_norm_w"] = torch.empty(D, dtype=torch.float32, device=q.device)
+    need = int(lib.la_backward_workspace_bytes(B, T, H, D, chunk))
+    if need == 0:
+        status = 3 if (D != HEAD_DIM or chunk not in (0, 64)) else 2
+        raise LAError(status, lib.la_status_string(status).decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(d_o), _ptr(dS_out),
+                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
+                           _ptr(out["dS_in"]), _ptr(out.get("dq_norm_w")), _ptr(out.get("dk_norm_w")), B, T, H, D,
+                           int(pos0), int(chunk), float(rope_base), float(rms_eps), _ptr(q_norm_w),
+                           _ptr(k_norm_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(q.device)))
+    return out
 
 
 def decode_step(q, k, v, gate, S, pos: int, rope_base: float = 10000.0, rms_eps: float = 1e-6,

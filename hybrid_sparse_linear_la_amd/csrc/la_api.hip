@@ -463,4 +463,103 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
   return launch_linear(out, s) == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+// Workspace of la_backward: forward and gradient segment states, the final
+// forward state (unused), fp32 gradients of the rotated q and k, and the parts of
+// the norm-weight gradients.
+static bool backward_layout(int B, int T, int H, const PrefillPlan& plan, size_t off[6]) {
+  const size_t st = (size_t)B * H * kHeadDim * kHeadDim * sizeof(float);
+  const size_t rows = (size_t)B * T * H * kHeadDim * sizeof(float);
+  off[0] = 0;                                   // forward segment states
+  off[1] = round_up(off[0] + plan.ws_bytes, 256);  // gradient segment states
+  off[2] = round_up(off[1] + plan.ws_bytes, 256);  // final forward state
+  off[3] = round_up(off[2] + st, 256);             // dqh
+  off[4] = round_up(off[3] + rows, 256);           // dkh
+  off[5] = round_up(off[4] + rows, 256);           // weight-gradient parts
+  return true;
+}
+
+size_t la_backward_workspace_bytes(int B, int T, int H, int D, int chunk) {
+  PrefillPlan plan;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64) || !plan_prefill(B, T, H, chunk, &plan)) return 0;
+  size_t off[6];
+  backward_layout(B, T, H, plan, off);
+  return off[5] + (size_t)2 * kPrologueBlocks * kHeadDim * sizeof(float);
+}
+
+la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                      const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
+                      la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
+                      int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
+                      const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k || !v || !gate_logits || !d_o || !dq || !dk || !dv || !dgate || !dS_in || !workspace)
+    return LA_ERR_NULL_PTR;
+  if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64)) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  const size_t need = la_backward_workspace_bytes(B, T, H, D, chunk);
+  const void* ptrs[] = {q, k, v, gate_logits, S_in, d_o, dS_out, dq, dk, dv, dgate, dS_in,
+                        dq_norm_w, dk_norm_w, q_norm_w, k_norm_w, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
+  const uint64_t wb = (uint64_t)D * sizeof(float);
+  const std::pair<const void*, uint64_t> ins[] = {{q, act}, {k, act}, {v, act}, {gate_logits, act}, {d_o, act},
+                                                  {S_in, st}, {dS_out, st}, {q_norm_w, wb}, {k_norm_w, wb}};
+  const std::pair<const void*, uint64_t> outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgate, act}, {dS_in, st},
+                                                   {dq_norm_w, wb}, {dk_norm_w, wb}, {workspace, need}};
+  for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
+    for (const auto& in : ins)
+      if (overlaps(outs[a].first, outs[a].second, in.first, in.second)) return LA_ERR_ALIASING;
+    for (size_t b = a + 1; b < sizeof(outs) / sizeof(outs[0]); ++b)
+      if (overlaps(outs[a].first, outs[a].second, outs[b].first, outs[b].second)) return LA_ERR_ALIASING;
+  }
+  if (workspace_bytes < need) return LA_ERR_WORKSPACE;
+
+  size_t off[6];
+  backward_layout(B, T, H, plan, off);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  BackwardParams bp{};
+  PrefillParams& p = bp.f;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = gate_logits;
+  p.o = nullptr;
+  p.ws = reinterpret_cast<float*>(ws + off[0]);
+  p.segs = nullptr;
+  p.seqs = nullptr;
+  p.S_in = S_in;
+  p.S_out = reinterpret_cast<float*>(ws + off[2]);
+  p.qw = q_norm_w;
+  p.kw = k_norm_w;
+  p.dout = d_o;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.nseg = plan.nseg;
+  p.cps = plan.cps;
+  p.pos0 = pos0;
+  p.eps = rms_eps;
+  rope_freqs(rope_base, &p.freqs);
+  bp.wsg = reinterpret_cast<float*>(ws + off[1]);
+  bp.dS_out = dS_out;
+  bp.dS_in = dS_in;
+  bp.dq = dq;
+  bp.dk = dk;
+  bp.dv = dv;
+  bp.dg = dgate;
+  bp.dqh = reinterpret_cast<float*>(ws + off[3]);
+  bp.dkh = reinterpret_cast<float*>(ws + off[4]);
+  bp.dq_w = dq_norm_w;
+  bp.dk_w = dk_norm_w;
+  bp.wpart = reinterpret_cast<float*>(ws + off[5]);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_segment_states(bp, plan, s) != hipSuccess) return LA_ERR_HIP;
+  return launch_backward_chunks(bp, plan, s) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 }  // extern "C"

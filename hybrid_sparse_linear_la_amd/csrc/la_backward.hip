@@ -1,0 +1,353 @@
+// Backward of the chunked prefill on gfx950 (chunk 64).
+//
+// For a loss with gradients do (of o) and dS_out (of the final state), per (b, h),
+// with du_t = do_t * sigmoid(g_t), u_t = qh_t S_t (the output before the gate),
+// and G_s = dS_out + sum_{t >= s} qh_t du_t^T (the gradient of the state S_s):
+//     dg  = do * u * sigmoid'(g)            dqh_t = du_t S_t^T
+//     dkh_s = G_s v_s                       dv_s  = G_s^T kh_s,      dS_in = G_0,
+// the reverse mode of S_t = S_{t-1} + k_t v_t^T and o_t = sigmoid(g_t) (q_t S_t)
+// ("MiniCPM-SALA: Hybridizing Sparse and Linear Attention for Efficient
+// Long-Context Modeling", 前置知识 > 线性注意力; output gate and QK-normalization
+// from "創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B模型，端側跑通百萬上下文",
+// 04 技術報告 > 02 模型架構 > (3) 線性注意力模塊).
+//
+// Chunked, for a chunk with state S (before it) and G (after it):
+//     u   = (Qh Kh^T . M) V + Qh S
+//     dQh = (dU V^T . M) Kh + dU S^T
+//     dKh = (dU V^T . M)^T Qh + V G^T
+//     dV  = (Qh Kh^T . M)^T dU + Kh G
+// and across chunks S <- S + Kh^T V, G(before) = G(after) + Qh^T dU.
+//
+// la_backward_chunk_kernel: one 512-thread workgroup per (b, h, segment) walks
+// its chunks forward from the segment's forward state S and gradient state G (at
+// the segment's first token, from the suffix scan) and subtracts Qh^T dU from G
+// chunk by chunk.  Wave w owns columns [16w, 16w + 16) of every output and of the
+// S, G accumulators; S and G are also written to LDS as bf16 (transposed) so the
+// S^T and G^T products can read any row.  dqh, dkh leave in fp32 for
+// la_prologue_backward_kernel, which rotates them back and applies the RMSNorm
+// Jacobian.  Chunks at the start and end of a sequence form their scores from a
+// hi/lo split of qh, kh and du: rows there sum few scores, and the bf16 rounding
+// of the operands would otherwise dominate their error.
+#include "la_device.hpp"
+#include "la_internal.hpp"
+#include "la_tiles.hpp"
+
+namespace la {
+namespace {
+
+constexpr int kBwdThreads = 512;
+constexpr int kSnapBytes = kD * kRowBytes;  // [128][128] bf16, 272-byte rows
+
+// Column operand of a [rows][128] tile in token order pi, rows 32 kk ..: lane n16
+// gets X[32kk + 4g + 16(e/4) + e%4][c0 + n16] (the transposed read of v_operand).
+__device__ __forceinline__ bf16x8 col_operand(const uint8_t* tile, int kk, int c0, int g4, int n16) {
+  return v_operand(tile, kk, c0, g4, n16);
+}
+
+// Score column operand: lane n16 gets P[32kk + 4g + 16(e/4) + e%4][s0 + n16] from a
+// [64][64] score tile.
+__device__ __forceinline__ bf16x8 score_col_operand(const uint8_t* sP, int kk, int s0, int g4, int n16) {
+  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 16, c)));
+}
+
+// Score row operand: lane n16 gets P[t][32kk + 4g + 16(e/4) + e%4].
+__device__ __forceinline__ bf16x8 score_row_operand(const uint8_t* sP, int t, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
+                   lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
+}
+
+__device__ __forceinline__ bf16x8 negate(bf16x8 x) {
+  uint4 u = __builtin_bit_cast(uint4, x);
+  u.x ^= 0x80008000u;
+  u.y ^= 0x80008000u;
+  u.z ^= 0x80008000u;
+  u.w ^= 0x80008000u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ void store_f32x4(float* dst, f32x4 x) {
+  *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+template <bool kWeights>
+__global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(BackwardParams bp) {
+  const PrefillParams& p = bp.f;
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sU[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sdP[kC * kScoreRowBytes];
+  // S^T and G^T snapshots; during the scores of an exact chunk the lo tiles of qh,
+  // kh and du live here instead
+  __shared__ __attribute__((aligned(16))) uint8_t sX[2 * kSnapBytes];
+  uint8_t* const sST = sX;
+  uint8_t* const sGT = sX + kSnapBytes;
+  uint8_t* const sQl = sX;
+  uint8_t* const sKl = sX + kTileBytes;
+  uint8_t* const sUl = sX + 2 * kTileBytes;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int j = tid & 15, rg = tid >> 4;
+  const Tile tl = decode_tile(p);
+  const int64_t rs = (int64_t)p.H * kD;
+
+  float wq[8], wk[8];
+  load_norm_weights(p.qw, j, wq);
+  load_norm_weights(p.kw, j, wk);
+  Rope L;
+  rope_init<32>(p, tid, rg, j, L);
+  double rev[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) rev[e] = p.freqs.rev[4 * j + e];
+
+  // S (forward) and G (gradient) states at the segment's first token: columns [16w, 16w + 16)
+  f32x4 Sacc[8], Gacc[8];
+  {
+    const float* gst = bp.wsg + (tl.state - p.ws);
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Sacc[rtk][r] = tl.state[state_elem(rtk, r, w, g4, n16)];
+        Gacc[rtk][r] = gst[state_elem(rtk, r, w, g4, n16)];
+      }
+  }
+  // score tiles above the diagonal are never written
+  for (int i = tid; i < kC * kScoreRowBytes / 16; i += kBwdThreads) {
+    reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
+    reinterpret_cast<uint4*>(sdP)[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  for (int c = 0; c < tl.nch; ++c) {
+    const int t0 = tl.t_begin + c * kC;
+    const int nv = min(kC, tl.t_end - t0);
+    const bool exact = (tl.seg == 0 && c == 0) || t0 + 2 * kC > p.T;
+    // ---- staging: qh, kh (prologue), v, du = do * sigmoid(g)
+    {
+      Rows<2> Qr, Kr, Vr, Dr, Gr;
+      const int64_t off = tl.base + (int64_t)t0 * rs;
+      load_rows<2, 32>(p.q + off, rs, nv, rg, j, Qr);
+      load_rows<2, 32>(p.k + off, rs, nv, rg, j, Kr);
+      load_rows<2, 32>(p.v + off, rs, nv, rg, j, Vr);
+      load_rows<2, 32>(p.dout + off, rs, nv, rg, j, Dr);
+      load_rows<2, 32>(p.g + off, rs, nv, rg, j, Gr);
+      float2 E[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
+      float2 E2[4] = {E[0], E[1], E[2], E[3]};
+      norm_rope_rows<kWeights, 2, 32, kC>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
+      norm_rope_rows<kWeights, 2, 32, kC>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
+      store_rows_masked<2, 32>(sV, Vr, nv, rg, j);
+      du_stage<2, 32>(sU, exact ? sUl : nullptr, Dr, Gr, nv, rg, j);
+    }
+    __syncthreads();
+    // ---- scores P = Qh Kh^T and dP = dU V^T (masked to s <= t), 20 tiles over 8 waves
+    for (int idx = w; idx < 20; idx += 8) {
+      const bool grad = idx >= 10;
+      const int ti = grad ? idx - 10 : idx;
+      const int rt = (kTileRT >> (2 * ti)) & 3, st = (kTileST >> (2 * ti)) & 3;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ++ks) {
+        const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
+        const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
+        if (!grad) {
+          const bf16x8 kf = as_bf16x8(lds_ld<uint4>(sK, ka));
+          const bf16x8 qf = as_bf16x8(lds_ld<uint4>(sQ, qa));
+          if (exact) {
+            acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qf, acc);
+            acc = mma(kf, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
+          }
+          acc = mma(kf, qf, acc);
+        } else {
+          const bf16x8 vf = as_bf16x8(lds_ld<uint4>(sV, ka));
+          const bf16x8 uf = as_bf16x8(lds_ld<uint4>(sU, qa));
+          if (exact) acc = mma(vf, as_bf16x8(lds_ld<uint4>(sUl, qa)), acc);
+          acc = mma(vf, uf, acc);
+        }
+      }
+      if (st == rt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g4 + r > n16) acc[r] = 0.f;
+      }
+      lds_st<uint2>(grad ? sdP : sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
+                    make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
+    }
+    // ---- G after the chunk: G -= Qh^T dU (this wave's columns)
+    {
+      bf16x8 nU[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_operand(sU, kk, 16 * w, g4, n16));
+      accumulate_state(Gacc, sQ, nU, g4, n16);
+    }
+    __syncthreads();
+    // ---- snapshots S^T[j][i] (S before the chunk) and G^T[j][i] (G after it), bf16
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk) {
+      const int off = tile_off(16 * w + n16, 16 * rtk + 4 * g4);
+      lds_st<uint2>(sST, off, make_uint2(pack2(Sacc[rtk][0], Sacc[rtk][1]), pack2(Sacc[rtk][2], Sacc[rtk][3])));
+      lds_st<uint2>(sGT, off, make_uint2(pack2(Gacc[rtk][0], Gacc[rtk][1]), pack2(Gacc[rtk][2], Gacc[rtk][3])));
+    }
+    __syncthreads();
+    // ---- outputs of this wave's 16 columns, row block by row block
+    {
+      bf16x8 SA[4], GA[4];  // S, G as A operands (key dims in order pi)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        SA[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        GA[kk] = pack8(Gacc[2 * kk], Gacc[2 * kk + 1]);
+      }
+      bf16x8 Vf[2], Uf[2], Kf[2], Qf[2];  // columns 16w + n16 of V, dU, Kh, Qh in token order pi
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        Vf[kk] = col_operand(sV, kk, 16 * w, g4, n16);
+        Uf[kk] = col_operand(sU, kk, 16 * w, g4, n16);
+        Kf[kk] = col_operand(sK, kk, 16 * w, g4, n16);
+        Qf[kk] = col_operand(sQ, kk, 16 * w, g4, n16);
+      }
+      const int col = 16 * w + 4 * g4;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int t = 16 * rt + n16;            // row of this lane in the chunk
+        const int64_t row = tl.base + (int64_t)(t0 + t) * rs + col;
+        const bool ok = t < nv;
+        // u = Qh S + (P V)  ->  dg
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mma(SA[kk], pi_operand(sQ, t, kk, g4), acc);
+#pragma unroll
+        for (int kk = 0; kk <= rt / 2; ++kk) acc = mma(Vf[kk], score_row_operand(sP, t, kk, g4), acc);
+        if (ok) {
+          const uint2 dor = *reinterpret_cast<const uint2*>(p.dout + row);
+          const uint2 gr = *reinterpret_cast<const uint2*>(p.g + row);
+          const float d[4] = {bf2f_lo(dor.x), bf2f_hi(dor.x), bf2f_lo(dor.y), bf2f_hi(dor.y)};
+          const float gg[4] = {bf2f_lo(gr.x), bf2f_hi(gr.x), bf2f_lo(gr.y), bf2f_hi(gr.y)};
+          float dg[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sg = sigmoidf_(gg[r]);
+            dg[r] = d[r] * acc[r] * sg * (1.0f - sg);
+          }
+          *reinterpret_cast<uint2*>(bp.dg + row) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+        }
+        // dQh = dU S^T + (dP Kh)
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mma(col_operand(sST, kk, 16 * w, g4, n16), pi_operand(sU, t, kk, g4), acc);
+#pragma unroll
+        for (int kk = 0; kk <= rt / 2; ++kk) acc = mma(Kf[kk], score_row_operand(sdP, t, kk, g4), acc);
+        if (ok) store_f32x4(bp.dqh + row, acc);
+        // dV = Kh G + (P^T dU)   (row t is the key token s here)
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mma(GA[kk], pi_operand(sK, t, kk, g4), acc);
+#pragma unroll
+        for (int kk = rt / 2; kk < 2; ++kk) acc = mma(Uf[kk], score_col_operand(sP, kk, 16 * rt, g4, n16), acc);
+        if (ok) *reinterpret_cast<uint2*>(bp.dv + row) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+        // dKh = V G^T + (dP^T Qh)
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = mma(col_operand(sGT, kk, 16 * w, g4, n16), pi_operand(sV, t, kk, g4), acc);
+#pragma unroll
+        for (int kk = rt / 2; kk < 2; ++kk) acc = mma(Qf[kk], score_col_operand(sdP, kk, 16 * rt, g4, n16), acc);
+        if (ok) store_f32x4(bp.dkh + row, acc);
+      }
+      // S before the next chunk: S += Kh^T V
+      accumulate_state(Sacc, sK, Vf, g4, n16);
+    }
+    __syncthreads();
+  }
+}
+
+// dx from d(rope(rmsnorm(x))) for one tensor: one wave per row, lane i holds the
+// RoPE pair (i, i + 64).  Rotating back by the same angle gives dn; then
+//     dx_i = w_i dn_i / r - x_i (sum_j w_j x_j dn_j) / (D r^3),   dw_i += dn_i x_i / r.
+// Each workgroup also leaves its part of dw in wpart[blockIdx].
+template <bool kWeights>
+__global__ __launch_bounds__(256) void la_prologue_backward_kernel(BackwardParams bp, int which) {
+  const PrefillParams& p = bp.f;
+  const uint16_t* const x = which ? p.k : p.q;
+  const float* const dy = which ? bp.dkh : bp.dqh;
+  uint16_t* const dx = which ? bp.dk : bp.dq;
+  const float* const wgt = which ? p.kw : p.qw;
+  __shared__ float sw[4][kD];
+
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const bool has_w = kWeights && wgt != nullptr;
+  const float w0 = has_w ? wgt[lane] : 1.0f, w1 = has_w ? wgt[lane + kHalf] : 1.0f;
+  const double rev = p.freqs.rev[lane];
+  float acc0 = 0.f, acc1 = 0.f;
+  const int64_t rows = (int64_t)p.B * p.T * p.H;
+  for (int64_t r = (int64_t)blockIdx.x * 4 + wv; r < rows; r += (int64_t)gridDim.x * 4) {
+    const int64_t t = (r / p.H) % p.T;
+    const float x0 = bf2f(x[r * kD + lane]), x1 = bf2f(x[r * kD + lane + kHalf]);
+    const float d0 = dy[r * kD + lane], d1 = dy[r * kD + lane + kHalf];
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+    const float inv = rsqrt_(ss * (1.0f / kD) + p.eps);
+    const float2 rot = rope_rotation(p.pos0 + t, rev);
+    const float n0 = d0 * rot.x + d1 * rot.y;
+    const float n1 = d1 * rot.x - d0 * rot.y;
+    float dot = w0 * x0 * n0 + w1 * x1 * n1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
+    const float k3 = dot * inv * inv * inv * (1.0f / kD);
+    dx[r * kD + lane] = f2bf(w0 * n0 * inv - x0 * k3);
+    dx[r * kD + lane + kHalf] = f2bf(w1 * n1 * inv - x1 * k3);
+    if (kWeights) {
+      acc0 += n0 * x0 * inv;
+      acc1 += n1 * x1 * inv;
+    }
+  }
+  if (kWeights) {
+    sw[wv][lane] = acc0;
+    sw[wv][lane + kHalf] = acc1;
+    __syncthreads();
+    if (threadIdx.x < kD) {
+      const int i = threadIdx.x;
+      bp.wpart[((int64_t)which * kPrologueBlocks + blockIdx.x) * kD + i] = sw[0][i] + sw[1][i] + sw[2][i] + sw[3][i];
+    }
+  }
+}
+
+// dw[i] = sum of the workgroup parts (fixed order).
+__global__ __launch_bounds__(256) void la_weight_grad_kernel(BackwardParams bp, int nblocks) {
+  const int i = threadIdx.x & (kD - 1), which = threadIdx.x >> 7;
+  float* const out = which ? bp.dk_w : bp.dq_w;
+  if (out == nullptr) return;
+  float s = 0.f;
+  for (int b = 0; b < nblocks; ++b) s += bp.wpart[((int64_t)which * kPrologueBlocks + b) * kD + i];
+  out[i] = s;
+}
+
+}  // namespace
+
+hipError_t launch_backward_chunks(const BackwardParams& bp, const PrefillPlan& plan, hipStream_t stream) {
+  const PrefillParams& p = bp.f;
+  // weight gradients without weights are taken at weights of one
+  const bool weights = p.qw != nullptr || p.kw != nullptr || bp.dq_w != nullptr || bp.dk_w != nullptr;
+  const dim3 grid((unsigned)(plan.nwork * p.H));
+  if (weights)
+    hipLaunchKernelGGL(la_backward_chunk_kernel<true>, grid, dim3(kBwdThreads), 0, stream, bp);
+  else
+    hipLaunchKernelGGL(la_backward_chunk_kernel<false>, grid, dim3(kBwdThreads), 0, stream, bp);
+  const int64_t rows = (int64_t)p.B * p.T * p.H;
+  const int nblocks = (int)std::min<int64_t>(kPrologueBlocks, (rows + 3) / 4);
+  for (int which = 0; which < 2; ++which) {
+    if (weights)
+      hipLaunchKernelGGL(la_prologue_backward_kernel<true>, dim3(nblocks), dim3(256), 0, stream, bp, which);
+    else
+      hipLaunchKernelGGL(la_prologue_backward_kernel<false>, dim3(nblocks), dim3(256), 0, stream, bp, which);
+  }
+  if (weights) hipLaunchKernelGGL(la_weight_grad_kernel, dim3(1), dim3(256), 0, stream, bp, nblocks);
+  return hipGetLastError();
+}
+
+}  // namespace la

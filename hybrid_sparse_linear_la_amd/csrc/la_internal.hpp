@@ -67,6 +67,7 @@ struct PrefillParams {
   float* S_out;       // [B][H][D][D]
   const float* qw;    // [D] or nullptr
   const float* kw;    // [D] or nullptr
+  const uint16_t* dout;  // backward only: gradient of o, [B][T][H][D]
   int B, T, H, nseg, cps;
   int64_t pos0;
   float eps;
@@ -107,5 +108,28 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipStream_t stream,
                           hipEvent_t const* events = nullptr);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// Backward of la_prefill (chunk 64, equal-length batches).
+struct BackwardParams {
+  PrefillParams f;  // forward inputs; f.ws: forward segment states, f.dout: gradient of o
+  float* wsg;       // gradient segment states, same layout as f.ws
+  const float* dS_out;  // [B][H][D][D] or nullptr
+  float* dS_in;         // [B][H][D][D]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  uint16_t* dg;
+  float* dqh;       // [B][T][H][D] fp32 scratch: gradients of the rotated, normalized q and k
+  float* dkh;
+  float* dq_w;      // [D] or nullptr (norm-weight gradients)
+  float* dk_w;
+  float* wpart;     // [2][kPrologueBlocks][D] fp32 scratch for the weight gradients
+};
+constexpr int kPrologueBlocks = 1024;
+
+// The forward segment states of la_prefill into f.ws (f.S_out receives the final
+// state), then the gradient segment states into wsg and dS_in.
+hipError_t launch_segment_states(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
+hipError_t launch_backward_chunks(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
 
 }  // namespace la

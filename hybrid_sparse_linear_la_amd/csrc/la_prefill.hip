@@ -37,280 +37,16 @@
 //     is ever written transposed.
 #include "la_device.hpp"
 #include "la_internal.hpp"
+#include "la_tiles.hpp"
 
 namespace la {
 namespace {
 
-constexpr int kC = 64;      // tokens per chunk
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowBytes = kD * 2 + 16;     // 128 bf16 + 16 bytes of padding
-constexpr int kTileBytes = kC * kRowBytes;  // one [64][128] bf16 tile
-constexpr int kExactRows = 16;              // rows whose scores use the hi/lo split
-
-typedef short bf16x4 __attribute__((ext_vector_type(4)));
-
-// [64][128] bf16 row tile with 272-byte rows: consecutive rows start 16 bytes
-// apart in the bank space, so the 8-byte operand reads (16 rows x 4 lane
-// groups), the transposed reads (4 rows x 4 groups) and the staging writes all
-// spread over the banks, and every offset is linear (immediate offsets).
-__device__ __forceinline__ int tile_off(int t, int d) { return t * kRowBytes + 2 * d; }
-
-// Transposed read: within each 16-lane group, lane L supplies the address of 4
-// bf16 and receives element L of each of the 4 rows formed by lanes 4r..4r+3.
-// Reading rows t0 + L / 4, columns c0 + 4 (L % 4) of a row tile gives lane L the
-// column c0 + L at rows t0 .. t0 + 3.
-__device__ __forceinline__ uint2 lds_tr(const uint8_t* base, int off) {
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_bf16x4*)(base + off));
-  return __builtin_bit_cast(uint2, v);
-}
-
-// Sum over the 16 lanes of a DPP row (quad swaps, then rotations by 4 and 8).
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
-  return x;
-}
-
-// Staging coordinates: a thread (rg, j) holds rows rg + kStep m (m < M) of a
-// chunk and dims {4j..4j+3} U {64+4j..64+4j+3}: each RoPE pair (i, i + 64) sits
-// in one thread, and 16 consecutive lanes cover a row.
-template <int M>
-struct Rows {
-  uint2 lo[M];  // dims 4j..4j+3, four bf16
-  uint2 hi[M];  // dims 64+4j..64+4j+3
-};
-
-// Unmasked, branch-free loads: rows at or beyond nvalid (>= 1) re-read the last
-// valid row, keeping every address inside the tensor.  Such rows of q, k and the
-// gate only reach masked scores and unstored outputs; v's are zeroed when staged.
-template <int M, int kStep>
-__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, int64_t rs, int nvalid,
-                                          int rg, int j, Rows<M>& R) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint16_t* src = base + (int64_t)min(rg + kStep * m, nvalid - 1) * rs;
-    R.lo[m] = ld_stream(src + 4 * j);
-    R.hi[m] = ld_stream(src + kHalf + 4 * j);
-  }
-}
-
-template <int M, int kStep>
-__device__ __forceinline__ void store_rows_masked(uint8_t* tile, const Rows<M>& R, int nvalid, int rg,
-                                                  int j) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const bool ok = rg + kStep * m < nvalid;
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), ok ? R.lo[m] : make_uint2(0u, 0u));
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), ok ? R.hi[m] : make_uint2(0u, 0u));
-  }
-}
-
-// sigmoid of the gate logits, staged as f16 (the value lies in (0, 1); f16 keeps
-// 11 significant bits, round toward zero).
-template <int M, int kStep>
-__device__ __forceinline__ void sigmoid_stage(uint8_t* tile, const Rows<M>& R, int rg, int j) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const uint2 a = R.lo[m], b = R.hi[m];
-    const uint2 lo = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(a.x)), sigmoidf_(bf2f_hi(a.x))),
-                                pack_f16x2(sigmoidf_(bf2f_lo(a.y)), sigmoidf_(bf2f_hi(a.y))));
-    const uint2 hi = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(b.x)), sigmoidf_(bf2f_hi(b.x))),
-                                pack_f16x2(sigmoidf_(bf2f_lo(b.y)), sigmoidf_(bf2f_hi(b.y))));
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), lo);
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), hi);
-  }
-}
-
-// RoPE per thread: A[e] = e^{i rg theta}, Z[e] = e^{i kStep theta} for the
-// thread's frequencies 4j+e; row rg + kStep m of a chunk at position p0 is
-// rotated by base(p0) * A * Z^m.  base_rev is the frequency of pair i = tid % 64,
-// for the per-chunk base rotation, kept in a register so the loop loads nothing.
-struct Rope {
-  float2 A[4];
-  float2 Z[4];
-  double base_rev;
-};
-
-template <int kStep>
-__device__ __forceinline__ void rope_init(const PrefillParams& p, int tid, int rg, int j, Rope& L) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const double rv = p.freqs.rev[4 * j + e];
-    L.A[e] = rope_rotation(rg, rv);
-    L.Z[e] = rope_rotation(kStep, rv);
-  }
-  L.base_rev = p.freqs.rev[tid & (kHalf - 1)];
-}
-
-// QK-normalization (RMSNorm over the 128 dims of row t, weights w) followed by
-// rotate-half RoPE with rotations E, in fp32; the bf16 result goes to `tile`.
-// With `lo` set, rows below kExactRows also store lo = bf16(y - bf16(y)) into
-// `lo`, for the scores of the first rows of a call.
-template <bool kWeights>
-__device__ __forceinline__ void norm_rope_row(uint2 rl, uint2 rh, const float (&w)[8], float eps,
-                                              const float2 (&E)[4], int t, int j, uint8_t* tile,
-                                              uint8_t* lo) {
-  const float ss = dot2_bf16(rh.y, rh.y, dot2_bf16(rh.x, rh.x, dot2_bf16(rl.y, rl.y, dot2_bf16(rl.x, rl.x, 0.f))));
-  const float inv = rsqrt_(row16_sum(ss) * (1.0f / kD) + eps);
-  const float x[8] = {bf2f_lo(rl.x), bf2f_hi(rl.x), bf2f_lo(rl.y), bf2f_hi(rl.y),
-                      bf2f_lo(rh.x), bf2f_hi(rh.x), bf2f_lo(rh.y), bf2f_hi(rh.y)};
-  float y[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = kWeights ? x[e] * w[e] : x[e];
-    const float b = kWeights ? x[4 + e] * w[4 + e] : x[4 + e];
-    const float c = E[e].x * inv, s = E[e].y * inv;
-    y[e] = fmaf(a, c, -b * s);
-    y[4 + e] = fmaf(b, c, a * s);
-  }
-  const uint2 hlo = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
-  const uint2 hhi = make_uint2(pack2(y[4], y[5]), pack2(y[6], y[7]));
-  lds_st<uint2>(tile, tile_off(t, 4 * j), hlo);
-  lds_st<uint2>(tile, tile_off(t, kHalf + 4 * j), hhi);
-  if (lo != nullptr && t < kExactRows) {
-    const uint2 llo = make_uint2(pack2(y[0] - bf2f_lo(hlo.x), y[1] - bf2f_hi(hlo.x)),
-                                 pack2(y[2] - bf2f_lo(hlo.y), y[3] - bf2f_hi(hlo.y)));
-    const uint2 lhi = make_uint2(pack2(y[4] - bf2f_lo(hhi.x), y[5] - bf2f_hi(hhi.x)),
-                                 pack2(y[6] - bf2f_lo(hhi.y), y[7] - bf2f_hi(hhi.y)));
-    lds_st<uint2>(lo, tile_off(t, 4 * j), llo);
-    lds_st<uint2>(lo, tile_off(t, kHalf + 4 * j), lhi);
-  }
-}
-
-// Rotations of the thread's rows rg + kStep m at its frequencies 4j + e, from the
-// chunk's base rotations sRot: E_0 = sRot * A, E_m = E_{m-1} * Z.
-template <int kStep>
-__device__ __forceinline__ void first_rotation(const float2* sRot, const Rope& L, int j, float2 (&E)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) E[e] = cmul(sRot[4 * j + e], L.A[e]);
-}
-__device__ __forceinline__ void next_rotation(const Rope& L, float2 (&E)[4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) E[e] = cmul(E[e], L.Z[e]);
-}
-
-// One tensor (k in the state kernel).
-template <bool kWeights, int M, int kStep>
-__device__ __forceinline__ void norm_rope_stage(const Rows<M>& R, const float (&w)[8], float eps,
-                                                const float2* sRot, const Rope& L, int rg, int j,
-                                                uint8_t* tile) {
-  float2 E[4];
-  first_rotation<kStep>(sRot, L, j, E);
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (m > 0) next_rotation(L, E);
-    norm_rope_row<kWeights>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, nullptr);
-  }
-}
-
-// One tensor, with the first row's rotations E already formed (advanced in place).
-template <bool kWeights, int M, int kStep>
-__device__ __forceinline__ void norm_rope_rows(const Rows<M>& R, const float (&w)[8], float eps, float2 (&E)[4],
-                                               const Rope& L, int rg, int j, uint8_t* tile, uint8_t* lo) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (m > 0) next_rotation(L, E);
-    norm_rope_row<kWeights>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, lo);
-  }
-}
-
-// q and k of the same rows share one rotation chain.
-template <bool kWeights, int M, int kStep>
-__device__ __forceinline__ void norm_rope_stage_qk(const Rows<M>& Qr, const Rows<M>& Kr, const float (&wq)[8],
-                                                   const float (&wk)[8], float eps, const float2* sRot,
-                                                   const Rope& L, int rg, int j, uint8_t* tq, uint8_t* tk,
-                                                   uint8_t* lq, uint8_t* lk) {
-  float2 E[4];
-  first_rotation<kStep>(sRot, L, j, E);
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (m > 0) next_rotation(L, E);
-    const int t = rg + kStep * m;
-    norm_rope_row<kWeights>(Qr.lo[m], Qr.hi[m], wq, eps, E, t, j, tq, lq);
-    norm_rope_row<kWeights>(Kr.lo[m], Kr.hi[m], wk, eps, E, t, j, tk, lk);
-  }
-}
-
-__device__ __forceinline__ void load_norm_weights(const float* w, int j, float (&out)[8]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    out[e] = w ? w[4 * j + e] : 1.0f;
-    out[4 + e] = w ? w[kHalf + 4 * j + e] : 1.0f;
-  }
-}
-
-struct Tile {
-  int b, h, seg, t_begin, t_end, nch;
-  int64_t base;      // element offset of (row 0, h, d = 0) for the rows of this tile's sequence
-  int64_t pos_base;  // absolute position of row 0 in those rows
-  float* state;      // this (b, h, segment)'s D x D state in the workspace
-};
-
-// Workgroup -> (b, h, segment).  Equal-length batches: blockIdx = h + H (seg +
-// nseg b), rows t of sequence b.  Variable-length batches: blockIdx = h + H s for
-// segment s of the table, rows t of the packed activations.
-__device__ __forceinline__ Tile decode_tile(const PrefillParams& p) {
-  Tile tl;
-  int bid = blockIdx.x;
-  tl.h = bid % p.H;
-  bid /= p.H;
-  if (p.segs != nullptr) {
-    const SegDesc d = p.segs[bid];
-    tl.b = d.seq;
-    tl.seg = d.seg_local;
-    tl.t_begin = d.t_begin;
-    tl.t_end = d.t_end;
-    tl.base = (int64_t)tl.h * kD;
-    tl.pos_base = d.pos_base;
-    tl.state = p.ws + ((int64_t)bid * p.H + tl.h) * kD * kD;
-  } else {
-    tl.seg = bid % p.nseg;
-    tl.b = bid / p.nseg;
-    tl.t_begin = tl.seg * p.cps * kC;
-    tl.t_end = min(p.T, tl.t_begin + p.cps * kC);
-    tl.base = ((int64_t)tl.b * p.T * p.H + tl.h) * kD;
-    tl.pos_base = p.pos0;
-    tl.state = p.ws + (((int64_t)tl.b * p.H + tl.h) * p.nseg + tl.seg) * kD * kD;
-  }
-  tl.nch = (tl.t_end - tl.t_begin + kC - 1) / kC;
-  return tl;
-}
-
-// S accumulator tile rtk of wave w: lane (g, n16) element r is
-// S[16 rtk + 4 g + r][16 w + n16].
-__device__ __forceinline__ int64_t state_elem(int rtk, int r, int w, int g4, int n16) {
-  return (int64_t)(16 * rtk + 4 * g4 + r) * kD + 16 * w + n16;
-}
-
-// Token-contraction operand of V: lane n16 gets V[32kk + 4g + 16(e/4) + e%4][c0 + n16].
-__device__ __forceinline__ bf16x8 v_operand(const uint8_t* sV, int kk, int c0, int g4, int n16) {
-  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
-  return as_bf16x8(lds_tr(sV, tile_off(t0, c)), lds_tr(sV, tile_off(t0 + 16, c)));
-}
-
-// S[:, 16w .. 16w+16) += Kh^T V over one chunk.
-__device__ __forceinline__ void accumulate_state(f32x4 (&Sacc)[8], const uint8_t* sK,
-                                                 const bf16x8 (&Vop)[2], int g4, int n16) {
-#pragma unroll
-  for (int kk = 0; kk < kC / 32; ++kk) {
-    const int t0 = 32 * kk + 4 * g4 + (n16 >> 2);
-#pragma unroll
-    for (int rtk = 0; rtk < 8; ++rtk) {
-      const int c = 16 * rtk + 4 * (n16 & 3);
-      const bf16x8 a = as_bf16x8(lds_tr(sK, tile_off(t0, c)), lds_tr(sK, tile_off(t0 + 16, c)));
-      Sacc[rtk] = mma(a, Vop[kk], Sacc[rtk]);
-    }
-  }
-}
-
 // --------------------------------------------------------------------------
 // Kh^T V summed over each segment.  LDS is double-buffered, so one barrier per
-// chunk separates staging from use.
-template <bool kWeights>
+// chunk separates staging from use.  With kGrad, the same sum for the backward:
+// Qh^T dU, the "keys" being the prologue of q and the "values" du = do * sigmoid(g).
+template <bool kWeights, bool kGrad>
 __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
@@ -321,9 +57,11 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
   const int j = tid & 15, rg = tid >> 4;
   const Tile tl = decode_tile(p);
   const int64_t rs = (int64_t)p.H * kD;
+  const uint16_t* const kin = kGrad ? p.q : p.k;
+  const uint16_t* const vin = kGrad ? p.dout : p.v;
 
   float wk[8];
-  load_norm_weights(p.kw, j, wk);
+  load_norm_weights(kGrad ? p.qw : p.kw, j, wk);
   Rope L;
   rope_init<32>(p, tid, rg, j, L);
 
@@ -331,12 +69,13 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
 #pragma unroll
   for (int a = 0; a < 8; ++a) Sacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Rows<2> Kr, Vr;
-  {
-    const int nv = min(kC, tl.t_end - tl.t_begin);
-    load_rows<2, 32>(p.k + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Kr);
-    load_rows<2, 32>(p.v + tl.base + (int64_t)tl.t_begin * rs, rs, nv, rg, j, Vr);
-  }
+  Rows<2> Kr, Vr, Gr;
+  auto load = [&](int t, int nv) {
+    load_rows<2, 32>(kin + tl.base + (int64_t)t * rs, rs, nv, rg, j, Kr);
+    load_rows<2, 32>(vin + tl.base + (int64_t)t * rs, rs, nv, rg, j, Vr);
+    if (kGrad) load_rows<2, 32>(p.g + tl.base + (int64_t)t * rs, rs, nv, rg, j, Gr);
+  };
+  load(tl.t_begin, min(kC, tl.t_end - tl.t_begin));
   if (tid < kHalf) sRot[0][tid] = rope_rotation(tl.pos_base + tl.t_begin, L.base_rev);
   __syncthreads();
 
@@ -346,12 +85,13 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
     uint8_t* bK = sK[c & 1];
     uint8_t* bV = sV[c & 1];
     norm_rope_stage<kWeights, 2, 32>(Kr, wk, p.eps, sRot[c & 1], L, rg, j, bK);
-    store_rows_masked<2, 32>(bV, Vr, nv, rg, j);
+    if (kGrad)
+      du_stage<2, 32>(bV, nullptr, Vr, Gr, nv, rg, j);
+    else
+      store_rows_masked<2, 32>(bV, Vr, nv, rg, j);
     if (c + 1 < tl.nch) {
       const int t1 = t0 + kC;
-      const int nv1 = min(kC, tl.t_end - t1);
-      load_rows<2, 32>(p.k + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Kr);
-      load_rows<2, 32>(p.v + tl.base + (int64_t)t1 * rs, rs, nv1, rg, j, Vr);
+      load(t1, min(kC, tl.t_end - t1));
       if (tid < kHalf) sRot[(c + 1) & 1][tid] = rope_rotation(tl.pos_base + t1, L.base_rev);
     }
     __syncthreads();
@@ -373,6 +113,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
 // inclusive total is the final state.  One thread per 4 consecutive elements.
 // A variable-length batch walks each sequence's own run of segments (none for an
 // empty sequence, whose final state is S_in) and skips single-token sequences.
+// kReverse (backward): the inclusive suffix seeded with dS_out (in S_in), so each
+// segment gets the state gradient at its first token; the total goes to S_out.
+template <bool kReverse>
 __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
   constexpr int64_t per = kD * kD / 4;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -389,13 +132,15 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
     stride = (int64_t)p.H * per;
   }
   float4 run = p.S_in ? reinterpret_cast<const float4*>(p.S_in)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < nseg; ++s) {
+  for (int i = 0; i < nseg; ++i) {
+    const int s = kReverse ? nseg - 1 - i : i;
     const float4 d = ws[s * stride];
-    ws[s * stride] = run;
+    if (!kReverse) ws[s * stride] = run;
     run.x += d.x;
     run.y += d.y;
     run.z += d.z;
     run.w += d.w;
+    if (kReverse) ws[s * stride] = run;
   }
   reinterpret_cast<float4*>(p.S_out)[idx] = run;
 }
@@ -408,12 +153,6 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
 constexpr int kConsumers = 256;               // 4 consumer waves
 constexpr int kProducers = 512;               // 8 producer waves
 constexpr int kOutThreads = kConsumers + kProducers;
-
-// Consumer operand in key order pi: lane n16 gets X[row][32kk + 4g + 16(e/4) + e%4].
-__device__ __forceinline__ bf16x8 pi_operand(const uint8_t* tile, int row, int kk, int g4) {
-  return as_bf16x8(lds_ld<uint2>(tile, tile_off(row, 32 * kk + 4 * g4)),
-                   lds_ld<uint2>(tile, tile_off(row, 32 * kk + 16 + 4 * g4)));
-}
 
 template <bool kWeights>
 __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, uint8_t (*sQ)[kTileBytes],
@@ -479,15 +218,6 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
     if (c + 1 < tl.nch) step(c + 1, Y);
   }
 }
-
-// Score tiles (row block rt, key block st <= rt) of a chunk dealt to the 4 consumer
-// waves (3/3/2/2): tile idx has rt = (kTileRT >> 2 idx) & 3, st = (kTileST >> 2 idx)
-// & 3 for the order (0,0) (1,1) (2,2) (3,3) (1,0) (2,1) (3,2) (2,0) (3,1) (3,0).
-constexpr uint32_t kTileRT = 0xfb9e4;
-constexpr uint32_t kTileST = 0x124e4;
-constexpr int kScoreRowBytes = kC * 2 + 16;  // [64][64] bf16 score tile, padded rows
-
-__device__ __forceinline__ int score_off(int t, int s) { return t * kScoreRowBytes + 2 * s; }
 
 // Phase A of a consumer chunk: this wave's share of the masked scores P = Qh Kh^T
 // (computed as P^T tiles, lane holding 4 consecutive keys of one query) into the
@@ -821,13 +551,13 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
   mark(0);
   if (plan.nwork > 0) {
     if (weights)
-      hipLaunchKernelGGL(la_chunk_state_kernel<true>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((la_chunk_state_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
     else
-      hipLaunchKernelGGL(la_chunk_state_kernel<false>, grid, dim3(kThreads), 0, stream, p);
+      hipLaunchKernelGGL((la_chunk_state_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
   }
   mark(1);
   if (plan.scan)
-    hipLaunchKernelGGL(la_state_scan_kernel, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(la_state_scan_kernel<false>, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
                        stream, p);
   mark(2);
   if (plan.nwork > 0 && plan.C == kC) {
@@ -849,6 +579,27 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
   mark(3);
   const hipError_t launch = hipGetLastError();
   return err != hipSuccess ? err : launch;
+}
+
+hipError_t launch_segment_states(const BackwardParams& bp, const PrefillPlan& plan, hipStream_t stream) {
+  const dim3 grid((unsigned)(plan.nwork * bp.f.H));
+  const dim3 scan_grid((unsigned)(((int64_t)bp.f.B * bp.f.H * kD * kD / 4 + 255) / 256));
+  PrefillParams f = bp.f;  // forward states into f.ws, final state into f.S_out
+  if (f.kw)
+    hipLaunchKernelGGL((la_chunk_state_kernel<true, false>), grid, dim3(kThreads), 0, stream, f);
+  else
+    hipLaunchKernelGGL((la_chunk_state_kernel<false, false>), grid, dim3(kThreads), 0, stream, f);
+  hipLaunchKernelGGL(la_state_scan_kernel<false>, scan_grid, dim3(256), 0, stream, f);
+  PrefillParams g = bp.f;  // gradient states: sums of Qh^T dU, suffix-scanned from dS_out
+  g.ws = bp.wsg;
+  g.S_in = bp.dS_out;
+  g.S_out = bp.dS_in;
+  if (g.qw)
+    hipLaunchKernelGGL((la_chunk_state_kernel<true, true>), grid, dim3(kThreads), 0, stream, g);
+  else
+    hipLaunchKernelGGL((la_chunk_state_kernel<false, true>), grid, dim3(kThreads), 0, stream, g);
+  hipLaunchKernelGGL(la_state_scan_kernel<true>, scan_grid, dim3(256), 0, stream, g);
+  return hipGetLastError();
 }
 
 }  // namespace la

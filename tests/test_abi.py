@@ -27,7 +27,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
          "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_linear", "la_layer_workspace_bytes",
-         "la_layer_forward", "la_decode_step"])
+         "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_decode_step"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -199,3 +199,26 @@ def test_linear_and_layer_validation(lib):
     assert layer(y=A + 1024) == 5            # y overlaps x
     assert layer(ws=A + 256 * MB) == 5       # workspace overlaps y
     assert layer(ws_bytes=4096) == 6
+
+
+def test_backward_validation(lib):
+    vp = ctypes.c_void_p
+    assert lib.la_backward_workspace_bytes(1, 300, 2, 128, 128) == 0   # chunk 64 only
+    assert lib.la_backward_workspace_bytes(1, 300, 2, 128, 0) > 2 * lib.la_prefill_workspace_bytes(1, 300, 2, 128, 0)
+
+    def bwd(q=A, k=A + MB, v=A + 2 * MB, g=A + 3 * MB, S_in=None, d_o=A + 4 * MB, dS_out=None, dq=A + 8 * MB,
+            dk=A + 9 * MB, dv=A + 10 * MB, dg=A + 11 * MB, dS_in=A + 12 * MB, B=1, T=300, H=2, D=128, chunk=0,
+            ws=A + 64 * MB, ws_bytes=1 << 30):
+        return lib.la_backward(vp(q), vp(k), vp(v), vp(g), vp(S_in), vp(d_o), vp(dS_out), vp(dq), vp(dk), vp(dv),
+                               vp(dg), vp(dS_in), None, None, B, T, H, D, 0, chunk, 10000.0, 1e-6, None, None,
+                               vp(ws), ws_bytes, None)
+    assert bwd(d_o=None) == 1
+    assert bwd(dS_in=None) == 1
+    assert bwd(T=0) == 2
+    assert bwd(chunk=128) == 3
+    assert bwd(D=64) == 3
+    assert bwd(dq=A + 8 * MB + 4) == 4
+    assert bwd(dq=A + 1024) == 5          # dq overlaps q
+    assert bwd(dk=A + 8 * MB + 64) == 5   # dk overlaps dq
+    assert bwd(ws=A + 12 * MB) == 5       # workspace overlaps dS_in
+    assert bwd(ws_bytes=4096) == 6

@@ -1,0 +1,96 @@
+"""GPU parity of la_backward (gradients of the prefill) against the fp64 oracle's
+reverse mode: dq, dk, dv, dgate per (b, t, h) row, dS_in per (b, h), the
+norm-weight gradients, on ragged and multi-segment shapes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_o_close, assert_S_close, to_np, to_np32
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def la():
+    import hybrid_sparse_linear_la_amd as la
+    la.library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return la
+
+
+def _inputs(B, T, H, seed, S_std, dS_std, weights):
+    gen = workloads.generator(seed, "cuda")
+    q, k, v, g = workloads.activations(B, T, H, D, seed, "cuda", gen=gen)
+    d_o = torch.randn((B, T, H, D), generator=gen, device="cuda").to(torch.bfloat16)
+    S_in = workloads.state(B, H, D, S_std, gen, "cuda") if S_std else None
+    dS_out = workloads.state(B, H, D, dS_std, gen, "cuda") if dS_std else None
+    qw = kw = None
+    if weights:
+        qw = torch.rand(D, generator=gen, device="cuda") + 0.5
+        kw = torch.rand(D, generator=gen, device="cuda") + 0.5
+    return q, k, v, g, d_o, S_in, dS_out, qw, kw
+
+
+def _check(grads, q, k, v, g, d_o, S_in, dS_out, pos0, qw, kw, weight_grads):
+    ref = oracle.backward(to_np32(q), to_np32(k), to_np32(v), to_np32(g), to_np32(d_o),
+                          S=None if S_in is None else to_np(S_in),
+                          dS_out=None if dS_out is None else to_np(dS_out), pos0=pos0,
+                          q_w=to_np32(qw) if qw is not None else (np.ones(D, np.float32) if weight_grads else None),
+                          k_w=to_np32(kw) if kw is not None else (np.ones(D, np.float32) if weight_grads else None))
+    errs = {}
+    for name, key in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dgate", "dg")):
+        errs[name] = assert_o_close(to_np(grads[name]), ref[key], what=name)["max"]
+    errs["dS_in"] = assert_S_close(to_np(grads["dS_in"]), ref["dS_in"], what="dS_in")["fro"]
+    if weight_grads:
+        for name, key in (("dq_norm_w", "dq_w"), ("dk_norm_w", "dk_w")):
+            got, want = to_np(grads[name]), ref[key]
+            rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+            assert rel <= 1e-2, f"{name}: relative error {rel:.2e}"
+            errs[name] = rel
+    return errs
+
+
+CASES = [
+    # B, T, H, pos0, S_std, dS_std, weights, weight_grads
+    (1, 1, 1, 0, 0.0, 0.0, False, False),
+    (1, 2, 2, 0, 0.0, 0.0, False, False),
+    (1, 63, 2, 0, 0.0, 0.0, False, False),
+    (1, 64, 1, 0, 0.0, 0.0, False, False),
+    (2, 65, 2, 5, 0.5, 0.3, False, False),
+    (1, 129, 2, 7, 0.0, 0.0, False, False),
+    (1, 300, 3, 262144, 0.2, 0.5, True, True),
+    (2, 1000, 4, 1000, 0.0, 0.0, False, True),
+    (1, 4096, 32, 0, 0.0, 0.0, False, False),       # several segments per head
+    (2, 5000, 8, 1048000, 0.1, 0.1, True, True),    # ragged last chunk, several segments
+]
+
+
+@pytest.mark.parametrize("B,T,H,pos0,S_std,dS_std,weights,weight_grads", CASES)
+def test_backward_matches_oracle(la, B, T, H, pos0, S_std, dS_std, weights, weight_grads):
+    print(f"backward case B={B} T={T} H={H} pos0={pos0} weights={weights}", flush=True)
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 500 + T, S_std, dS_std, weights)
+    grads = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, pos0=pos0, q_norm_w=qw, k_norm_w=kw,
+                        weight_grads=weight_grads)
+    torch.cuda.synchronize()
+    errs = _check(grads, q, k, v, g, d_o, S_in, dS_out, pos0, qw, kw, weight_grads)
+    print(f"  errors {errs}", flush=True)
+
+
+def test_backward_is_deterministic(la):
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(1, 3000, 16, 7, 0.1, 0.1, True)
+    a = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, q_norm_w=qw, k_norm_w=kw, weight_grads=True)
+    b = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, q_norm_w=qw, k_norm_w=kw, weight_grads=True)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+
+
+def test_backward_rejects_bad_arguments(la):
+    q, k, v, g, d_o, _, _, _, _ = _inputs(1, 64, 2, 9, 0.0, 0.0, False)
+    with pytest.raises(la.LAError):
+        la.backward(q, k, v, g, d_o, chunk=128)
+    with pytest.raises(ValueError):
+        la.backward(q, k, v, g, d_o[:, :32].contiguous())
