@@ -191,6 +191,39 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
                            const float* k_norm_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of workspace la_backward needs (0 for an invalid shape or a chunk other
+ * than 0 / 64): two sets of segment states, fp32 gradients of the rotated q and
+ * k ([B, T, H, D] each) and 1 MiB for the norm-weight gradient parts.
+ */
+size_t la_backward_workspace_bytes(int B, int T, int H, int D, int chunk);
+
+/*
+ * Gradients of la_prefill for a loss with gradient d_o of o ([B, T, H, D] bf16)
+ * and dS_out of S_out ([B, H, D, D] fp32, or NULL for zeros): the reverse mode of
+ * the recurrence S_t = S_{t-1} + k_t v_t^T, o_t = sigmoid(g_t) * (q_t S_t) of
+ * "MiniCPM-SALA: Hybridizing Sparse and Linear Attention for Efficient
+ * Long-Context Modeling" (前置知识 > 线性注意力), through the output gate, RoPE and
+ * QK-RMSNorm of the report's linear-attention module.  The pages train the
+ * converted linear layers ("創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B模型，
+ * 端側跑通百萬上下文", 04 技術報告 > 03 模型訓練).
+ *   q, k, v, gate_logits, S_in, pos0, rope_base, rms_eps, q_norm_w, k_norm_w :
+ *       the forward call's arguments (S_in may be NULL)
+ *   dq, dk, dv, dgate : [B, T, H, D] bf16 outputs
+ *   dS_in             : [B, H, D, D] fp32 output (gradient of the initial state)
+ *   dq_norm_w, dk_norm_w : [D] fp32 outputs or NULL; without norm weights they are
+ *       the gradients at weights of one
+ *   chunk : 0 or 64
+ * Outputs must not overlap each other, the inputs or the workspace.  The
+ * forward is recomputed inside the call (segment states and the pre-gate output).
+ */
+la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                      const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
+                      la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
+                      int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
+                      const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
  * One decode step: one token per sequence at absolute position pos.
  *   q, k, v, gate_logits : [B, H, D] bf16.
  *   S : [B, H, D, D] fp32 state, updated in place (S += kh v^T).

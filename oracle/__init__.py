@@ -22,7 +22,7 @@ What each function follows (pages cited by title and section):
   * ``backward`` -- the gradients of ``forward`` (reverse mode of the same
     recurrence, through the gate, RoPE and RMSNorm) for given output and
     final-state gradients; what training the converted linear layers needs
-    (technical-report page, 03 訓練: the linear layers are trained after
+    (technical-report page, 03 模型訓練: the linear layers are trained after
     conversion).
   * ``linear`` / ``layer_forward`` -- the projections around the layer (one
     fused q/k/v/gate projection and the output projection; hidden 4096, 32 heads
