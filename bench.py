@@ -19,6 +19,7 @@ Prints one JSON line (rank 0, N = 1):
             one la_prefill_varlen call, beside the same work as two calls
   layer     one layer on a 32K-token prompt (hidden 4096): q/k/v/gate projection,
             the layer, output projection; the projections against bf16 MFMA peak
+  backward  la_backward over the 256K-token input
 """
 from __future__ import annotations
 
@@ -356,6 +357,31 @@ def bench_layer(la, torch, workloads, hip, args, steps=5):
     }
 
 
+def bench_backward(la, torch, workloads, hip, tensors, steps=3):
+    """la_backward over the 256K-token prefill input (seeded output gradient)."""
+    q, k, v, g = tensors
+    B, T, H, D = q.shape
+    gen = workloads.generator(7, "cuda")
+    d_o = torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16)
+    ws = torch.empty(la.backward_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
+    la.backward(q, k, v, g, d_o, workspace=ws)
+    stream = torch.cuda.current_stream().cuda_stream
+    e = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(e[0], stream)
+    for _ in range(steps):
+        la.backward(q, k, v, g, d_o, workspace=ws)
+    hip.record(e[1], stream)
+    ms = hip.ms(e[0], e[1]) / steps
+    hip.destroy(e)
+    # bytes every backward must move: read q, k, v, g, d_o and write dq, dk, dv, dgate
+    comp = 9 * 256 * B * T * H
+    return {"workload": "backward_" + workloads.PREFILL_256K.name, "steps": steps, "ms": round(ms, 4),
+            "tokens_per_s": round(B * T / (ms / 1e3), 1), "compulsory_bytes": comp,
+            "hbm_roof_ms": round(comp / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+            "path_frac": round(comp / (HBM_PEAK_GBS * 1e9) / (ms / 1e3), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +395,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-varlen", action="store_true", help="skip the mixed prefill/decode batch")
     ap.add_argument("--no-layer", action="store_true", help="skip the layer forward with its projections")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward of the 256K prefill")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -401,6 +428,7 @@ def main():
     decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
     varlen = None if args.no_varlen else bench_varlen(la, torch, workloads, hip, args)
     layer = None if args.no_layer else bench_layer(la, torch, workloads, hip, args)
+    backward = None if args.no_backward else bench_backward(la, torch, workloads, hip, tensors)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
@@ -423,6 +451,7 @@ def main():
         "decode": decode,
         "varlen": varlen,
         "layer": layer,
+        "backward": backward,
     }
     print(json.dumps(line), flush=True)
 

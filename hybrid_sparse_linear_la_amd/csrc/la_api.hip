@@ -464,11 +464,11 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
 }
 
 // Workspace of la_backward: forward and gradient segment states, the final
-// forward state (unused), fp32 gradients of the rotated q and k, and the parts of
+// forward state (unused), bf16 gradients of the rotated q and k, and the parts of
 // the norm-weight gradients.
 static bool backward_layout(int B, int T, int H, const PrefillPlan& plan, size_t off[6]) {
   const size_t st = (size_t)B * H * kHeadDim * kHeadDim * sizeof(float);
-  const size_t rows = (size_t)B * T * H * kHeadDim * sizeof(float);
+  const size_t rows = (size_t)B * T * H * kHeadDim * sizeof(la_bf16);
   off[0] = 0;                                   // forward segment states
   off[1] = round_up(off[0] + plan.ws_bytes, 256);  // gradient segment states
   off[2] = round_up(off[1] + plan.ws_bytes, 256);  // final forward state
@@ -552,8 +552,8 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
   bp.dk = dk;
   bp.dv = dv;
   bp.dg = dgate;
-  bp.dqh = reinterpret_cast<float*>(ws + off[3]);
-  bp.dkh = reinterpret_cast<float*>(ws + off[4]);
+  bp.dqh = reinterpret_cast<la_bf16*>(ws + off[3]);
+  bp.dkh = reinterpret_cast<la_bf16*>(ws + off[4]);
   bp.dq_w = dq_norm_w;
   bp.dk_w = dk_norm_w;
   bp.wpart = reinterpret_cast<float*>(ws + off[5]);

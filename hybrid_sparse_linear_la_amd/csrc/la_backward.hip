@@ -23,7 +23,7 @@
 // the segment's first token, from the suffix scan) and subtracts Qh^T dU from G
 // chunk by chunk.  Wave w owns columns [16w, 16w + 16) of every output and of the
 // S, G accumulators; S and G are also written to LDS as bf16 (transposed) so the
-// S^T and G^T products can read any row.  dqh, dkh leave in fp32 for
+// S^T and G^T products can read any row.  dqh, dkh leave in bf16 for
 // la_prologue_backward_kernel, which rotates them back and applies the RMSNorm
 // Jacobian.  Chunks at the start and end of a sequence form their scores from a
 // hi/lo split of qh, kh and du: rows there sum few scores, and the bf16 rounding
@@ -66,8 +66,8 @@ __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ void store_f32x4(float* dst, f32x4 x) {
-  *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 x) {
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
 }
 
 template <bool kWeights>
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
           acc = mma(col_operand(sST, kk, 16 * w, g4, n16), pi_operand(sU, t, kk, g4), acc);
 #pragma unroll
         for (int kk = 0; kk <= rt / 2; ++kk) acc = mma(Kf[kk], score_row_operand(sdP, t, kk, g4), acc);
-        if (ok) store_f32x4(bp.dqh + row, acc);
+        if (ok) store_bf16x4(bp.dqh + row, acc);
         // dV = Kh G + (P^T dU)   (row t is the key token s here)
         acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
           acc = mma(col_operand(sGT, kk, 16 * w, g4, n16), pi_operand(sV, t, kk, g4), acc);
 #pragma unroll
         for (int kk = rt / 2; kk < 2; ++kk) acc = mma(Qf[kk], score_col_operand(sdP, kk, 16 * rt, g4, n16), acc);
-        if (ok) store_f32x4(bp.dkh + row, acc);
+        if (ok) store_bf16x4(bp.dkh + row, acc);
       }
       // S before the next chunk: S += Kh^T V
       accumulate_state(Sacc, sK, Vf, g4, n16);
@@ -265,54 +265,104 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   }
 }
 
-// dx from d(rope(rmsnorm(x))) for one tensor: one wave per row, lane i holds the
-// RoPE pair (i, i + 64).  Rotating back by the same angle gives dn; then
+// dq, dk from the gradients of the rotated, normalized rows (dqh, dkh): rotating
+// back by the same angle gives dn, then through RMSNorm (n = w x / r):
 //     dx_i = w_i dn_i / r - x_i (sum_j w_j x_j dn_j) / (D r^3),   dw_i += dn_i x_i / r.
-// Each workgroup also leaves its part of dw in wpart[blockIdx].
-template <bool kWeights>
-__global__ __launch_bounds__(256) void la_prologue_backward_kernel(BackwardParams bp, int which) {
-  const PrefillParams& p = bp.f;
-  const uint16_t* const x = which ? p.k : p.q;
-  const float* const dy = which ? bp.dkh : bp.dqh;
-  uint16_t* const dx = which ? bp.dk : bp.dq;
-  const float* const wgt = which ? p.kw : p.qw;
-  __shared__ float sw[4][kD];
+// A workgroup of 512 threads takes 64-token chunks of one head in turn, staged like
+// the forward: thread (rg, j) holds rows rg and rg + 32 and dims 4j..4j+3 with
+// their RoPE partners 64+4j..; the rotations come from the chunk's base rotation.
+// Each workgroup leaves its part of dw in wpart[which][blockIdx].
+constexpr int kProThreads = 512;
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const bool has_w = kWeights && wgt != nullptr;
-  const float w0 = has_w ? wgt[lane] : 1.0f, w1 = has_w ? wgt[lane + kHalf] : 1.0f;
-  const double rev = p.freqs.rev[lane];
-  float acc0 = 0.f, acc1 = 0.f;
-  const int64_t rows = (int64_t)p.B * p.T * p.H;
-  for (int64_t r = (int64_t)blockIdx.x * 4 + wv; r < rows; r += (int64_t)gridDim.x * 4) {
-    const int64_t t = (r / p.H) % p.T;
-    const float x0 = bf2f(x[r * kD + lane]), x1 = bf2f(x[r * kD + lane + kHalf]);
-    const float d0 = dy[r * kD + lane], d1 = dy[r * kD + lane + kHalf];
-    float ss = x0 * x0 + x1 * x1;
+template <bool kWeights>
+__global__ __launch_bounds__(kProThreads) void la_prologue_backward_kernel(BackwardParams bp) {
+  const PrefillParams& p = bp.f;
+  __shared__ float2 sRot[kHalf];
+  __shared__ float sW[2][32][kD / 8][8];  // weight-gradient parts of each row group, per tensor
+
+  const int tid = threadIdx.x, j = tid & 15, rg = tid >> 4;
+  const int64_t rs = (int64_t)p.H * kD;
+  float w[2][8];
+  load_norm_weights(p.qw, j, w[0]);
+  load_norm_weights(p.kw, j, w[1]);
+  Rope L;
+  rope_init<32>(p, tid, rg, j, L);
+  float dw[2][8];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-    const float inv = rsqrt_(ss * (1.0f / kD) + p.eps);
-    const float2 rot = rope_rotation(p.pos0 + t, rev);
-    const float n0 = d0 * rot.x + d1 * rot.y;
-    const float n1 = d1 * rot.x - d0 * rot.y;
-    float dot = w0 * x0 * n0 + w1 * x1 * n1;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) dot += __shfl_xor(dot, o);
-    const float k3 = dot * inv * inv * inv * (1.0f / kD);
-    dx[r * kD + lane] = f2bf(w0 * n0 * inv - x0 * k3);
-    dx[r * kD + lane + kHalf] = f2bf(w1 * n1 * inv - x1 * k3);
-    if (kWeights) {
-      acc0 += n0 * x0 * inv;
-      acc1 += n1 * x1 * inv;
+    for (int e = 0; e < 8; ++e) dw[a][e] = 0.f;
+
+  const int nch = (p.T + kC - 1) / kC;
+  const int64_t items = (int64_t)p.B * p.H * nch;
+  for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+    const int c = (int)(item % nch);
+    const int64_t bh = item / nch;
+    const int64_t base = ((bh / p.H) * p.T * p.H + bh % p.H) * kD;
+    const int t0 = c * kC, nv = min(kC, p.T - t0);
+    if (tid < kHalf) sRot[tid] = rope_rotation(p.pos0 + t0, L.base_rev);
+    Rows<2> X[2], Y[2];
+    load_rows<2, 32>(p.q + base + (int64_t)t0 * rs, rs, nv, rg, j, X[0]);
+    load_rows<2, 32>(p.k + base + (int64_t)t0 * rs, rs, nv, rg, j, X[1]);
+    load_rows<2, 32>(bp.dqh + base + (int64_t)t0 * rs, rs, nv, rg, j, Y[0]);
+    load_rows<2, 32>(bp.dkh + base + (int64_t)t0 * rs, rs, nv, rg, j, Y[1]);
+    __syncthreads();
+    float2 E[4];
+    first_rotation<32>(sRot, L, j, E);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (m > 0) next_rotation(L, E);
+      const int t = rg + 32 * m;
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const uint2 xl = X[a].lo[m], xh = X[a].hi[m], yl = Y[a].lo[m], yh = Y[a].hi[m];
+        const float x[8] = {bf2f_lo(xl.x), bf2f_hi(xl.x), bf2f_lo(xl.y), bf2f_hi(xl.y),
+                            bf2f_lo(xh.x), bf2f_hi(xh.x), bf2f_lo(xh.y), bf2f_hi(xh.y)};
+        const float y[8] = {bf2f_lo(yl.x), bf2f_hi(yl.x), bf2f_lo(yl.y), bf2f_hi(yl.y),
+                            bf2f_lo(yh.x), bf2f_hi(yh.x), bf2f_lo(yh.y), bf2f_hi(yh.y)};
+        float dn[8], ss = 0.f, dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dn[e] = y[e] * E[e].x + y[4 + e] * E[e].y;
+          dn[4 + e] = y[4 + e] * E[e].x - y[e] * E[e].y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ss += x[e] * x[e];
+          dot += w[a][e] * x[e] * dn[e];
+        }
+        ss = row16_sum(ss);
+        dot = row16_sum(dot);
+        const float inv = rsqrt_(ss * (1.0f / kD) + p.eps);
+        const float k3 = dot * inv * inv * inv * (1.0f / kD);
+        float dx[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          dx[e] = w[a][e] * dn[e] * inv - x[e] * k3;
+          if (kWeights && t < nv) dw[a][e] += dn[e] * x[e] * inv;
+        }
+        if (t < nv) {
+          uint16_t* dst = (a ? bp.dk : bp.dq) + base + (int64_t)(t0 + t) * rs;
+          *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(pack2(dx[0], dx[1]), pack2(dx[2], dx[3]));
+          *reinterpret_cast<uint2*>(dst + kHalf + 4 * j) = make_uint2(pack2(dx[4], dx[5]), pack2(dx[6], dx[7]));
+        }
+      }
     }
+    __syncthreads();  // sRot is rewritten for the next chunk
   }
   if (kWeights) {
-    sw[wv][lane] = acc0;
-    sw[wv][lane + kHalf] = acc1;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sW[a][rg][j][e] = dw[a][e];
     __syncthreads();
-    if (threadIdx.x < kD) {
-      const int i = threadIdx.x;
-      bp.wpart[((int64_t)which * kPrologueBlocks + blockIdx.x) * kD + i] = sw[0][i] + sw[1][i] + sw[2][i] + sw[3][i];
+    if (tid < 2 * kD) {
+      const int a = tid / kD, i = tid % kD;
+      // dim i is held by thread j = (i % 64) / 4 as element e = i % 4 (+ 4 for the upper half)
+      const int jj = (i % kHalf) / 4, e = (i % 4) + (i >= kHalf ? 4 : 0);
+      float s = 0.f;
+      for (int r = 0; r < 32; ++r) s += sW[a][r][jj][e];
+      bp.wpart[((int64_t)a * kPrologueBlocks + blockIdx.x) * kD + i] = s;
     }
   }
 }
@@ -338,14 +388,12 @@ hipError_t launch_backward_chunks(const BackwardParams& bp, const PrefillPlan& p
     hipLaunchKernelGGL(la_backward_chunk_kernel<true>, grid, dim3(kBwdThreads), 0, stream, bp);
   else
     hipLaunchKernelGGL(la_backward_chunk_kernel<false>, grid, dim3(kBwdThreads), 0, stream, bp);
-  const int64_t rows = (int64_t)p.B * p.T * p.H;
-  const int nblocks = (int)std::min<int64_t>(kPrologueBlocks, (rows + 3) / 4);
-  for (int which = 0; which < 2; ++which) {
-    if (weights)
-      hipLaunchKernelGGL(la_prologue_backward_kernel<true>, dim3(nblocks), dim3(256), 0, stream, bp, which);
-    else
-      hipLaunchKernelGGL(la_prologue_backward_kernel<false>, dim3(nblocks), dim3(256), 0, stream, bp, which);
-  }
+  const int64_t items = (int64_t)p.B * p.H * ((p.T + kC - 1) / kC);
+  const int nblocks = (int)std::min<int64_t>(kPrologueBlocks, items);
+  if (weights)
+    hipLaunchKernelGGL(la_prologue_backward_kernel<true>, dim3(nblocks), dim3(kProThreads), 0, stream, bp);
+  else
+    hipLaunchKernelGGL(la_prologue_backward_kernel<false>, dim3(nblocks), dim3(kProThreads), 0, stream, bp);
   if (weights) hipLaunchKernelGGL(la_weight_grad_kernel, dim3(1), dim3(256), 0, stream, bp, nblocks);
   return hipGetLastError();
 }

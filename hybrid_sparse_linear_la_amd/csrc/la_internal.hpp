@@ -119,13 +119,13 @@ struct BackwardParams {
   uint16_t* dk;
   uint16_t* dv;
   uint16_t* dg;
-  float* dqh;       // [B][T][H][D] fp32 scratch: gradients of the rotated, normalized q and k
-  float* dkh;
+  uint16_t* dqh;    // [B][T][H][D] bf16 scratch: gradients of the rotated, normalized q and k
+  uint16_t* dkh;
   float* dq_w;      // [D] or nullptr (norm-weight gradients)
   float* dk_w;
   float* wpart;     // [2][kPrologueBlocks][D] fp32 scratch for the weight gradients
 };
-constexpr int kPrologueBlocks = 1024;
+constexpr int kPrologueBlocks = 2048;
 
 // The forward segment states of la_prefill into f.ws (f.S_out receives the final
 // state), then the gradient segment states into wsg and dS_in.

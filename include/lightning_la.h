@@ -192,8 +192,8 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
 
 /*
  * Bytes of workspace la_backward needs (0 for an invalid shape or a chunk other
- * than 0 / 64): two sets of segment states, fp32 gradients of the rotated q and
- * k ([B, T, H, D] each) and 1 MiB for the norm-weight gradient parts.
+ * than 0 / 64): two sets of segment states, bf16 gradients of the rotated q and
+ * k ([B, T, H, D] each) and 2 MiB for the norm-weight gradient parts.
  */
 size_t la_backward_workspace_bytes(int B, int T, int H, int D, int chunk);
 

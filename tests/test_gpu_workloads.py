@@ -10,7 +10,8 @@ benchmark times (default chunk, B = 1, 32 heads x 128):
   * batched decode (64 sequences x 32 heads, 1000 steps from position 262144):
     o at every step and S after steps 1, 10 and 1000 against the oracle;
   * a packed serving batch (4 prompts of 16384 tokens and 60 decode steps) in one
-    variable-length call: every decode row and sampled prompt heads.
+    variable-length call: every decode row and sampled prompt heads;
+  * the backward of the 32K-token prefill: every gradient row against the oracle.
 """
 import numpy as np
 import pytest
@@ -154,3 +155,22 @@ def test_serving_mix_varlen(la):
             eo = assert_o_close(to_np(o[t0:t1, h:h + 1][None]), o_ref, what=f"prompt {b} head {h}")
             assert_S_close(to_np(S_out[b:b + 1, h:h + 1]), S_ref, what=f"prompt {b} head {h} state")
             print(f"serving mix prompt {b} head {h}: o {eo}", flush=True)
+
+
+def test_backward_32k_all_heads(la):
+    """Gradients of the 32K-token prefill (32 heads x 128) for a seeded output
+    gradient and final-state gradient: every row of dq, dk, dv, dgate and every
+    dS_in against the oracle's reverse mode."""
+    w = workloads.PREFILL_32K
+    print(f"workload {w.name} backward", flush=True)
+    gen = workloads.generator(w.seed, "cuda")
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, w.D, w.seed, "cuda", gen=gen)
+    d_o = torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16)
+    dS_out = workloads.state(w.B, w.H, w.D, 0.02, gen, "cuda")
+    grads = la.backward(q, k, v, g, d_o, dS_out=dS_out)
+    torch.cuda.synchronize()
+    ref = oracle.backward(to_np32(q), to_np32(k), to_np32(v), to_np32(g), to_np32(d_o), dS_out=to_np(dS_out))
+    for name, key in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dgate", "dg")):
+        e = assert_o_close(to_np(grads[name]), ref[key], what=f"32K {name}")
+        print(f"32K backward {name}: {e}", flush=True)
+    assert_S_close(to_np(grads["dS_in"]), ref["dS_in"], what="32K dS_in")
