@@ -70,6 +70,15 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 x) {
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
 }
 
+// Stores row blocks rt = 0..3 (row 16 rt + n16 of the chunk, columns col..col+3) of
+// a bf16 output, rows at or past nv skipped.
+__device__ __forceinline__ void store_rows4(uint16_t* out, const f32x4 (&acc)[4], int64_t base, int t0,
+                                            int64_t rs, int col, int nv, int n16) {
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+    if (16 * rt + n16 < nv) store_bf16x4(out + base + (int64_t)(t0 + 16 * rt + n16) * rs + col, acc[rt]);
+}
+
 template <bool kWeights>
 __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(BackwardParams bp) {
   const PrefillParams& p = bp.f;
@@ -94,9 +103,6 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   const Tile tl = decode_tile(p);
   const int64_t rs = (int64_t)p.H * kD;
 
-  float wq[8], wk[8];
-  load_norm_weights(p.qw, j, wq);
-  load_norm_weights(p.kw, j, wk);
   Rope L;
   rope_init<32>(p, tid, rg, j, L);
   double rev[4];
@@ -138,6 +144,12 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
       float2 E2[4] = {E[0], E[1], E[2], E[3]};
+      // norm weights are re-read each chunk (from cache) rather than held in registers
+      float wq[8], wk[8];
+      if (kWeights) {
+        load_norm_weights(p.qw, j, wq);
+        load_norm_weights(p.kw, j, wk);
+      }
       norm_rope_rows<kWeights, 2, 32, kC>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
       norm_rope_rows<kWeights, 2, 32, kC>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
       store_rows_masked<2, 32>(sV, Vr, nv, rg, j);
@@ -193,72 +205,103 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       lds_st<uint2>(sGT, off, make_uint2(pack2(Gacc[rtk][0], Gacc[rtk][1]), pack2(Gacc[rtk][2], Gacc[rtk][3])));
     }
     __syncthreads();
-    // ---- outputs of this wave's 16 columns, row block by row block
+    // ---- outputs of this wave's 16 columns.  Each output is formed for the four row
+    // blocks at once: every A operand (S, G, S^T, G^T, or a column of V, Kh, dU, Qh)
+    // is read once and feeds four independent accumulation chains.
     {
-      bf16x8 SA[4], GA[4];  // S, G as A operands (key dims in order pi)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        SA[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
-        GA[kk] = pack8(Gacc[2 * kk], Gacc[2 * kk + 1]);
-      }
-      bf16x8 Vf[2], Uf[2], Kf[2], Qf[2];  // columns 16w + n16 of V, dU, Kh, Qh in token order pi
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        Vf[kk] = col_operand(sV, kk, 16 * w, g4, n16);
-        Uf[kk] = col_operand(sU, kk, 16 * w, g4, n16);
-        Kf[kk] = col_operand(sK, kk, 16 * w, g4, n16);
-        Qf[kk] = col_operand(sQ, kk, 16 * w, g4, n16);
-      }
       const int col = 16 * w + 4 * g4;
+      // do and g of the lane's output rows (rows past the chunk clamped to its last row)
+      uint2 dor[4], gr[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int t = 16 * rt + n16;            // row of this lane in the chunk
-        const int64_t row = tl.base + (int64_t)(t0 + t) * rs + col;
-        const bool ok = t < nv;
-        // u = Qh S + (P V)  ->  dg
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mma(SA[kk], pi_operand(sQ, t, kk, g4), acc);
-#pragma unroll
-        for (int kk = 0; kk <= rt / 2; ++kk) acc = mma(Vf[kk], score_row_operand(sP, t, kk, g4), acc);
-        if (ok) {
-          const uint2 dor = *reinterpret_cast<const uint2*>(p.dout + row);
-          const uint2 gr = *reinterpret_cast<const uint2*>(p.g + row);
-          const float d[4] = {bf2f_lo(dor.x), bf2f_hi(dor.x), bf2f_lo(dor.y), bf2f_hi(dor.y)};
-          const float gg[4] = {bf2f_lo(gr.x), bf2f_hi(gr.x), bf2f_lo(gr.y), bf2f_hi(gr.y)};
-          float dg[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sg = sigmoidf_(gg[r]);
-            dg[r] = d[r] * acc[r] * sg * (1.0f - sg);
-          }
-          *reinterpret_cast<uint2*>(bp.dg + row) = make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
-        }
-        // dQh = dU S^T + (dP Kh)
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = mma(col_operand(sST, kk, 16 * w, g4, n16), pi_operand(sU, t, kk, g4), acc);
-#pragma unroll
-        for (int kk = 0; kk <= rt / 2; ++kk) acc = mma(Kf[kk], score_row_operand(sdP, t, kk, g4), acc);
-        if (ok) store_bf16x4(bp.dqh + row, acc);
-        // dV = Kh G + (P^T dU)   (row t is the key token s here)
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mma(GA[kk], pi_operand(sK, t, kk, g4), acc);
-#pragma unroll
-        for (int kk = rt / 2; kk < 2; ++kk) acc = mma(Uf[kk], score_col_operand(sP, kk, 16 * rt, g4, n16), acc);
-        if (ok) *reinterpret_cast<uint2*>(bp.dv + row) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
-        // dKh = V G^T + (dP^T Qh)
-        acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = mma(col_operand(sGT, kk, 16 * w, g4, n16), pi_operand(sV, t, kk, g4), acc);
-#pragma unroll
-        for (int kk = rt / 2; kk < 2; ++kk) acc = mma(Qf[kk], score_col_operand(sdP, kk, 16 * rt, g4, n16), acc);
-        if (ok) store_bf16x4(bp.dkh + row, acc);
+        const int64_t crow = tl.base + (int64_t)(t0 + min(16 * rt + n16, nv - 1)) * rs + col;
+        dor[rt] = *reinterpret_cast<const uint2*>(p.dout + crow);
+        gr[rt] = *reinterpret_cast<const uint2*>(p.g + crow);
       }
+      f32x4 acc[4];
+      // u = Qh S + (P V)  ->  dg = do * u * sigmoid'(g)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sQ, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = col_operand(sV, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row_operand(sP, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float d[4] = {bf2f_lo(dor[rt].x), bf2f_hi(dor[rt].x), bf2f_lo(dor[rt].y), bf2f_hi(dor[rt].y)};
+        const float gg[4] = {bf2f_lo(gr[rt].x), bf2f_hi(gr[rt].x), bf2f_lo(gr[rt].y), bf2f_hi(gr[rt].y)};
+        float dg[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float sg = sigmoidf_(gg[r]);
+          dg[r] = d[r] * acc[rt][r] * sg * (1.0f - sg);
+        }
+        if (16 * rt + n16 < nv)
+          *reinterpret_cast<uint2*>(bp.dg + tl.base + (int64_t)(t0 + 16 * rt + n16) * rs + col) =
+              make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
+      }
+      // dQh = dU S^T + (dP Kh)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = col_operand(sST, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sU, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = col_operand(sK, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row_operand(sdP, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+      store_rows4(bp.dqh, acc, tl.base, t0, rs, col, nv, n16);
+      // dV = Kh G + (P^T dU)   (the row is the key token s here)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = pack8(Gacc[2 * kk], Gacc[2 * kk + 1]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sK, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = col_operand(sU, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 0; rt < 2 * kk + 2; ++rt)
+          acc[rt] = mma(a, score_col_operand(sP, kk, 16 * rt, g4, n16), acc[rt]);
+      }
+      store_rows4(bp.dv, acc, tl.base, t0, rs, col, nv, n16);
+      // dKh = V G^T + (dP^T Qh)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = col_operand(sGT, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sV, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = col_operand(sQ, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 0; rt < 2 * kk + 2; ++rt)
+          acc[rt] = mma(a, score_col_operand(sdP, kk, 16 * rt, g4, n16), acc[rt]);
+      }
+      store_rows4(bp.dkh, acc, tl.base, t0, rs, col, nv, n16);
       // S before the next chunk: S += Kh^T V
+      bf16x8 Vf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_operand(sV, kk, 16 * w, g4, n16);
       accumulate_state(Sacc, sK, Vf, g4, n16);
     }
     __syncthreads();
