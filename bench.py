@@ -40,7 +40,7 @@ TOKEN_HEAD_BYTES = 1280         # read q, k, v, gate (4 x 256 B) + write o (256 
 STATE_BYTES = 128 * 128 * 4     # one fp32 D x D state
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_output_kernel.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "hybrid_sparse_linear_la_amd", "csrc", f)
-                  for f in ("la_prefill.hip", "la_device.hpp")]
+                  for f in ("la_prefill.hip", "la_tiles.hpp", "la_device.hpp", "la_internal.hpp")]
 
 
 class HipEvents:
