@@ -38,23 +38,55 @@ namespace {
 constexpr int kBwdThreads = 512;
 constexpr int kSnapBytes = kD * kRowBytes;  // [128][128] bf16, 272-byte rows
 
-// Column operand of a [rows][128] tile in token order pi, rows 32 kk ..: lane n16
-// gets X[32kk + 4g + 16(e/4) + e%4][c0 + n16] (the transposed read of v_operand).
-__device__ __forceinline__ bf16x8 col_operand(const uint8_t* tile, int kk, int c0, int g4, int n16) {
-  return v_operand(tile, kk, c0, g4, n16);
+// The chunk's q, k, v and du tiles use the TilePi layout (288-byte rows, key
+// dims stored in order pi); the S^T, G^T snapshots and the score tiles are
+// row-major with natural columns.
+constexpr int kPiTileBytes = kC * TilePi::kRow;
+
+// Column operand of a snapshot ([128][128], 272-byte rows) in order pi over its
+// rows: lane n16 gets X[32kk + 4g + 16(e/4) + e%4][c0 + n16].
+__device__ __forceinline__ bf16x8 snap_col(const uint8_t* snap, int kk, int c0, int g4, int n16) {
+  return v_operand(snap, kk, c0, g4, n16);
 }
 
-// Score column operand: lane n16 gets P[32kk + 4g + 16(e/4) + e%4][s0 + n16] from a
-// [64][64] score tile.
-__device__ __forceinline__ bf16x8 score_col_operand(const uint8_t* sP, int kk, int s0, int g4, int n16) {
-  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
-  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 16, c)));
+// Row operand in key order pi from a TilePi tile: lane (g, n16) gets dims
+// pi(8g + e) of row t, which are 16 contiguous bytes.
+__device__ __forceinline__ bf16x8 pi_row(const uint8_t* tile, int t, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint4>(tile, t * TilePi::kRow + 2 * (32 * kk + 8 * g4)));
 }
 
-// Score row operand: lane n16 gets P[t][32kk + 4g + 16(e/4) + e%4].
-__device__ __forceinline__ bf16x8 score_row_operand(const uint8_t* sP, int t, int kk, int g4) {
-  return as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
-                   lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
+// Column operand of a TilePi tile with tokens in natural order: lane n16 gets
+// X[32kk + 8g + e][c0 + n16] (two transposed reads of 4 rows each).
+__device__ __forceinline__ bf16x8 col_nat(const uint8_t* tile, int kk, int c0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(tile, TilePi::off(t0, c)), lds_tr(tile, TilePi::off(t0 + 4, c)));
+}
+
+// Score column operand, tokens in natural order: lane n16 gets P[32kk + 8g + e][s0 + n16].
+__device__ __forceinline__ bf16x8 score_col(const uint8_t* sP, int kk, int s0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 4, c)));
+}
+
+// Score row operand, tokens in natural order: lane n16 gets P[t][32kk + 8g + e].
+__device__ __forceinline__ bf16x8 score_row(const uint8_t* sP, int t, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint4>(sP, score_off(t, 32 * kk + 8 * g4)));
+}
+
+// X[:, 16w .. 16w+16) += A^T B over one chunk, A a TilePi tile (its 128 columns
+// are the accumulator rows), B the chunk's column operand (col_nat, 16 columns).
+__device__ __forceinline__ void accumulate_nat(f32x4 (&acc)[8], const uint8_t* A, const bf16x8 (&Bop)[2],
+                                               int g4, int n16) {
+#pragma unroll
+  for (int kk = 0; kk < kC / 32; ++kk) {
+    const int t0 = 32 * kk + 8 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk) {
+      const int c = 16 * rtk + 4 * (n16 & 3);
+      const bf16x8 a = as_bf16x8(lds_tr(A, TilePi::off(t0, c)), lds_tr(A, TilePi::off(t0 + 4, c)));
+      acc[rtk] = mma(a, Bop[kk], acc[rtk]);
+    }
+  }
 }
 
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
@@ -82,10 +114,10 @@ __device__ __forceinline__ void store_rows4(uint16_t* out, const f32x4 (&acc)[4]
 template <bool kWeights>
 __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(BackwardParams bp) {
   const PrefillParams& p = bp.f;
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sK[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sU[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[kPiTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[kPiTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[kPiTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sU[kPiTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sdP[kC * kScoreRowBytes];
   // S^T and G^T snapshots; during the scores of an exact chunk the lo tiles of qh,
@@ -94,8 +126,9 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   uint8_t* const sST = sX;
   uint8_t* const sGT = sX + kSnapBytes;
   uint8_t* const sQl = sX;
-  uint8_t* const sKl = sX + kTileBytes;
-  uint8_t* const sUl = sX + 2 * kTileBytes;
+  uint8_t* const sKl = sX + kPiTileBytes;
+  uint8_t* const sUl = sX + 2 * kPiTileBytes;
+  static_assert(3 * kPiTileBytes <= 2 * kSnapBytes, "lo tiles must fit the snapshot area");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -150,10 +183,10 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
         load_norm_weights(p.qw, j, wq);
         load_norm_weights(p.kw, j, wk);
       }
-      norm_rope_rows<kWeights, 2, 32, kC>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
-      norm_rope_rows<kWeights, 2, 32, kC>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
-      store_rows_masked<2, 32>(sV, Vr, nv, rg, j);
-      du_stage<2, 32>(sU, exact ? sUl : nullptr, Dr, Gr, nv, rg, j);
+      norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
+      norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
+      store_rows_masked<2, 32, TilePi>(sV, Vr, nv, rg, j);
+      du_stage<2, 32, TilePi>(sU, exact ? sUl : nullptr, Dr, Gr, nv, rg, j);
     }
     __syncthreads();
     // ---- scores P = Qh Kh^T and dP = dU V^T (masked to s <= t), 20 tiles over 8 waves
@@ -164,8 +197,10 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kD / 32; ++ks) {
-        const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
-        const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
+        // any order of the 128 dims serves the dot products: both operands read the
+        // same 16 stored bytes
+        const int ka = (16 * st + n16) * TilePi::kRow + 2 * (32 * ks + 8 * g4);
+        const int qa = (16 * rt + n16) * TilePi::kRow + 2 * (32 * ks + 8 * g4);
         if (!grad) {
           const bf16x8 kf = as_bf16x8(lds_ld<uint4>(sK, ka));
           const bf16x8 qf = as_bf16x8(lds_ld<uint4>(sQ, qa));
@@ -193,8 +228,8 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     {
       bf16x8 nU[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_operand(sU, kk, 16 * w, g4, n16));
-      accumulate_state(Gacc, sQ, nU, g4, n16);
+      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_nat(sU, kk, 16 * w, g4, n16));
+      accumulate_nat(Gacc, sQ, nU, g4, n16);
     }
     __syncthreads();
     // ---- snapshots S^T[j][i] (S before the chunk) and G^T[j][i] (G after it), bf16
@@ -226,13 +261,13 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 a = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sQ, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sQ, 16 * rt + n16, kk, g4), acc[rt]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_operand(sV, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat(sV, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row_operand(sP, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sP, 16 * rt + n16, kk, g4), acc[rt]);
       }
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -253,15 +288,15 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = col_operand(sST, kk, 16 * w, g4, n16);
+        const bf16x8 a = snap_col(sST, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sU, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sU, 16 * rt + n16, kk, g4), acc[rt]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_operand(sK, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat(sK, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row_operand(sdP, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sdP, 16 * rt + n16, kk, g4), acc[rt]);
       }
       store_rows4(bp.dqh, acc, tl.base, t0, rs, col, nv, n16);
       // dV = Kh G + (P^T dU)   (the row is the key token s here)
@@ -271,14 +306,13 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       for (int kk = 0; kk < 4; ++kk) {
         const bf16x8 a = pack8(Gacc[2 * kk], Gacc[2 * kk + 1]);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sK, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sK, 16 * rt + n16, kk, g4), acc[rt]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_operand(sU, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat(sU, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 2 * kk + 2; ++rt)
-          acc[rt] = mma(a, score_col_operand(sP, kk, 16 * rt, g4, n16), acc[rt]);
+        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sP, kk, 16 * rt, g4, n16), acc[rt]);
       }
       store_rows4(bp.dv, acc, tl.base, t0, rs, col, nv, n16);
       // dKh = V G^T + (dP^T Qh)
@@ -286,23 +320,22 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = col_operand(sGT, kk, 16 * w, g4, n16);
+        const bf16x8 a = snap_col(sGT, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_operand(sV, 16 * rt + n16, kk, g4), acc[rt]);
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sV, 16 * rt + n16, kk, g4), acc[rt]);
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_operand(sQ, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat(sQ, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 2 * kk + 2; ++rt)
-          acc[rt] = mma(a, score_col_operand(sdP, kk, 16 * rt, g4, n16), acc[rt]);
+        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sdP, kk, 16 * rt, g4, n16), acc[rt]);
       }
       store_rows4(bp.dkh, acc, tl.base, t0, rs, col, nv, n16);
       // S before the next chunk: S += Kh^T V
       bf16x8 Vf[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_operand(sV, kk, 16 * w, g4, n16);
-      accumulate_state(Sacc, sK, Vf, g4, n16);
+      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat(sV, kk, 16 * w, g4, n16);
+      accumulate_nat(Sacc, sK, Vf, g4, n16);
     }
     __syncthreads();
   }

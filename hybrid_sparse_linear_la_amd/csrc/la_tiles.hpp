@@ -30,6 +30,24 @@ typedef short bf16x4 __attribute__((ext_vector_type(4)));
 // spread over the banks, and every offset is linear (immediate offsets).
 __device__ __forceinline__ int tile_off(int t, int d) { return t * kRowBytes + 2 * d; }
 
+// Row-tile layouts for the staging helpers.  TileNat is the tile above.  TilePi
+// has 288-byte rows and stores each 32-dim block in the key order pi: dim
+// 32kk + 16h + 4g + r sits at position 32kk + 8g + 4h + r, so the 8 dims a lane
+// takes in order pi are 16 contiguous bytes (one ds_read_b128, which is
+// conflict-free at this row stride), while any 4 consecutive dims starting at a
+// multiple of 4 stay contiguous (8-byte stores and transposed reads).
+struct TileNat {
+  static constexpr int kRow = kRowBytes;
+  __device__ static __forceinline__ int off(int t, int d) { return tile_off(t, d); }
+};
+struct TilePi {
+  static constexpr int kRow = kD * 2 + 32;
+  __device__ static __forceinline__ int pos(int d) {
+    return (d & ~31) | ((d & 12) << 1) | ((d & 16) >> 2) | (d & 3);
+  }
+  __device__ static __forceinline__ int off(int t, int d) { return t * kRow + 2 * pos(d); }
+};
+
 // Transposed read: within each 16-lane group, lane L supplies the address of 4
 // bf16 and receives element L of each of the 4 rows formed by lanes 4r..4r+3.
 // Reading rows t0 + L / 4, columns c0 + 4 (L % 4) of a row tile gives lane L the
@@ -72,14 +90,14 @@ __device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, int
   }
 }
 
-template <int M, int kStep>
+template <int M, int kStep, class Lay = TileNat>
 __device__ __forceinline__ void store_rows_masked(uint8_t* tile, const Rows<M>& R, int nvalid, int rg,
                                                   int j) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const bool ok = rg + kStep * m < nvalid;
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), ok ? R.lo[m] : make_uint2(0u, 0u));
-    lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), ok ? R.hi[m] : make_uint2(0u, 0u));
+    lds_st<uint2>(tile, Lay::off(rg + kStep * m, 4 * j), ok ? R.lo[m] : make_uint2(0u, 0u));
+    lds_st<uint2>(tile, Lay::off(rg + kStep * m, kHalf + 4 * j), ok ? R.hi[m] : make_uint2(0u, 0u));
   }
 }
 
@@ -101,7 +119,7 @@ __device__ __forceinline__ void sigmoid_stage(uint8_t* tile, const Rows<M>& R, i
 
 // du = do * sigmoid(g) of rows rg + kStep m as bf16 into `tile` (rows at or past
 // nvalid zeroed); with `lo`, also lo = bf16(du - bf16(du)) for exact chunks.
-template <int M, int kStep>
+template <int M, int kStep, class Lay = TileNat>
 __device__ __forceinline__ void du_stage(uint8_t* tile, uint8_t* lo, const Rows<M>& D, const Rows<M>& G,
                                          int nvalid, int rg, int j) {
 #pragma unroll
@@ -115,7 +133,7 @@ __device__ __forceinline__ void du_stage(uint8_t* tile, uint8_t* lo, const Rows<
       const float u[4] = {bf2f_lo(d.x) * sigmoidf_(bf2f_lo(g.x)), bf2f_hi(d.x) * sigmoidf_(bf2f_hi(g.x)),
                           bf2f_lo(d.y) * sigmoidf_(bf2f_lo(g.y)), bf2f_hi(d.y) * sigmoidf_(bf2f_hi(g.y))};
       const uint2 hiw = ok ? make_uint2(pack2(u[0], u[1]), pack2(u[2], u[3])) : make_uint2(0u, 0u);
-      const int off = tile_off(t, half * kHalf + 4 * j);
+      const int off = Lay::off(t, half * kHalf + 4 * j);
       lds_st<uint2>(tile, off, hiw);
       if (lo != nullptr) {
         const uint2 low = ok ? make_uint2(pack2(u[0] - bf2f_lo(hiw.x), u[1] - bf2f_hi(hiw.x)),
@@ -152,7 +170,7 @@ __device__ __forceinline__ void rope_init(const PrefillParams& p, int tid, int r
 // rotate-half RoPE with rotations E, in fp32; the bf16 result goes to `tile`.
 // With `lo` set, rows below kExactRows also store lo = bf16(y - bf16(y)) into
 // `lo`, for the scores of the first rows of a call.
-template <bool kWeights, int kLoRows = kExactRows>
+template <bool kWeights, int kLoRows = kExactRows, class Lay = TileNat>
 __device__ __forceinline__ void norm_rope_row(uint2 rl, uint2 rh, const float (&w)[8], float eps,
                                               const float2 (&E)[4], int t, int j, uint8_t* tile,
                                               uint8_t* lo) {
@@ -171,15 +189,15 @@ __device__ __forceinline__ void norm_rope_row(uint2 rl, uint2 rh, const float (&
   }
   const uint2 hlo = make_uint2(pack2(y[0], y[1]), pack2(y[2], y[3]));
   const uint2 hhi = make_uint2(pack2(y[4], y[5]), pack2(y[6], y[7]));
-  lds_st<uint2>(tile, tile_off(t, 4 * j), hlo);
-  lds_st<uint2>(tile, tile_off(t, kHalf + 4 * j), hhi);
+  lds_st<uint2>(tile, Lay::off(t, 4 * j), hlo);
+  lds_st<uint2>(tile, Lay::off(t, kHalf + 4 * j), hhi);
   if (lo != nullptr && t < kLoRows) {
     const uint2 llo = make_uint2(pack2(y[0] - bf2f_lo(hlo.x), y[1] - bf2f_hi(hlo.x)),
                                  pack2(y[2] - bf2f_lo(hlo.y), y[3] - bf2f_hi(hlo.y)));
     const uint2 lhi = make_uint2(pack2(y[4] - bf2f_lo(hhi.x), y[5] - bf2f_hi(hhi.x)),
                                  pack2(y[6] - bf2f_lo(hhi.y), y[7] - bf2f_hi(hhi.y)));
-    lds_st<uint2>(lo, tile_off(t, 4 * j), llo);
-    lds_st<uint2>(lo, tile_off(t, kHalf + 4 * j), lhi);
+    lds_st<uint2>(lo, Lay::off(t, 4 * j), llo);
+    lds_st<uint2>(lo, Lay::off(t, kHalf + 4 * j), lhi);
   }
 }
 
@@ -211,13 +229,13 @@ __device__ __forceinline__ void norm_rope_stage(const Rows<M>& R, const float (&
 
 // One tensor, with the first row's rotations E already formed (advanced in place);
 // `lo` receives the lo parts of rows below kLoRows.
-template <bool kWeights, int M, int kStep, int kLoRows = kExactRows>
+template <bool kWeights, int M, int kStep, int kLoRows = kExactRows, class Lay = TileNat>
 __device__ __forceinline__ void norm_rope_rows(const Rows<M>& R, const float (&w)[8], float eps, float2 (&E)[4],
                                                const Rope& L, int rg, int j, uint8_t* tile, uint8_t* lo) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     if (m > 0) next_rotation(L, E);
-    norm_rope_row<kWeights, kLoRows>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, lo);
+    norm_rope_row<kWeights, kLoRows, Lay>(R.lo[m], R.hi[m], w, eps, E, rg + kStep * m, j, tile, lo);
   }
 }
 
