@@ -49,46 +49,6 @@ __device__ __forceinline__ bf16x8 snap_col(const uint8_t* snap, int kk, int c0, 
   return v_operand(snap, kk, c0, g4, n16);
 }
 
-// Row operand in key order pi from a TilePi tile: lane (g, n16) gets dims
-// pi(8g + e) of row t, which are 16 contiguous bytes.
-__device__ __forceinline__ bf16x8 pi_row(const uint8_t* tile, int t, int kk, int g4) {
-  return as_bf16x8(lds_ld<uint4>(tile, t * TilePi::kRow + 2 * (32 * kk + 8 * g4)));
-}
-
-// Column operand of a TilePi tile with tokens in natural order: lane n16 gets
-// X[32kk + 8g + e][c0 + n16] (two transposed reads of 4 rows each).
-__device__ __forceinline__ bf16x8 col_nat(const uint8_t* tile, int kk, int c0, int g4, int n16) {
-  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
-  return as_bf16x8(lds_tr(tile, TilePi::off(t0, c)), lds_tr(tile, TilePi::off(t0 + 4, c)));
-}
-
-// Score column operand, tokens in natural order: lane n16 gets P[32kk + 8g + e][s0 + n16].
-__device__ __forceinline__ bf16x8 score_col(const uint8_t* sP, int kk, int s0, int g4, int n16) {
-  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
-  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 4, c)));
-}
-
-// Score row operand, tokens in natural order: lane n16 gets P[t][32kk + 8g + e].
-__device__ __forceinline__ bf16x8 score_row(const uint8_t* sP, int t, int kk, int g4) {
-  return as_bf16x8(lds_ld<uint4>(sP, score_off(t, 32 * kk + 8 * g4)));
-}
-
-// X[:, 16w .. 16w+16) += A^T B over one chunk, A a TilePi tile (its 128 columns
-// are the accumulator rows), B the chunk's column operand (col_nat, 16 columns).
-__device__ __forceinline__ void accumulate_nat(f32x4 (&acc)[8], const uint8_t* A, const bf16x8 (&Bop)[2],
-                                               int g4, int n16) {
-#pragma unroll
-  for (int kk = 0; kk < kC / 32; ++kk) {
-    const int t0 = 32 * kk + 8 * g4 + (n16 >> 2);
-#pragma unroll
-    for (int rtk = 0; rtk < 8; ++rtk) {
-      const int c = 16 * rtk + 4 * (n16 & 3);
-      const bf16x8 a = as_bf16x8(lds_tr(A, TilePi::off(t0, c)), lds_tr(A, TilePi::off(t0 + 4, c)));
-      acc[rtk] = mma(a, Bop[kk], acc[rtk]);
-    }
-  }
-}
-
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
   uint4 u = __builtin_bit_cast(uint4, x);
   u.x ^= 0x80008000u;
@@ -228,7 +188,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     {
       bf16x8 nU[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_nat(sU, kk, 16 * w, g4, n16));
+      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_nat<TilePi>(sU, kk, 16 * w, g4, n16));
       accumulate_nat(Gacc, sQ, nU, g4, n16);
     }
     __syncthreads();
@@ -265,7 +225,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat(sV, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat<TilePi>(sV, kk, 16 * w, g4, n16);
 #pragma unroll
         for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sP, 16 * rt + n16, kk, g4), acc[rt]);
       }
@@ -294,7 +254,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat(sK, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat<TilePi>(sK, kk, 16 * w, g4, n16);
 #pragma unroll
         for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sdP, 16 * rt + n16, kk, g4), acc[rt]);
       }
@@ -310,7 +270,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat(sU, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat<TilePi>(sU, kk, 16 * w, g4, n16);
 #pragma unroll
         for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sP, kk, 16 * rt, g4, n16), acc[rt]);
       }
@@ -326,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat(sQ, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_nat<TilePi>(sQ, kk, 16 * w, g4, n16);
 #pragma unroll
         for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sdP, kk, 16 * rt, g4, n16), acc[rt]);
       }
@@ -334,7 +294,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       // S before the next chunk: S += Kh^T V
       bf16x8 Vf[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat(sV, kk, 16 * w, g4, n16);
+      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat<TilePi>(sV, kk, 16 * w, g4, n16);
       accumulate_nat(Sacc, sK, Vf, g4, n16);
     }
     __syncthreads();

@@ -345,5 +345,49 @@ constexpr int kScoreRowBytes = kC * 2 + 16;  // [64][64] bf16 score tile, padded
 
 __device__ __forceinline__ int score_off(int t, int s) { return t * kScoreRowBytes + 2 * s; }
 
+// ---- operands in natural token order and from TilePi tiles
+
+// Row operand in key order pi from a TilePi tile: lane (g, n16) gets dims
+// pi(8g + e) of row t, which are 16 contiguous bytes.
+__device__ __forceinline__ bf16x8 pi_row(const uint8_t* tile, int t, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint4>(tile, t * TilePi::kRow + 2 * (32 * kk + 8 * g4)));
+}
+
+// Column operand with tokens in natural order: lane n16 gets X[32kk + 8g + e][c0 + n16]
+// (two transposed reads of 4 rows each).
+template <class Lay>
+__device__ __forceinline__ bf16x8 col_nat(const uint8_t* tile, int kk, int c0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(tile, Lay::off(t0, c)), lds_tr(tile, Lay::off(t0 + 4, c)));
+}
+
+// Score row operand, tokens in natural order: lane n16 gets P[t][32kk + 8g + e].
+__device__ __forceinline__ bf16x8 score_row(const uint8_t* sP, int t, int kk, int g4) {
+  return as_bf16x8(lds_ld<uint4>(sP, score_off(t, 32 * kk + 8 * g4)));
+}
+
+// Score column operand, tokens in natural order: lane n16 gets P[32kk + 8g + e][s0 + n16].
+__device__ __forceinline__ bf16x8 score_col(const uint8_t* sP, int kk, int s0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 4, c)));
+}
+
+// acc[rtk] (rows 16 rtk .. + 16 of X = A^T B, this wave's 16 columns) += over one
+// chunk, A a TilePi tile whose 128 columns are the rows of X, B the chunk's column
+// operand (col_nat, tokens in natural order).
+__device__ __forceinline__ void accumulate_nat(f32x4 (&acc)[8], const uint8_t* A, const bf16x8 (&Bop)[2],
+                                               int g4, int n16) {
+#pragma unroll
+  for (int kk = 0; kk < kC / 32; ++kk) {
+    const int t0 = 32 * kk + 8 * g4 + (n16 >> 2);
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk) {
+      const int c = 16 * rtk + 4 * (n16 & 3);
+      const bf16x8 a = as_bf16x8(lds_tr(A, TilePi::off(t0, c)), lds_tr(A, TilePi::off(t0 + 4, c)));
+      acc[rtk] = mma(a, Bop[kk], acc[rtk]);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace la
