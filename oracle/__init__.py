@@ -32,6 +32,12 @@ What each function follows (pages cited by title and section):
     q, k, v, g and the layer output o to bfloat16 (nearest-even) where they are
     handed on, so the comparison measures the layer's arithmetic rather than the
     hand-over format.
+  * ``sparse_forward`` / ``sparse_decode`` -- the sparse attention layers of the
+    same hybrid (block selection, NoPE, output gate): technical-report rendering,
+    02 模型架構 (2) 稀疏注意力模塊 and (4) 混合位置編碼, and "9B端側開源模型跑通百萬上下文，
+    面壁全新稀疏-線性混合注意力" (architecture section).  The arithmetic is in
+    ``sparse_oracle.c`` (own library), whose header lists the readings taken where
+    the pages are silent.
 """
 from __future__ import annotations
 
@@ -76,6 +82,51 @@ def _bind(lib):
         lib.lao_backward.argtypes = [_f32p] * 5 + [ctypes.c_int] * 4 + [
             ctypes.c_int64, ctypes.c_double, ctypes.c_double, _f32p, _f32p, _f64p, _f64p] + [_f64p] * 7
     return lib
+
+
+_SPARSE_SRC = os.path.join(_DIR, "sparse_oracle.c")
+_SPARSE_LIB = os.path.join(_DIR, "libsparseoracle.so")
+_slib = None
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+def build_sparse(force: bool = True) -> str:
+    """Compile sparse_oracle.c into libsparseoracle.so with gcc (-O2 -fopenmp)."""
+    if force or not os.path.exists(_SPARSE_LIB) or os.path.getmtime(_SPARSE_LIB) < os.path.getmtime(_SPARSE_SRC):
+        tmp = _SPARSE_LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", _SPARSE_SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _SPARSE_LIB)
+    return _SPARSE_LIB
+
+
+def _bind_sparse(lib):
+    lib.lso_set_threads.argtypes = [ctypes.c_int]
+    lib.lso_sparse_forward.argtypes = [_f32p] * 4 + [ctypes.c_int] * 6 + [_i32p, ctypes.c_int, _f64p, _f64p]
+    lib.lso_sparse_decode.argtypes = [_f32p] * 4 + [_i32p] + [ctypes.c_int] * 6 + [_i32p, ctypes.c_int, _f64p,
+                                                                                       _f64p]
+    return lib
+
+
+def _load_sparse():
+    global _slib
+    if _slib is None:
+        if not os.path.exists(_SPARSE_LIB) or os.path.getmtime(_SPARSE_LIB) < os.path.getmtime(_SPARSE_SRC):
+            build_sparse(force=True)
+        _slib = _bind_sparse(ctypes.CDLL(_SPARSE_LIB))
+    return _slib
+
+
+@contextlib.contextmanager
+def use_sparse_library(path: str):
+    """Temporarily route the sparse-layer calls to another build of sparse_oracle.c."""
+    global _slib
+    saved = _load_sparse()
+    _slib = _bind_sparse(ctypes.CDLL(path))
+    try:
+        yield
+    finally:
+        _slib = saved
 
 
 def _load():
@@ -248,3 +299,48 @@ def backward(q, k, v, g, do, S=None, dS_out=None, pos0: int = 0, base: float = 1
     if dkw is not None:
         out["dk_w"] = dkw.sum(axis=0)
     return out
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def sparse_forward(q, k, v, g, block: int = 64, topk: int = 16, sel=None, threads: int = 0):
+    """Sparse layer over whole sequences from position 0 (readings in sparse_oracle.c).
+    q, k, v, g: [B, T, H, D].  With ``sel`` ([B, H, ceil(T / block), topk] int32, -1 =
+    unused) those blocks are attended instead of the computed choice.  Returns
+    (o [B, T, H, D] float64, sel int32, scores [B, H, nqb, T // block] float64)."""
+    q, k, v, g = (_f32(x) for x in (q, k, v, g))
+    B, T, H, D = q.shape
+    assert D <= 1024 and block >= 1 and topk >= 1
+    nqb, nkb = -(-T // block), T // block
+    use = sel is not None
+    s = _i32(sel).copy() if use else np.empty((B, H, nqb, topk), np.int32)
+    assert s.shape == (B, H, nqb, topk)
+    scores = np.zeros((B, H, nqb, max(nkb, 1)), np.float64)
+    o = np.empty((B, T, H, D), np.float64)
+    lib = _load_sparse()
+    lib.lso_set_threads(int(threads))
+    lib.lso_sparse_forward(_p32(q), _p32(k), _p32(v), _p32(g), B, T, H, D, int(block), int(topk),
+                           s.ctypes.data_as(_i32p), int(use), _p64(scores), _p64(o))
+    return o, s, scores[..., :nkb]
+
+
+def sparse_decode(q, k_cache, v_cache, g, lens, block: int = 64, topk: int = 16, sel=None, threads: int = 0):
+    """One decode step of the sparse layer.  q, g: [B, H, D] (the query of each cache's
+    last valid token); k_cache, v_cache: [B, Tmax, H, D]; lens: [B] valid tokens (>= 1).
+    Returns (o [B, H, D] float64, sel [B, H, topk] int32, scores [B, H, Tmax // block])."""
+    q, k_cache, v_cache, g = (_f32(x) for x in (q, k_cache, v_cache, g))
+    B, Tmax, H, D = k_cache.shape
+    lens = _i32(lens)
+    assert lens.shape == (B,) and np.all(lens >= 1) and np.all(lens <= Tmax) and D <= 1024
+    use = sel is not None
+    s = _i32(sel).copy() if use else np.empty((B, H, topk), np.int32)
+    nkb = Tmax // block
+    scores = np.zeros((B, H, max(nkb, 1)), np.float64)
+    o = np.empty((B, H, D), np.float64)
+    lib = _load_sparse()
+    lib.lso_set_threads(int(threads))
+    lib.lso_sparse_decode(_p32(q), _p32(k_cache), _p32(v_cache), _p32(g), lens.ctypes.data_as(_i32p), B, Tmax, H,
+                          D, int(block), int(topk), s.ctypes.data_as(_i32p), int(use), _p64(scores), _p64(o))
+    return o, s, scores[..., :nkb]
