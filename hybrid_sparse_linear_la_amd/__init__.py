@@ -25,7 +25,9 @@ __all__ = ["prefill", "decode_step", "prefill_varlen", "linear", "layer_forward"
            "prefill_workspace_bytes", "backward_workspace_bytes",
            "layer_workspace_bytes",
            "prefill_varlen_workspace_bytes", "LAError", "library", "lib_path",
-           "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS"]
+           "STATUS", "HEAD_DIM", "DEFAULT_CHUNK", "SUPPORTED_CHUNKS",
+           "sparse_prefill", "sparse_prefill_workspace_bytes", "sparse_block_means", "sparse_decode",
+           "SPARSE_BLOCK"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "liblightning_la.so")
@@ -33,6 +35,7 @@ lib_path = os.path.join(_PKG, "liblightning_la.so")
 HEAD_DIM = 128
 DEFAULT_CHUNK = 64
 SUPPORTED_CHUNKS = (0, 64, 128, 256)
+SPARSE_BLOCK = 64
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
     4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",
@@ -88,6 +91,14 @@ def library():
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
             ctypes.c_int64, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
+        lib.la_sparse_prefill_workspace_bytes.restype = ctypes.c_size_t
+        lib.la_sparse_prefill_workspace_bytes.argtypes = [ctypes.c_int] * 6
+        lib.la_sparse_prefill.restype = ctypes.c_int
+        lib.la_sparse_prefill.argtypes = [_vp] * 6 + [ctypes.c_int] * 6 + [_vp, ctypes.c_size_t, _vp]
+        lib.la_sparse_block_means.restype = ctypes.c_int
+        lib.la_sparse_block_means.argtypes = [_vp, _vp] + [ctypes.c_int] * 7 + [_vp]
+        lib.la_sparse_decode.restype = ctypes.c_int
+        lib.la_sparse_decode.argtypes = [_vp] * 8 + [ctypes.c_int] * 6 + [_vp]
         _lib = lib
     return _lib
 
@@ -354,3 +365,75 @@ def decode_step(q, k, v, gate, S, pos: int, rope_base: float = 10000.0, rms_eps:
                               int(pos), float(rope_base), float(rms_eps), _ptr(q_norm_w),
                               _ptr(k_norm_w), _stream(q.device)))
     return out
+
+
+# ---- sparse attention layers (block selection, NoPE, output gate)
+
+def sparse_prefill_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, topk: int = 16) -> int:
+    return int(library().la_sparse_prefill_workspace_bytes(B, T, H, D, 0, topk))
+
+
+def sparse_prefill(q, k, v, gate, topk: int = 16, return_sel: bool = False, out=None, workspace=None):
+    """Sparse layer over whole sequences.  q, k, v, gate: bf16 [B, T, H, 128] on the
+    GPU.  Returns o (bf16, shaped as q), and with ``return_sel`` also the chosen key
+    blocks (int32 [B, H, ceil(T / 64), topk], increasing, then -1)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+        _act(n, t, 4)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    B, T, H, D = q.shape
+    o = torch.empty_like(q) if out is None else out
+    _act("out", o, 4)
+    nqb = -(-T // SPARSE_BLOCK)
+    sel = torch.empty((B, H, nqb, topk), dtype=torch.int32, device=q.device) if return_sel else None
+    need = int(lib.la_sparse_prefill_workspace_bytes(B, T, H, D, 0, topk))
+    if need == 0:
+        raise LAError(3, lib.la_status_string(3).decode())
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.la_sparse_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(o), _ptr(sel), B, T, H, D, 0,
+                                 int(topk), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(q.device)))
+    return (o, sel) if return_sel else o
+
+
+def sparse_block_means(k_cache, means=None, first_block: int = 0, nblocks=None):
+    """Block means (fp32 [B, H, Tmax / 64, 128]) of a key cache [B, Tmax, H, 128];
+    only blocks [first_block, first_block + nblocks) are (re)computed."""
+    lib = library()
+    _act("k_cache", k_cache, 4)
+    B, Tmax, H, D = k_cache.shape
+    shape = (B, H, Tmax // SPARSE_BLOCK, D)
+    if means is None:
+        means = torch.zeros(shape, dtype=torch.float32, device=k_cache.device)
+    _f32("means", means, shape)
+    if nblocks is None:
+        nblocks = Tmax // SPARSE_BLOCK - first_block
+    _check(lib.la_sparse_block_means(_ptr(k_cache), _ptr(means), B, Tmax, H, D, 0, int(first_block), int(nblocks),
+                                     _stream(k_cache.device)))
+    return means
+
+
+def sparse_decode(q, k_cache, v_cache, means, gate, lens, topk: int = 16, return_sel: bool = False, out=None):
+    """One decode step of the sparse layer.  q, gate: bf16 [B, H, 128] (the newest
+    token's query; its k, v already in the caches); k_cache, v_cache: bf16
+    [B, Tmax, H, 128]; means: their block means; lens: int32 [B] on the GPU (valid
+    tokens, the newest included).  Returns o bf16 [B, H, 128] (and the chosen blocks,
+    int32 [B, H, topk], with ``return_sel``)."""
+    lib = library()
+    _act("q", q, 3)
+    _act("gate", gate, 3)
+    _act("k_cache", k_cache, 4)
+    _act("v_cache", v_cache, 4)
+    B, Tmax, H, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or q.shape != (B, H, D) or gate.shape != q.shape:
+        raise ValueError("shapes of q, gate, k_cache, v_cache disagree")
+    _f32("means", means, (B, H, Tmax // SPARSE_BLOCK, D))
+    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or not lens.is_cuda:
+        raise ValueError("lens must be an int32 GPU tensor of shape [B]")
+    o = torch.empty_like(q) if out is None else out
+    sel = torch.empty((B, H, topk), dtype=torch.int32, device=q.device) if return_sel else None
+    _check(lib.la_sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(means), _ptr(gate), _ptr(lens),
+                                _ptr(o), _ptr(sel), B, Tmax, H, D, 0, int(topk), _stream(q.device)))
+    return (o, sel) if return_sel else o

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblightning_la.so")
-SOURCES = ("la_api.hip", "la_prefill.hip", "la_decode.hip", "la_gemm.hip", "la_backward.hip")
+SOURCES = ("la_api.hip", "la_prefill.hip", "la_decode.hip", "la_gemm.hip", "la_backward.hip", "la_sparse.hip")
 ARCH = os.environ.get("LA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

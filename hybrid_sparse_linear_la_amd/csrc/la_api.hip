@@ -562,4 +562,117 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
   return launch_backward_chunks(bp, plan, s) == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
+static bool sparse_shape_ok(int B, int T, int H, int D, int block, int topk, la_status* st) {
+  if (B < 1 || T < 1 || H < 1 || B > 65535 || H > 65535) {
+    *st = LA_ERR_BAD_SHAPE;
+    return false;
+  }
+  if (D != kHeadDim || (block != 0 && block != kSparseBlock) || topk < 1 || topk > kSparseMaxTopk ||
+      T / kSparseBlock > kSparseMaxBlocks) {
+    *st = LA_ERR_UNSUPPORTED;
+    return false;
+  }
+  return true;
+}
+
+size_t la_sparse_prefill_workspace_bytes(int B, int T, int H, int D, int block, int topk) {
+  la_status st;
+  if (!sparse_shape_ok(B, T, H, D, block, topk, &st)) return 0;
+  const size_t means = (size_t)B * H * (T / kSparseBlock) * D * sizeof(float);
+  return round_up(means > 0 ? means : 1, 256);
+}
+
+la_status la_sparse_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                            la_bf16* o, int32_t* sel, int B, int T, int H, int D, int block, int topk,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !gate_logits || !o || !workspace) return LA_ERR_NULL_PTR;
+  la_status st;
+  if (!sparse_shape_ok(B, T, H, D, block, topk, &st)) return st;
+  const int64_t nqb = (T + kSparseBlock - 1) / kSparseBlock;
+  if (nqb * H * B >= ((int64_t)1 << 31)) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {q, k, v, gate_logits, o, sel, workspace};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const size_t need = la_sparse_prefill_workspace_bytes(B, T, H, D, block, topk);
+  if (workspace_bytes < need) return LA_ERR_WORKSPACE;
+  const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
+  const uint64_t selb = sel ? (uint64_t)B * H * nqb * topk * sizeof(int32_t) : 0;
+  const void* ins[] = {q, k, v, gate_logits};
+  for (const void* in : ins)
+    if (overlaps(o, act, in, act) || overlaps(sel, selb, in, act) || overlaps(workspace, need, in, act))
+      return LA_ERR_ALIASING;
+  if (overlaps(o, act, sel, selb) || overlaps(o, act, workspace, need) || overlaps(sel, selb, workspace, need))
+    return LA_ERR_ALIASING;
+  SparseParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = gate_logits;
+  p.o = o;
+  p.kmean = static_cast<float*>(workspace);
+  p.sel = sel;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.topk = topk;
+  return launch_sparse_prefill(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_sparse_block_means(const la_bf16* k_cache, float* means, int B, int Tmax, int H, int D, int block,
+                                int first_block, int nblocks, void* stream) {
+  if (!k_cache || !means) return LA_ERR_NULL_PTR;
+  la_status st;
+  if (!sparse_shape_ok(B, Tmax, H, D, block, 1, &st)) return st;
+  if (first_block < 0 || nblocks < 0 || (int64_t)first_block + nblocks > Tmax / kSparseBlock)
+    return LA_ERR_BAD_SHAPE;
+  if (!aligned16(k_cache) || !aligned16(means)) return LA_ERR_ALIGNMENT;
+  const uint64_t cache = (uint64_t)B * Tmax * H * D * sizeof(la_bf16);
+  if (overlaps(means, (uint64_t)B * H * (Tmax / kSparseBlock) * D * sizeof(float), k_cache, cache))
+    return LA_ERR_ALIASING;
+  SparseParams p{};
+  p.k = k_cache;
+  p.kmean = means;
+  p.B = B;
+  p.T = Tmax;
+  p.H = H;
+  p.topk = 1;
+  return launch_sparse_means(p, first_block, nblocks, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK
+                                                                                                     : LA_ERR_HIP;
+}
+
+la_status la_sparse_decode(const la_bf16* q, const la_bf16* k_cache, const la_bf16* v_cache, const float* means,
+                           const la_bf16* gate_logits, const int32_t* lens, la_bf16* o, int32_t* sel, int B,
+                           int Tmax, int H, int D, int block, int topk, void* stream) {
+  if (!q || !k_cache || !v_cache || !means || !gate_logits || !lens || !o) return LA_ERR_NULL_PTR;
+  la_status st;
+  if (!sparse_shape_ok(B, Tmax, H, D, block, topk, &st)) return st;
+  if ((int64_t)B * H >= ((int64_t)1 << 31)) return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {q, k_cache, v_cache, means, gate_logits, o, sel};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  const uint64_t row = (uint64_t)B * H * D * sizeof(la_bf16);
+  const uint64_t cache = (uint64_t)B * Tmax * H * D * sizeof(la_bf16);
+  const uint64_t mb = (uint64_t)B * H * (Tmax / kSparseBlock) * D * sizeof(float);
+  const uint64_t selb = sel ? (uint64_t)B * H * topk * sizeof(int32_t) : 0;
+  const std::pair<const void*, uint64_t> ins[] = {{q, row}, {k_cache, cache}, {v_cache, cache},
+                                                  {means, mb}, {gate_logits, row}, {lens, (uint64_t)B * 4}};
+  for (const auto& in : ins)
+    if (overlaps(o, row, in.first, in.second) || overlaps(sel, selb, in.first, in.second)) return LA_ERR_ALIASING;
+  if (overlaps(o, row, sel, selb)) return LA_ERR_ALIASING;
+  SparseParams p{};
+  p.q = q;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.g = gate_logits;
+  p.o = o;
+  p.kmean = const_cast<float*>(means);
+  p.sel = sel;
+  p.lens = lens;
+  p.B = B;
+  p.T = Tmax;
+  p.H = H;
+  p.topk = topk;
+  return launch_sparse_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
 }  // extern "C"

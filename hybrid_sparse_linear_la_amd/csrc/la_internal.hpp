@@ -132,4 +132,27 @@ constexpr int kPrologueBlocks = 2048;
 hipError_t launch_segment_states(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
 hipError_t launch_backward_chunks(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
 
+// Sparse attention layer (block-selected causal softmax attention, NoPE, output
+// gate).  Blocks of kSparseBlock tokens; a key block is scored by its mean key.
+constexpr int kSparseBlock = 64;
+constexpr int kSparseMaxTopk = 64;
+constexpr int kSparseMaxBlocks = 8192;  // key blocks per sequence (512K tokens)
+
+struct SparseParams {
+  const uint16_t* q;   // prefill [B][T][H][D]; decode [B][H][D]
+  const uint16_t* k;   // prefill [B][T][H][D]; decode: cache [B][T][H][D] (T = Tmax)
+  const uint16_t* v;
+  const uint16_t* g;   // shaped as q
+  uint16_t* o;         // shaped as q
+  float* kmean;        // [B][H][T / kSparseBlock][D] fp32 block means of k
+  int32_t* sel;        // prefill [B][H][nqb][topk], decode [B][H][topk], or nullptr
+  const int32_t* lens; // decode: valid tokens per sequence (the query is the last)
+  int B, T, H, topk;
+};
+
+// Means of key blocks [first, first + nblocks) of every (b, h) of p.k into p.kmean.
+hipError_t launch_sparse_means(const SparseParams& p, int first, int nblocks, hipStream_t stream);
+hipError_t launch_sparse_prefill(const SparseParams& p, hipStream_t stream);
+hipError_t launch_sparse_decode(const SparseParams& p, hipStream_t stream);
+
 }  // namespace la

@@ -235,6 +235,63 @@ la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
                          int64_t pos, float rope_base, float rms_eps, const float* q_norm_w,
                          const float* k_norm_w, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * The sparse attention layers of the same hybrid (InfLLM-v2 block selection, no
+ * position encoding, output gate): "創新Transformer！面壁基於稀疏-線性混合架構SALA訓練9B
+ * 模型，端側跑通百萬上下文", 04 技術報告 > 02 模型架構 > (2) 稀疏注意力模塊 (each query
+ * reaches only a few key/value blocks chosen by block selection; dense at ordinary
+ * lengths; output gate) and (4) 混合位置編碼 (NoPE in these layers).
+ * Readings where the pages are silent: causal softmax attention with scale
+ * 1/sqrt(D); blocks of 64 tokens; key block j is scored by its mean key kbar_j and a
+ * block of queries by its mean query (a decode step: the query itself):
+ * s = qbar . kbar_j over the complete blocks j before the query's block; the topk
+ * best (ties to the lower block) plus the query's own block up to the query are
+ * attended; o = sigmoid(g) * (attention output).  With at most topk earlier blocks
+ * the layer is dense causal attention.
+ * Layouts: q, k, v, gate logits, o: bf16 [B, T, H, D] (decode q, gate, o: [B, H, D];
+ * caches [B, Tmax, H, D]); block means fp32 [B, H, T / 64, D].
+ * Supported: D == 128, block in {0 (= 64), 64}, 1 <= topk <= 64, at most 8192 key
+ * blocks per sequence (T or Tmax <= 524288), B and H <= 65535.
+ */
+
+/* Workspace of la_sparse_prefill: the key-block means, fp32 [B, H, T / 64, D]
+ * (0 for an unsupported shape). */
+size_t la_sparse_prefill_workspace_bytes(int B, int T, int H, int D, int block, int topk);
+
+/*
+ * Sparse layer over whole sequences from position 0.
+ *   q, k, v, gate_logits : [B, T, H, D] bf16;  o : [B, T, H, D] bf16 output.
+ *   sel : NULL, or int32 [B, H, ceil(T / 64), topk] output: each query block's chosen
+ *         key blocks in increasing order, then -1.
+ * Outputs must not overlap the inputs, each other or the workspace.
+ */
+la_status la_sparse_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                            la_bf16* o, int32_t* sel, int B, int T, int H, int D, int block, int topk,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Means of key blocks [first_block, first_block + nblocks) of a key cache
+ * k_cache ([B, Tmax, H, D] bf16) into means ([B, H, Tmax / 64, D] fp32), for
+ * la_sparse_decode.  A serving loop calls it once per completed block; the blocks
+ * named must be filled ((first_block + nblocks) * 64 <= Tmax).
+ */
+la_status la_sparse_block_means(const la_bf16* k_cache, float* means, int B, int Tmax, int H, int D, int block,
+                                int first_block, int nblocks, void* stream);
+
+/*
+ * One decode step of the sparse layer per sequence.
+ *   q, gate_logits : [B, H, D] bf16, the query of each sequence's newest token,
+ *       whose k and v are already in the caches;
+ *   k_cache, v_cache : [B, Tmax, H, D] bf16;  means : their block means
+ *       (la_sparse_block_means) for every complete block before the newest token's;
+ *   lens : device int32 [B], valid tokens per sequence (the newest included), read
+ *       on the device; values outside [1, Tmax] are clamped into it;
+ *   o : [B, H, D] bf16 output;  sel : NULL or int32 [B, H, topk] output.
+ */
+la_status la_sparse_decode(const la_bf16* q, const la_bf16* k_cache, const la_bf16* v_cache, const float* means,
+                           const la_bf16* gate_logits, const int32_t* lens, la_bf16* o, int32_t* sel, int B,
+                           int Tmax, int H, int D, int block, int topk, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

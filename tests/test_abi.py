@@ -27,7 +27,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
          "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_linear", "la_layer_workspace_bytes",
-         "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_decode_step"])
+         "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_decode_step",
+         "la_sparse_prefill_workspace_bytes", "la_sparse_prefill", "la_sparse_block_means", "la_sparse_decode"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -222,3 +223,51 @@ def test_backward_validation(lib):
     assert bwd(dk=A + 8 * MB + 64) == 5   # dk overlaps dq
     assert bwd(ws=A + 12 * MB) == 5       # workspace overlaps dS_in
     assert bwd(ws_bytes=4096) == 6
+
+
+def test_sparse_validation(lib):
+    vp = ctypes.c_void_p
+    # workspace: fp32 means of the complete 64-token key blocks
+    assert lib.la_sparse_prefill_workspace_bytes(1, 32768, 32, 128, 0, 16) == 32 * 512 * 128 * 4
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 64, 16) == 2 * 4 * 128 * 4
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 32, 16) == 0     # block 64 only
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 0, 0) == 0       # topk in [1, 64]
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 0, 65) == 0
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 64, 0, 16) == 0
+    assert lib.la_sparse_prefill_workspace_bytes(1, 64 * 8192 + 64, 1, 128, 0, 16) == 0   # > 8192 key blocks
+
+    def pre(q=A, k=A + MB, v=A + 2 * MB, g=A + 3 * MB, o=A + 4 * MB, sel=None, B=1, T=300, H=2, D=128, block=0,
+            topk=16, ws=A + 8 * MB, ws_bytes=1 << 20):
+        return lib.la_sparse_prefill(vp(q), vp(k), vp(v), vp(g), vp(o), vp(sel), B, T, H, D, block, topk, vp(ws),
+                                     ws_bytes, None)
+    assert pre(k=None) == 1
+    assert pre(ws=None) == 1
+    assert pre(T=0) == 2
+    assert pre(topk=0) == 3
+    assert pre(block=128) == 3
+    assert pre(o=A + 4 * MB + 8) == 4
+    assert pre(o=A + 1024) == 5              # o overlaps q
+    assert pre(sel=A + 4 * MB + 256) == 5    # sel overlaps o
+    assert pre(ws=A + 3 * MB) == 5           # workspace overlaps gate
+    assert pre(ws_bytes=1024) == 6
+
+    def means(k=A, m=A + 64 * MB, B=1, Tmax=1024, H=2, D=128, block=0, first=0, n=16):
+        return lib.la_sparse_block_means(vp(k), vp(m), B, Tmax, H, D, block, first, n, None)
+    assert means(m=None) == 1
+    assert means(n=17) == 2                  # past the cache
+    assert means(first=-1) == 2
+    assert means(D=96) == 3
+    assert means(m=A + 4) == 4
+    assert means(m=A + 1024) == 5
+
+    def dec(q=A, kc=A + MB, vc=A + 64 * MB, m=A + 128 * MB, g=A + 129 * MB, lens=A + 130 * MB, o=A + 131 * MB,
+            sel=None, B=2, Tmax=4096, H=2, D=128, block=0, topk=16):
+        return lib.la_sparse_decode(vp(q), vp(kc), vp(vc), vp(m), vp(g), vp(lens), vp(o), vp(sel), B, Tmax, H, D,
+                                    block, topk, None)
+    assert dec(lens=None) == 1
+    assert dec(m=None) == 1
+    assert dec(B=0) == 2
+    assert dec(topk=65) == 3
+    assert dec(o=A + 131 * MB + 2) == 4
+    assert dec(o=A + 2 * MB) == 5            # o inside the key cache
+    assert dec(sel=A + 130 * MB) == 5        # sel overlaps lens

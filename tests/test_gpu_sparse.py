@@ -1,0 +1,166 @@
+"""GPU parity of the sparse layer (la_sparse_prefill, la_sparse_block_means,
+la_sparse_decode) against the fp64 oracle.
+
+The block choice is an integer decision taken from fp32 scores on the GPU and fp64
+scores in the oracle, so near-ties may resolve differently: the GPU's choice is
+checked for validity (the right number of blocks, all of them candidates, none
+scoring below an unchosen candidate by more than the fp32 rounding of a 128-term
+dot product), and the outputs are compared with the oracle evaluated on the GPU's
+choice, to the layer's row tolerance (2e-2 relative)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_o_close, to_np, to_np32
+
+pytestmark = pytest.mark.gpu
+D = 128
+BLK = 64
+
+
+@pytest.fixture(scope="module")
+def la():
+    import hybrid_sparse_linear_la_amd as la
+    la.library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return la
+
+
+def _check_choice(sel, scores, ncand, topk, what):
+    """sel: [..., topk] chosen blocks (increasing, then -1); scores: [..., nkb] fp64
+    oracle scores; ncand: candidates per entry (same leading shape)."""
+    sel = np.asarray(sel)
+    flat_sel = sel.reshape(-1, sel.shape[-1])
+    flat_sc = scores.reshape(-1, scores.shape[-1]) if scores.shape[-1] else np.zeros((flat_sel.shape[0], 0))
+    flat_n = np.broadcast_to(ncand, sel.shape[:-1]).reshape(-1)
+    differ = 0
+    for e in range(flat_sel.shape[0]):
+        n = int(flat_n[e])
+        chosen = [int(x) for x in flat_sel[e] if x >= 0]
+        assert len(chosen) == min(topk, n), f"{what} entry {e}: {len(chosen)} blocks for {n} candidates"
+        assert chosen == sorted(set(chosen)) and all(0 <= x < n for x in chosen), f"{what} entry {e}: {chosen}"
+        assert all(x == -1 for x in flat_sel[e][len(chosen):]), f"{what} entry {e}: padding"
+        if n > topk:
+            sc = flat_sc[e, :n]
+            rest = np.setdiff1d(np.arange(n), chosen)
+            tol = 1e-4 * np.abs(sc).max() + 1e-6
+            assert sc[chosen].min() >= sc[rest].max() - tol, f"{what} entry {e}: a better block was left out"
+            best = sorted(np.lexsort((np.arange(n), -sc))[:topk].tolist())
+            differ += best != chosen
+    return differ
+
+
+def _prefill_case(la, B, T, H, topk, seed):
+    q, k, v, g = workloads.activations(B, T, H, D, seed, "cuda")
+    o, sel = la.sparse_prefill(q, k, v, g, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    f = [to_np32(x) for x in (q, k, v, g)]
+    # the oracle evaluated on the GPU's choice; its scores do not depend on the choice
+    o_ref, _, scores = oracle.sparse_forward(*f, block=BLK, topk=topk, sel=sel.cpu().numpy())
+    nqb = -(-T // BLK)
+    ncand = np.minimum(np.arange(nqb), T // BLK)
+    differ = _check_choice(sel.cpu().numpy(), scores, ncand[None, None, :], topk, f"prefill T={T}")
+    err = assert_o_close(to_np(o), o_ref, what=f"sparse prefill B={B} T={T} H={H} topk={topk}")
+    return err, differ
+
+
+PREFILL_CASES = [
+    # B, T, H, topk
+    (1, 1, 1, 16),            # one token
+    (1, 64, 2, 16),           # one full block
+    (2, 300, 3, 16),          # dense regime (at most 4 earlier blocks)
+    (1, 65 * 64 + 17, 2, 4),  # sparse: 65 full blocks and a ragged tail
+    (2, 40 * 64, 2, 1),       # topk 1
+    (1, 30 * 64 + 1, 1, 64),  # topk 64 (dense up to block 64), last block a single token
+]
+
+
+@pytest.mark.parametrize("B,T,H,topk", PREFILL_CASES)
+def test_sparse_prefill_matches_oracle(la, B, T, H, topk):
+    print(f"sparse prefill B={B} T={T} H={H} topk={topk}", flush=True)
+    err, differ = _prefill_case(la, B, T, H, topk, seed=100 + T % 97 + topk)
+    print(f"  row error max {err['max']:.2e}, choices differing from the fp64 order: {differ}", flush=True)
+
+
+def _caches(B, Tmax, H, seed):
+    gen = workloads.generator(seed, "cuda")
+    kc, vc = (torch.randn((B, Tmax, H, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(2))
+    q, g = (torch.randn((B, H, D), generator=gen, device="cuda").to(torch.bfloat16) for _ in range(2))
+    return q, kc, vc, g
+
+
+@pytest.mark.parametrize("lens,H,topk", [([1, 63, 64, 65, 1000, 4096], 2, 16), ([4096, 2000], 3, 4),
+                                         ([129, 3000], 2, 64)])
+def test_sparse_decode_matches_oracle(la, lens, H, topk):
+    print(f"sparse decode lens={lens} H={H} topk={topk}", flush=True)
+    B, Tmax = len(lens), 4096
+    q, kc, vc, g = _caches(B, Tmax, H, seed=200 + topk)
+    means = la.sparse_block_means(kc)
+    lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, sel = la.sparse_decode(q, kc, vc, means, g, lt, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    f = [to_np32(x) for x in (q, kc, vc, g)]
+    o_ref, _, scores = oracle.sparse_decode(*f, np.array(lens), block=BLK, topk=topk, sel=sel.cpu().numpy())
+    ncand = np.array([(n - 1) // BLK for n in lens])
+    _check_choice(sel.cpu().numpy(), scores, ncand[:, None], topk, "decode")
+    assert_o_close(to_np(o)[:, None], o_ref[:, None], what=f"sparse decode lens={lens}")
+
+
+def test_block_means_match_and_update_in_place(la):
+    B, Tmax, H = 2, 1024, 3
+    _, kc, _, _ = _caches(B, Tmax, H, seed=7)
+    means = la.sparse_block_means(kc)
+    ref = to_np32(kc).astype(np.float64).reshape(B, Tmax // BLK, BLK, H, D).mean(axis=2).transpose(0, 2, 1, 3)
+    np.testing.assert_allclose(to_np(means), ref, rtol=1e-5, atol=1e-6)
+    # recompute two blocks after changing them
+    kc[:, 3 * BLK:5 * BLK] = 0
+    la.sparse_block_means(kc, means, first_block=3, nblocks=2)
+    torch.cuda.synchronize()
+    ref[:, :, 3:5] = 0
+    np.testing.assert_allclose(to_np(means), ref, rtol=1e-5, atol=1e-6)
+
+
+def test_decode_is_the_last_row_of_prefill(la):
+    """When the newest token opens a block, decode and prefill take the same choice
+    (the query block is that token); outputs agree to the rounding of each path."""
+    B, H, topk = 1, 2, 4
+    T = 40 * BLK + 1
+    q, k, v, g = workloads.activations(B, T, H, D, 17, "cuda")
+    o, sel = la.sparse_prefill(q, k, v, g, topk=topk, return_sel=True)
+    means = la.sparse_block_means(k)
+    od, seld = la.sparse_decode(q[:, -1].contiguous(), k, v, means, g[:, -1].contiguous(),
+                                torch.tensor([T], dtype=torch.int32, device="cuda"), topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    assert torch.equal(seld, sel[:, :, -1])
+    a, b = to_np(od), to_np(o[:, -1])
+    rel = np.linalg.norm(a - b, axis=-1) / np.linalg.norm(b, axis=-1)
+    assert rel.max() <= 2e-2, rel.max()
+
+
+def test_sparse_prefill_32k_sampled_heads(la):
+    """The 32K workload (B 1, T 32768, H 32, topk 16) as the bench runs it; the
+    oracle checks two heads (all 512 query blocks each)."""
+    w = workloads.SPARSE_32K
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, D, w.seed, "cuda")
+    o, sel = la.sparse_prefill(q, k, v, g, topk=w.topk, return_sel=True)
+    torch.cuda.synchronize()
+    for h in (0, 29):
+        f = [to_np32(x[:, :, h:h + 1]) for x in (q, k, v, g)]
+        s = sel[:, h:h + 1].cpu().numpy()
+        o_ref, _, scores = oracle.sparse_forward(*f, block=BLK, topk=w.topk, sel=s)
+        differ = _check_choice(s, scores, np.arange(w.T // BLK)[None, None, :], w.topk, f"32K head {h}")
+        e = assert_o_close(to_np(o[:, :, h:h + 1]), o_ref, what=f"32K head {h}")
+        print(f"head {h}: row error max {e['max']:.2e}, choices differing from the fp64 order: {differ}",
+              flush=True)
+
+
+def test_sparse_rejects_bad_arguments(la):
+    q, k, v, g = workloads.activations(1, 100, 2, D, 3, "cuda")
+    with pytest.raises(la.LAError):
+        la.sparse_prefill(q, k, v, g, topk=0)
+    with pytest.raises(la.LAError):
+        la.sparse_prefill(q, k, v, g, topk=65)
+    with pytest.raises(ValueError):
+        la.sparse_prefill(q, k[:, :50].contiguous(), v, g)

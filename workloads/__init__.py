@@ -139,3 +139,32 @@ def layer_inputs(B: int, T: int, hidden: int, H: int, D: int, seed: int, device=
     w_qkvg = (torch.randn((4 * H * D, hidden), generator=gen, device=device) / hidden ** 0.5).to(torch.bfloat16)
     w_o = (torch.randn((hidden, H * D), generator=gen, device=device) / (H * D) ** 0.5).to(torch.bfloat16)
     return x, w_qkvg, w_o
+
+
+@dataclasses.dataclass(frozen=True)
+class SparseWorkload:
+    """Sparse-layer inputs: q, k, v, gate logits ~ N(0, 1) bf16 drawn as by
+    ``activations`` (prefill: [B, T, H, D]); decode draws the caches [B, T, H, D]
+    and then q, gate [B, H, D], every sequence full (T valid tokens)."""
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    topk: int
+    seed: int
+
+
+# A 32K-token prompt through one sparse layer (32 heads x 128, 16 chosen blocks of 64).
+SPARSE_32K = SparseWorkload("sparse_prefill_b1_t32768_h32_d128_top16", 1, 32768, 32, 128, 16, seed=8)
+# Batched decode against 128K-token caches (8 sequences, 32 heads).
+SPARSE_DECODE = SparseWorkload("sparse_decode_b8_ctx131072_h32_d128_top16", 8, 131072, 32, 128, 16, seed=9)
+
+
+def sparse_decode_inputs(w: SparseWorkload, device="cpu"):
+    """(q, k_cache, v_cache, gate) of one decode step; the caches hold T tokens."""
+    gen = generator(w.seed, device)
+    kc, vc = (torch.randn((w.B, w.T, w.H, w.D), generator=gen, device=device).to(torch.bfloat16)
+              for _ in range(2))
+    q, g = (torch.randn((w.B, w.H, w.D), generator=gen, device=device).to(torch.bfloat16) for _ in range(2))
+    return q, kc, vc, g
