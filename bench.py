@@ -382,6 +382,69 @@ def bench_backward(la, torch, workloads, hip, tensors, steps=3):
             "path_frac": round(comp / (HBM_PEAK_GBS * 1e9) / (ms / 1e3), 4)}
 
 
+def sparse_prefill_keys(T: int, topk: int, block: int = 64) -> int:
+    """Keys attended over all rows of one (b, h): row t of query block i sees
+    min(i, topk) whole blocks and its own block up to itself."""
+    total = 0
+    for i in range(-(-T // block)):
+        r0, r1 = i * block, min(i * block + block, T)
+        n = r1 - r0
+        total += n * min(i, topk) * block + n * (n + 1) // 2
+    return total
+
+
+def bench_sparse(la, torch, workloads, hip, steps=5):
+    """The sparse layer: prefill of the 32K workload (MFMA-bound: 4 D flops per
+    attended key and query, q k and p v) and one batched decode step against 128K
+    caches (HBM-bound: the key means scanned and the chosen key/value rows)."""
+    w = workloads.SPARSE_32K
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, w.D, w.seed, "cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(la.sparse_prefill_workspace_bytes(w.B, w.T, w.H, w.D, w.topk), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, n):
+        fn()
+        e = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(e[0], stream)
+        for _ in range(n):
+            fn()
+        hip.record(e[1], stream)
+        ms = hip.ms(e[0], e[1]) / n
+        hip.destroy(e)
+        return ms
+
+    pre_ms = timed(lambda: la.sparse_prefill(q, k, v, g, topk=w.topk, out=o, workspace=ws), steps)
+    flops = 4 * w.D * sparse_prefill_keys(w.T, w.topk) * w.B * w.H
+    tf = flops / (pre_ms / 1e3) / 1e12
+    prefill = {"workload": w.name, "ms": round(pre_ms, 4), "tokens_per_s": round(w.B * w.T / (pre_ms / 1e3), 1),
+               "flops": flops, "roofline": {"bound": "mfma", "kernel": "la_sparse_prefill (means + attention)",
+                                            "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                                            "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}}
+    del q, k, v, g, o, ws
+
+    d = workloads.SPARSE_DECODE
+    qd, kc, vc, gd = workloads.sparse_decode_inputs(d, "cuda")
+    means = la.sparse_block_means(kc)
+    lens = torch.full((d.B,), d.T, dtype=torch.int32, device="cuda")
+    od = torch.empty_like(qd)
+    dec_ms = timed(lambda: la.sparse_decode(qd, kc, vc, means, gd, lens, topk=d.topk, out=od), 20)
+    nblk = d.T // 64
+    own = (d.T - 1) // 64
+    cand = own
+    keys = min(cand, d.topk) * 64 + (d.T - 1 - own * 64 + 1)
+    bytes_step = d.B * d.H * (cand * d.D * 4 + keys * 2 * d.D * 2 + 3 * d.D * 2)
+    gbs = bytes_step / (dec_ms / 1e3) / 1e9
+    decode = {"workload": d.name, "us_per_step": round(dec_ms * 1e3, 2), "bytes_per_step": bytes_step,
+              "key_blocks": nblk, "roofline": {"bound": "hbm", "kernel": "la_sparse_decode_kernel",
+                                               "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                               "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del qd, kc, vc, gd, means
+    return {"prefill": prefill, "decode": decode}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +459,7 @@ def main():
     ap.add_argument("--no-varlen", action="store_true", help="skip the mixed prefill/decode batch")
     ap.add_argument("--no-layer", action="store_true", help="skip the layer forward with its projections")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward of the 256K prefill")
+    ap.add_argument("--no-sparse", action="store_true", help="skip the sparse layer (32K prefill, 128K decode)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -429,6 +493,7 @@ def main():
     varlen = None if args.no_varlen else bench_varlen(la, torch, workloads, hip, args)
     layer = None if args.no_layer else bench_layer(la, torch, workloads, hip, args)
     backward = None if args.no_backward else bench_backward(la, torch, workloads, hip, tensors)
+    sparse = None if args.no_sparse else bench_sparse(la, torch, workloads, hip)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
@@ -452,6 +517,7 @@ def main():
         "varlen": varlen,
         "layer": layer,
         "backward": backward,
+        "sparse": sparse,
     }
     print(json.dumps(line), flush=True)
 
