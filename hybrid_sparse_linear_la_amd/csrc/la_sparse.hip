@@ -15,7 +15,8 @@
 // la_sparse_means_kernel: block means of k (fp32), one workgroup per (block, h, b).
 // la_sparse_prefill_kernel: one 256-thread workgroup per (query block, h, b).
 //   1. selection: the query-block mean, its scores against the key means (16 lanes
-//      per key block), top-k by repeated block-wide argmax, sorted by block index;
+//      per key block), top-k (a threshold from the maxima of 64 residue classes,
+//      then exact ranks among the candidates above it), sorted by block index;
 //   2. attention, flash style over the own block (first: every query sees at least
 //      itself, so the running max is finite from the start) and then the selected
 //      blocks, K and V tiles double-buffered in LDS with the next block's global
@@ -89,78 +90,176 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_means_kernel(SparseP
   }
 }
 
-// Scores sc[j] = qm . kmean[j] for j < n: 16 lanes per key block (8 dims each).
-// qm is in LDS; every thread of the workgroup calls it.
+// Scores sc[j] = qm . kmean[j] for j < n: 16 lanes per key block (8 dims each),
+// four key blocks per lane group in flight.  qm is in LDS; every thread of the
+// workgroup calls it.
 __device__ __forceinline__ void block_scores(const float* qm, const float* kmean, int n, float* sc) {
   const int tid = threadIdx.x, grp = tid >> 4, c = tid & 15;
+  constexpr int kGroups = kSparseThreads / 16;
   float q8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) q8[e] = qm[8 * c + e];
-  for (int j = grp; j < n; j += kSparseThreads / 16) {
-    const float4 a = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c);
-    const float4 b = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c + 4);
-    float s = a.x * q8[0];
-    s = fmaf(a.y, q8[1], s);
-    s = fmaf(a.z, q8[2], s);
-    s = fmaf(a.w, q8[3], s);
-    s = fmaf(b.x, q8[4], s);
-    s = fmaf(b.y, q8[5], s);
-    s = fmaf(b.z, q8[6], s);
-    s = fmaf(b.w, q8[7], s);
-    s = row16_sum(s);  // the 16 lanes of a DPP row share j, so all of them are active here
-    if (c == 0) sc[j] = s;
+  for (int j0 = grp; j0 < n; j0 += 4 * kGroups) {
+    float4 a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = min(j0 + u * kGroups, n - 1);  // past n: a valid row, result unused
+      a[u] = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c);
+      b[u] = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float s = a[u].x * q8[0];
+      s = fmaf(a[u].y, q8[1], s);
+      s = fmaf(a[u].z, q8[2], s);
+      s = fmaf(a[u].w, q8[3], s);
+      s = fmaf(b[u].x, q8[4], s);
+      s = fmaf(b[u].y, q8[5], s);
+      s = fmaf(b[u].z, q8[6], s);
+      s = fmaf(b[u].w, q8[7], s);
+      s = row16_sum(s);  // the 16 lanes of a DPP row share j0, so all of them are active here
+      const int j = j0 + u * kGroups;
+      if (c == 0 && j < n) sc[j] = s;
+    }
   }
 }
 
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-// The min(topk, n) best of sc[0..n) (ties to the lower index) into list, sorted by
-// index; returns their number.  sc is consumed.  Every thread calls it; it ends on
-// a barrier.
-__device__ int select_topk(float* sc, int n, int topk, int* list, float* red_v, int* red_i) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// Scratch of select_topk in LDS.
+struct SelectScratch {
+  float gmax[kSparseThreads];  // per-thread best (score, index)
+  int gidx[kSparseThreads];
+  int count;                   // survivors
+  float thresh;                // the threshold candidate (score, index)
+  int thresh_idx;
+};
+
+__device__ __forceinline__ bool above(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// The min(topk, n) best of sc[0..n) (higher score first, ties to the lower index)
+// into list, sorted by index; returns their number.  For n > topk:
+//   1. the best candidate of each of the 64 residue classes j mod 64 (each class
+//      non-empty since n > topk and topk <= 64); the topk-th best of these,
+//      (M, jM), is reached by topk distinct candidates, so every chosen candidate
+//      ranks at or above it (wave 0 ranks the 64 class bests by reading one lane
+//      per step);
+//   2. the candidates at or above (M, jM) survive into surv as (score, index)
+//      pairs (order immaterial): with random scores a few dozen, with all scores
+//      equal exactly topk;
+//   3. with at most 64 survivors wave 0 holds one per lane and counts, reading one
+//      lane per step, each survivor's rank and, for the chosen ones, its place in
+//      index order; more survivors (a few classes holding most of the best scores)
+//      are ranked from LDS by all threads and then sorted.
+// surv holds 2 cap ints (cap pairs) and at least n ints.  Every thread calls it;
+// it ends on a barrier.
+__device__ int select_topk(const float* sc, int n, int topk, int* list, int* surv, int cap, SelectScratch* ss) {
+  const int tid = threadIdx.x, lane = tid & 63;
   if (n <= topk) {
     for (int x = tid; x < n; x += kSparseThreads) list[x] = x;
     __syncthreads();
     return n;
   }
-  for (int r = 0; r < topk; ++r) {
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int x = tid; x < n; x += kSparseThreads)
-      if (better(sc[x], x, bv, bi)) {
-        bv = sc[x];
-        bi = x;
-      }
+  float gm = -INFINITY;
+  int gi = INT_MAX;
+  for (int j = tid; j < n; j += kSparseThreads)
+    if (above(sc[j], j, gm, gi)) {
+      gm = sc[j];
+      gi = j;
+    }
+  ss->gmax[tid] = gm;
+  ss->gidx[tid] = gi;
+  if (tid == 0) ss->count = 0;
+  if (tid < topk) list[tid] = -1;  // slots left empty (non-finite scores) are skipped by the callers
+  __syncthreads();
+  if (tid < 64) {
+    float c = ss->gmax[tid];
+    int ci = ss->gidx[tid];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+    for (int q = 1; q < 4; ++q)
+      if (above(ss->gmax[tid + 64 * q], ss->gidx[tid + 64 * q], c, ci)) {
+        c = ss->gmax[tid + 64 * q];
+        ci = ss->gidx[tid + 64 * q];
+      }
+    int rank = 0;
+    for (int y = 0; y < 64; ++y) rank += above(lane_f(c, y), __builtin_amdgcn_readlane(ci, y), c, ci);
+    if (lane == 0) {
+      ss->thresh = -INFINITY;  // kept only if no class best ranks topk - 1 (non-finite scores)
+      ss->thresh_idx = INT_MAX;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (rank == topk - 1) {
+      ss->thresh = c;
+      ss->thresh_idx = ci;
+    }
+  }
+  __syncthreads();
+  const float M = ss->thresh;
+  const int jM = ss->thresh_idx;
+  for (int j = tid; j < n; j += kSparseThreads) {
+    const float v = sc[j];
+    if (v > M || (v == M && j <= jM)) {
+      const int x = atomicAdd(&ss->count, 1);
+      if (x < cap) {
+        surv[2 * x] = __float_as_int(v);
+        surv[2 * x + 1] = j;
       }
     }
-    if (lane == 0) {
-      red_v[w] = bv;
-      red_i[w] = bi;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float v0 = red_v[0];
-      int i0 = red_i[0];
-      for (int q = 1; q < kSparseThreads / 64; ++q)
-        if (better(red_v[q], red_i[q], v0, i0)) {
-          v0 = red_v[q];
-          i0 = red_i[q];
-        }
-      const bool ok = i0 >= 0 && i0 < n;  // no finite score left (non-finite inputs): leave the slot empty
-      list[r] = ok ? i0 : -1;
-      if (ok) sc[i0] = -INFINITY;
-    }
-    __syncthreads();
   }
-  if (tid == 0) {  // insertion sort by block index; empty slots (-1) go first and are skipped by callers
+  __syncthreads();
+  const int S = ss->count;
+  if (S <= 64) {
+    if (tid < 64) {
+      const bool mine = lane < S;
+      const float vx = mine ? __int_as_float(surv[2 * lane]) : -INFINITY;
+      const int jx = mine ? surv[2 * lane + 1] : INT_MAX;
+      int r = 0;
+      for (int y = 0; y < S; ++y) r += above(lane_f(vx, y), __builtin_amdgcn_readlane(jx, y), vx, jx);
+      const bool chosen = mine && r < topk;
+      int pos = 0;  // place among the chosen in index order
+      for (int y = 0; y < S; ++y) {
+        const int jy = __builtin_amdgcn_readlane(jx, y);
+        const int ry = __builtin_amdgcn_readlane(r, y);
+        pos += (ry < topk) && (jy < jx);
+      }
+      if (chosen) list[pos] = jx;
+    }
+    __syncthreads();
+    return topk;
+  }
+  if (S <= cap) {
+    for (int x = tid; x < S; x += kSparseThreads) {
+      const float vx = __int_as_float(surv[2 * x]);
+      const int jx = surv[2 * x + 1];
+      int r = 0;
+#pragma unroll 8
+      for (int y = 0; y < S; ++y) {
+        const int2 e = reinterpret_cast<const int2*>(surv)[y];
+        r += above(__int_as_float(e.x), e.y, vx, jx);
+      }
+      if (r < topk) list[r] = jx;
+    }
+  } else {
+    // more survivors than pairs fit: indices only, scores read back
+    if (tid == 0) ss->count = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += kSparseThreads)
+      if (sc[j] > M || (sc[j] == M && j <= jM)) surv[atomicAdd(&ss->count, 1)] = j;
+    __syncthreads();
+    for (int x = tid; x < S; x += kSparseThreads) {
+      const int jx = surv[x];
+      const float vx = sc[jx];
+      int r = 0;
+      for (int y = 0; y < S; ++y) r += above(sc[surv[y]], surv[y], vx, jx);
+      if (r < topk) list[r] = jx;
+    }
+  }
+  __syncthreads();
+  if (tid == 0)  // insertion sort by block index
     for (int a = 1; a < topk; ++a) {
       const int x = list[a];
       int y = a - 1;
@@ -170,7 +269,6 @@ __device__ int select_topk(float* sc, int n, int topk, int* list, float* red_v, 
       }
       list[y + 1] = x;
     }
-  }
   __syncthreads();
   return topk;
 }
@@ -192,9 +290,8 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_prefill_kernel(Spars
   __shared__ __attribute__((aligned(16))) uint8_t sKV[2][kKVStage];
   __shared__ float sQm[kD];
   __shared__ int sList[kSparseMaxTopk];
-  __shared__ float red_v[4];
-  __shared__ int red_i[4];
-  static_assert(kSparseMaxBlocks * 4 <= kKVStage, "scores must fit one tile stage");
+  __shared__ SelectScratch ss;
+  static_assert(kSparseMaxBlocks * 4 <= kKVStage, "scores and survivor indices must each fit one tile stage");
   static_assert(16 * kD * 4 <= kKVStage, "partial sums must fit one tile stage");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -210,7 +307,7 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_prefill_kernel(Spars
   // ---- selection
   int nlist;
   if (ncand <= p.topk) {
-    nlist = select_topk(nullptr, ncand, p.topk, sList, red_v, red_i);
+    nlist = select_topk(nullptr, ncand, p.topk, sList, nullptr, 0, &ss);
   } else {
     float* part = reinterpret_cast<float*>(sKV[1]);
     {
@@ -235,7 +332,7 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_prefill_kernel(Spars
     float* sc = reinterpret_cast<float*>(sKV[0]);
     block_scores(sQm, p.kmean + ((int64_t)b * p.H + h) * nkb * kD, ncand, sc);
     __syncthreads();
-    nlist = select_topk(sc, ncand, p.topk, sList, red_v, red_i);
+    nlist = select_topk(sc, ncand, p.topk, sList, reinterpret_cast<int*>(sKV[1]), kKVStage / 8, &ss);
   }
   if (p.sel != nullptr)
     for (int x = tid; x < p.topk; x += kSparseThreads) {
@@ -374,9 +471,10 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   __shared__ float sc[kSparseMaxBlocks];  // block scores, then the attention weights
   __shared__ float sQ[kD];
   __shared__ float part[16][kD];
+  __shared__ int surv[2 * kSparseMaxBlocks];
   __shared__ int sList[kSparseMaxTopk];
+  __shared__ SelectScratch ss;
   __shared__ float red_v[4];
-  __shared__ int red_i[4];
   static_assert((kSparseMaxTopk + 1) * kSB <= kSparseMaxBlocks, "weights must fit the score array");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -390,11 +488,11 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   __syncthreads();
   int nlist;
   if (ncand <= p.topk) {
-    nlist = select_topk(nullptr, ncand, p.topk, sList, red_v, red_i);
+    nlist = select_topk(nullptr, ncand, p.topk, sList, nullptr, 0, &ss);
   } else {
     block_scores(sQ, p.kmean + (int64_t)bh * (p.T / kSB) * kD, ncand, sc);
     __syncthreads();
-    nlist = select_topk(sc, ncand, p.topk, sList, red_v, red_i);
+    nlist = select_topk(sc, ncand, p.topk, sList, surv, kSparseMaxBlocks, &ss);
   }
   if (p.sel != nullptr)
     for (int x = tid; x < p.topk; x += kSparseThreads) {

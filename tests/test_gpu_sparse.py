@@ -156,6 +156,24 @@ def test_sparse_prefill_32k_sampled_heads(la):
               flush=True)
 
 
+def test_tied_scores_choose_the_lowest_blocks(la):
+    """Identical keys give every key block the same mean and every candidate the
+    same score: each query block must take the topk lowest blocks."""
+    B, T, H, topk = 1, 40 * BLK + 7, 2, 4
+    q, k, v, g = workloads.activations(B, T, H, D, 23, "cuda")
+    k = k[:, :1].expand(B, T, H, D).contiguous()
+    o, sel = la.sparse_prefill(q, k, v, g, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy()
+    for i in range(s.shape[2]):
+        want = list(range(min(i, topk))) + [-1] * (topk - min(i, topk))
+        assert list(s[0, 0, i]) == want and list(s[0, 1, i]) == want, (i, s[0, :, i])
+    f = [to_np32(x) for x in (q, k, v, g)]
+    o_ref, sel_ref, _ = oracle.sparse_forward(*f, block=BLK, topk=topk)
+    assert np.array_equal(sel_ref, s)
+    assert_o_close(to_np(o), o_ref, what="tied scores")
+
+
 def test_sparse_rejects_bad_arguments(la):
     q, k, v, g = workloads.activations(1, 100, 2, D, 3, "cuda")
     with pytest.raises(la.LAError):
