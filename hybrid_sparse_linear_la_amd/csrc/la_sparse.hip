@@ -91,24 +91,25 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_means_kernel(SparseP
 }
 
 // Scores sc[j] = qm . kmean[j] for j < n: 16 lanes per key block (8 dims each),
-// four key blocks per lane group in flight.  qm is in LDS; every thread of the
+// kInFlight key blocks per lane group in flight.  qm is in LDS; every thread of the
 // workgroup calls it.
+template <int kInFlight>
 __device__ __forceinline__ void block_scores(const float* qm, const float* kmean, int n, float* sc) {
   const int tid = threadIdx.x, grp = tid >> 4, c = tid & 15;
   constexpr int kGroups = kSparseThreads / 16;
   float q8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) q8[e] = qm[8 * c + e];
-  for (int j0 = grp; j0 < n; j0 += 4 * kGroups) {
-    float4 a[4], b[4];
+  for (int j0 = grp; j0 < n; j0 += kInFlight * kGroups) {
+    float4 a[kInFlight], b[kInFlight];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kInFlight; ++u) {
       const int j = min(j0 + u * kGroups, n - 1);  // past n: a valid row, result unused
       a[u] = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c);
       b[u] = *reinterpret_cast<const float4*>(kmean + (int64_t)j * kD + 8 * c + 4);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kInFlight; ++u) {
       float s = a[u].x * q8[0];
       s = fmaf(a[u].y, q8[1], s);
       s = fmaf(a[u].z, q8[2], s);
@@ -330,7 +331,7 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_prefill_kernel(Spars
     }
     __syncthreads();
     float* sc = reinterpret_cast<float*>(sKV[0]);
-    block_scores(sQm, p.kmean + ((int64_t)b * p.H + h) * nkb * kD, ncand, sc);
+    block_scores<4>(sQm, p.kmean + ((int64_t)b * p.H + h) * nkb * kD, ncand, sc);
     __syncthreads();
     nlist = select_topk(sc, ncand, p.topk, sList, reinterpret_cast<int*>(sKV[1]), kKVStage / 8, &ss);
   }
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   if (ncand <= p.topk) {
     nlist = select_topk(nullptr, ncand, p.topk, sList, nullptr, 0, &ss);
   } else {
-    block_scores(sQ, p.kmean + (int64_t)bh * (p.T / kSB) * kD, ncand, sc);
+    block_scores<8>(sQ, p.kmean + (int64_t)bh * (p.T / kSB) * kD, ncand, sc);
     __syncthreads();
     nlist = select_topk(sc, ncand, p.topk, sList, surv, kSparseMaxBlocks, &ss);
   }
@@ -519,12 +520,22 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
     float q8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) q8[e] = sQ[8 * c + e];
-    for (int n = grp; n < nk; n += kSparseThreads / 16) {
-      const int row = key_row(n);
-      float s = 0.f;
-      if (row >= 0) s = dot_bf16x8(*reinterpret_cast<const uint4*>(p.k + cbase + (int64_t)row * rs + 8 * c), q8);
-      s = row16_sum(s);
-      if (c == 0) sc[n] = row >= 0 ? s * cs : -INFINITY;
+    constexpr int kGroups = kSparseThreads / 16;
+    for (int n0 = grp; n0 < nk; n0 += 4 * kGroups) {  // four key rows per lane group in flight
+      uint4 u[4];
+      int row[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int n = n0 + x * kGroups;
+        row[x] = n < nk ? key_row(n) : -1;
+        u[x] = *reinterpret_cast<const uint4*>(p.k + cbase + (int64_t)max(row[x], 0) * rs + 8 * c);
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int n = n0 + x * kGroups;
+        const float s = row16_sum(dot_bf16x8(u[x], q8));
+        if (c == 0 && n < nk) sc[n] = row[x] >= 0 ? s * cs : -INFINITY;
+      }
     }
   }
   __syncthreads();
@@ -548,19 +559,28 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   {
     const int kg = tid >> 4, c = tid & 15;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int n = kg; n < nk; n += kSparseThreads / 16) {
-      const int row = key_row(n);
-      if (row < 0) continue;
-      const uint4 u = *reinterpret_cast<const uint4*>(p.v + cbase + (int64_t)row * rs + 8 * c);
-      const float pn = sc[n];
-      acc[0] = fmaf(pn, bf2f_lo(u.x), acc[0]);
-      acc[1] = fmaf(pn, bf2f_hi(u.x), acc[1]);
-      acc[2] = fmaf(pn, bf2f_lo(u.y), acc[2]);
-      acc[3] = fmaf(pn, bf2f_hi(u.y), acc[3]);
-      acc[4] = fmaf(pn, bf2f_lo(u.z), acc[4]);
-      acc[5] = fmaf(pn, bf2f_hi(u.z), acc[5]);
-      acc[6] = fmaf(pn, bf2f_lo(u.w), acc[6]);
-      acc[7] = fmaf(pn, bf2f_hi(u.w), acc[7]);
+    constexpr int kGroups = kSparseThreads / 16;
+    for (int n0 = kg; n0 < nk; n0 += 4 * kGroups) {  // four value rows per lane group in flight
+      uint4 u[4];
+      float pn[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int n = n0 + x * kGroups;
+        const int row = n < nk ? key_row(n) : -1;
+        u[x] = *reinterpret_cast<const uint4*>(p.v + cbase + (int64_t)max(row, 0) * rs + 8 * c);
+        pn[x] = row >= 0 ? sc[n] : 0.f;  // empty slots and rows past the list weigh nothing
+      }
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        acc[0] = fmaf(pn[x], bf2f_lo(u[x].x), acc[0]);
+        acc[1] = fmaf(pn[x], bf2f_hi(u[x].x), acc[1]);
+        acc[2] = fmaf(pn[x], bf2f_lo(u[x].y), acc[2]);
+        acc[3] = fmaf(pn[x], bf2f_hi(u[x].y), acc[3]);
+        acc[4] = fmaf(pn[x], bf2f_lo(u[x].z), acc[4]);
+        acc[5] = fmaf(pn[x], bf2f_hi(u[x].z), acc[5]);
+        acc[6] = fmaf(pn[x], bf2f_lo(u[x].w), acc[6]);
+        acc[7] = fmaf(pn[x], bf2f_hi(u[x].w), acc[7]);
+      }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) part[kg][8 * c + e] = acc[e];
