@@ -62,6 +62,72 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 x) {
   *reinterpret_cast<uint2*>(dst) = make_uint2(pack2(x[0], x[1]), pack2(x[2], x[3]));
 }
 
+// One row piece of the prologue backward.  x: the raw row's dims 4j..4j+3 and
+// 64+4j..64+4j+3 (xl, xh), y: the gradient of the rotated normalized row at the
+// same dims, w: the norm weights there, E: the row's rotations.  Rotating back
+// gives dn, then through RMSNorm (n = w x / r):
+//     dx_i = w_i dn_i / r - x_i (sum_j w_j x_j dn_j) / (D r^3),
+// the sums over the row's 16 lanes.  Returns dx and, for the weight gradient
+// (dw_i += dn_i x_i / r), dn and 1 / r.
+__device__ __forceinline__ void prologue_back_row(uint2 xl, uint2 xh, uint2 yl, uint2 yh, const float (&w)[8],
+                                                  const float2 (&E)[4], float eps, float (&dx)[8], float (&dn)[8],
+                                                  float (&x)[8], float& inv) {
+  const float xs[8] = {bf2f_lo(xl.x), bf2f_hi(xl.x), bf2f_lo(xl.y), bf2f_hi(xl.y),
+                       bf2f_lo(xh.x), bf2f_hi(xh.x), bf2f_lo(xh.y), bf2f_hi(xh.y)};
+  const float y[8] = {bf2f_lo(yl.x), bf2f_hi(yl.x), bf2f_lo(yl.y), bf2f_hi(yl.y),
+                      bf2f_lo(yh.x), bf2f_hi(yh.x), bf2f_lo(yh.y), bf2f_hi(yh.y)};
+  float ss = 0.f, dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    dn[e] = y[e] * E[e].x + y[4 + e] * E[e].y;
+    dn[4 + e] = y[4 + e] * E[e].x - y[e] * E[e].y;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = xs[e];
+    ss += xs[e] * xs[e];
+    dot += w[e] * xs[e] * dn[e];
+  }
+  ss = row16_sum(ss);
+  dot = row16_sum(dot);
+  inv = rsqrt_(ss * (1.0f / kD) + eps);
+  const float k3 = dot * inv * inv * inv * (1.0f / kD);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) dx[e] = w[e] * dn[e] * inv - xs[e] * k3;
+}
+
+__device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const float (&v)[8]) {
+  *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
+  *reinterpret_cast<uint2*>(dst + kHalf + 4 * j) = make_uint2(pack2(v[4], v[5]), pack2(v[6], v[7]));
+}
+
+// The prologue backward of one chunk inside the chunk kernel: thread (rg, j) takes
+// rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
+// (272-byte rows), q, k again from memory (cached since the chunk's staging).
+__device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
+                                                   int nv, int64_t rs, int rg, int j, const Rope& L, float2 (&E)[4],
+                                                   const uint8_t* sDq, const uint8_t* sDk) {
+  Rows<2> X[2];
+  load_rows<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
+  load_rows<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
+  float w[2][8];
+  load_norm_weights(p.qw, j, w[0]);
+  load_norm_weights(p.kw, j, w[1]);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (m > 0) next_rotation(L, E);
+    const int t = rg + 32 * m;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint8_t* Y = a ? sDk : sDq;
+      float dx[8], dn[8], x[8], inv;
+      prologue_back_row(X[a].lo[m], X[a].hi[m], lds_ld<uint2>(Y, tile_off(t, 4 * j)),
+                        lds_ld<uint2>(Y, tile_off(t, kHalf + 4 * j)), w[a], E, p.eps, dx, dn, x, inv);
+      if (t < nv) store_row_pieces((a ? bp.dk : bp.dq) + base + (int64_t)t * rs, j, dx);
+    }
+  }
+}
+
 // Stores row blocks rt = 0..3 (row 16 rt + n16 of the chunk, columns col..col+3) of
 // a bf16 output, rows at or past nv skipped.
 __device__ __forceinline__ void store_rows4(uint16_t* out, const f32x4 (&acc)[4], int64_t base, int t0,
@@ -71,7 +137,7 @@ __device__ __forceinline__ void store_rows4(uint16_t* out, const f32x4 (&acc)[4]
     if (16 * rt + n16 < nv) store_bf16x4(out + base + (int64_t)(t0 + 16 * rt + n16) * rs + col, acc[rt]);
 }
 
-template <bool kWeights>
+template <bool kWeights, bool kFuse>
 __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(BackwardParams bp) {
   const PrefillParams& p = bp.f;
   __shared__ __attribute__((aligned(16))) uint8_t sQ[kPiTileBytes];
@@ -203,6 +269,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     // ---- outputs of this wave's 16 columns.  Each output is formed for the four row
     // blocks at once: every A operand (S, G, S^T, G^T, or a column of V, Kh, dU, Qh)
     // is read once and feeds four independent accumulation chains.
+    uint2 dqp[4], dkp[4];  // fused: this lane's bf16 dqh, dkh (rows 16 rt + n16, 4 columns)
     {
       const int col = 16 * w + 4 * g4;
       // do and g of the lane's output rows (rows past the chunk clamped to its last row)
@@ -243,22 +310,6 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
           *reinterpret_cast<uint2*>(bp.dg + tl.base + (int64_t)(t0 + 16 * rt + n16) * rs + col) =
               make_uint2(pack2(dg[0], dg[1]), pack2(dg[2], dg[3]));
       }
-      // dQh = dU S^T + (dP Kh)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a = snap_col(sST, kk, 16 * w, g4, n16);
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sU, 16 * rt + n16, kk, g4), acc[rt]);
-      }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat<TilePi>(sK, kk, 16 * w, g4, n16);
-#pragma unroll
-        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sdP, 16 * rt + n16, kk, g4), acc[rt]);
-      }
-      store_rows4(bp.dqh, acc, tl.base, t0, rs, col, nv, n16);
       // dV = Kh G + (P^T dU)   (the row is the key token s here)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -275,6 +326,11 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
         for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sP, kk, 16 * rt, g4, n16), acc[rt]);
       }
       store_rows4(bp.dv, acc, tl.base, t0, rs, col, nv, n16);
+      // S before the next chunk: S += Kh^T V (dQh below reads S before the chunk from its snapshot)
+      bf16x8 Vf[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat<TilePi>(sV, kk, 16 * w, g4, n16);
+      accumulate_nat(Sacc, sK, Vf, g4, n16);
       // dKh = V G^T + (dP^T Qh)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -290,14 +346,53 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
 #pragma unroll
         for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sdP, kk, 16 * rt, g4, n16), acc[rt]);
       }
-      store_rows4(bp.dkh, acc, tl.base, t0, rs, col, nv, n16);
-      // S before the next chunk: S += Kh^T V
-      bf16x8 Vf[2];
+      if (kFuse) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat<TilePi>(sV, kk, 16 * w, g4, n16);
-      accumulate_nat(Sacc, sK, Vf, g4, n16);
+        for (int rt = 0; rt < 4; ++rt) dkp[rt] = make_uint2(pack2(acc[rt][0], acc[rt][1]), pack2(acc[rt][2], acc[rt][3]));
+      } else {
+        store_rows4(bp.dkh, acc, tl.base, t0, rs, col, nv, n16);
+      }
+      // dQh = dU S^T + (dP Kh)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8 a = snap_col(sST, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt] = mma(a, pi_row(sU, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8 a = col_nat<TilePi>(sK, kk, 16 * w, g4, n16);
+#pragma unroll
+        for (int rt = 2 * kk; rt < 4; ++rt) acc[rt] = mma(a, score_row(sdP, 16 * rt + n16, kk, g4), acc[rt]);
+      }
+      if (kFuse) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) dqp[rt] = make_uint2(pack2(acc[rt][0], acc[rt][1]), pack2(acc[rt][2], acc[rt][3]));
+      } else {
+        store_rows4(bp.dqh, acc, tl.base, t0, rs, col, nv, n16);
+      }
     }
     __syncthreads();
+    if (kFuse) {
+      // dqh, dkh of this chunk through LDS (the snapshot area is free now) into the
+      // staging layout, then rotated back and through the RMSNorm Jacobian
+      const int col = 16 * w + 4 * g4;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        lds_st<uint2>(sX, tile_off(16 * rt + n16, col), dqp[rt]);
+        lds_st<uint2>(sX + kSnapBytes, tile_off(16 * rt + n16, col), dkp[rt]);
+      }
+      __syncthreads();
+      float2 E[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
+      prologue_back_rows(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes);
+      // the next chunk's hi/lo tiles overwrite the area
+      const int t1 = t0 + kC;
+      if (c + 1 < tl.nch && t1 + 2 * kC > p.T) __syncthreads();
+    }
   }
 }
 
@@ -351,37 +446,12 @@ __global__ __launch_bounds__(kProThreads) void la_prologue_backward_kernel(Backw
       const int t = rg + 32 * m;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const uint2 xl = X[a].lo[m], xh = X[a].hi[m], yl = Y[a].lo[m], yh = Y[a].hi[m];
-        const float x[8] = {bf2f_lo(xl.x), bf2f_hi(xl.x), bf2f_lo(xl.y), bf2f_hi(xl.y),
-                            bf2f_lo(xh.x), bf2f_hi(xh.x), bf2f_lo(xh.y), bf2f_hi(xh.y)};
-        const float y[8] = {bf2f_lo(yl.x), bf2f_hi(yl.x), bf2f_lo(yl.y), bf2f_hi(yl.y),
-                            bf2f_lo(yh.x), bf2f_hi(yh.x), bf2f_lo(yh.y), bf2f_hi(yh.y)};
-        float dn[8], ss = 0.f, dot = 0.f;
+        float dx[8], dn[8], x[8], inv;
+        prologue_back_row(X[a].lo[m], X[a].hi[m], Y[a].lo[m], Y[a].hi[m], w[a], E, p.eps, dx, dn, x, inv);
+        if (kWeights && t < nv)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dn[e] = y[e] * E[e].x + y[4 + e] * E[e].y;
-          dn[4 + e] = y[4 + e] * E[e].x - y[e] * E[e].y;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          ss += x[e] * x[e];
-          dot += w[a][e] * x[e] * dn[e];
-        }
-        ss = row16_sum(ss);
-        dot = row16_sum(dot);
-        const float inv = rsqrt_(ss * (1.0f / kD) + p.eps);
-        const float k3 = dot * inv * inv * inv * (1.0f / kD);
-        float dx[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          dx[e] = w[a][e] * dn[e] * inv - x[e] * k3;
-          if (kWeights && t < nv) dw[a][e] += dn[e] * x[e] * inv;
-        }
-        if (t < nv) {
-          uint16_t* dst = (a ? bp.dk : bp.dq) + base + (int64_t)(t0 + t) * rs;
-          *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(pack2(dx[0], dx[1]), pack2(dx[2], dx[3]));
-          *reinterpret_cast<uint2*>(dst + kHalf + 4 * j) = make_uint2(pack2(dx[4], dx[5]), pack2(dx[6], dx[7]));
-        }
+          for (int e = 0; e < 8; ++e) dw[a][e] += dn[e] * x[e] * inv;
+        if (t < nv) store_row_pieces((a ? bp.dk : bp.dq) + base + (int64_t)(t0 + t) * rs, j, dx);
       }
     }
     __syncthreads();  // sRot is rewritten for the next chunk
@@ -420,10 +490,20 @@ hipError_t launch_backward_chunks(const BackwardParams& bp, const PrefillPlan& p
   // weight gradients without weights are taken at weights of one
   const bool weights = p.qw != nullptr || p.kw != nullptr || bp.dq_w != nullptr || bp.dk_w != nullptr;
   const dim3 grid((unsigned)(plan.nwork * p.H));
+  // without norm-weight gradients the prologue backward runs inside the chunk kernel
+  if (bp.dq_w == nullptr && bp.dk_w == nullptr) {
+    if (p.qw != nullptr || p.kw != nullptr)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<true, true>), grid, dim3(kBwdThreads), 0, stream, bp);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<false, true>), grid, dim3(kBwdThreads), 0, stream,
+                         bp);
+    return hipGetLastError();
+  }
   if (weights)
-    hipLaunchKernelGGL(la_backward_chunk_kernel<true>, grid, dim3(kBwdThreads), 0, stream, bp);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<true, false>), grid, dim3(kBwdThreads), 0, stream, bp);
   else
-    hipLaunchKernelGGL(la_backward_chunk_kernel<false>, grid, dim3(kBwdThreads), 0, stream, bp);
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<false, false>), grid, dim3(kBwdThreads), 0, stream,
+                       bp);
   const int64_t items = (int64_t)p.B * p.H * ((p.T + kC - 1) / kC);
   const int nblocks = (int)std::min<int64_t>(kPrologueBlocks, items);
   if (weights)
