@@ -104,9 +104,10 @@ __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const flo
 // The prologue backward of one chunk inside the chunk kernel: thread (rg, j) takes
 // rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
 // (272-byte rows), q, k again from memory (cached since the chunk's staging).
+// dw receives the thread's norm-weight gradient terms (its two rows summed).
 __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
                                                    int nv, int64_t rs, int rg, int j, const Rope& L, float2 (&E)[4],
-                                                   const uint8_t* sDq, const uint8_t* sDk) {
+                                                   const uint8_t* sDq, const uint8_t* sDk, float (&dw)[2][8]) {
   Rows<2> X[2];
   load_rows<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
   load_rows<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
@@ -123,6 +124,8 @@ __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const
       float dx[8], dn[8], x[8], inv;
       prologue_back_row(X[a].lo[m], X[a].hi[m], lds_ld<uint2>(Y, tile_off(t, 4 * j)),
                         lds_ld<uint2>(Y, tile_off(t, kHalf + 4 * j)), w[a], E, p.eps, dx, dn, x, inv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dw[a][e] = (m > 0 ? dw[a][e] : 0.f) + (t < nv ? dn[e] * x[e] * inv : 0.f);
       if (t < nv) store_row_pieces((a ? bp.dk : bp.dq) + base + (int64_t)t * rs, j, dx);
     }
   }
@@ -180,6 +183,8 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
         Gacc[rtk][r] = gst[state_elem(rtk, r, w, g4, n16)];
       }
   }
+  const bool wgrad = kFuse && (bp.dq_w != nullptr || bp.dk_w != nullptr);
+  float dw_acc = 0.f;  // with wgrad: thread tid < 256 sums dw[tid / 128][tid % 128] over the chunks
   // score tiles above the diagonal are never written
   for (int i = tid; i < kC * kScoreRowBytes / 16; i += kBwdThreads) {
     reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -388,12 +393,43 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       float2 E[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
-      prologue_back_rows(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes);
+      float dw[2][8];
+      prologue_back_rows(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, dw);
+      if (wgrad) {
+        // the wave's four row groups (lanes 16 apart) summed, then the 8 waves' parts in
+        // the unused middle of the area, summed in a fixed order into dw_acc
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float x = dw[a][e];
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            dw[a][e] = x;
+          }
+        // [8 waves][2][128] between the dqh tile (first 17 KiB) and the dkh tile
+        float* part = reinterpret_cast<float*>(sX + kTileBytes);
+        static_assert(kTileBytes + kWaves * 2 * kD * 4 <= kSnapBytes, "weight parts overlap the dkh tile");
+        if (lane < 16)
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[(w * 2 + a) * kD + (e < 4 ? 4 * j + e : kHalf + 4 * j + e - 4)] = dw[a][e];
+        __syncthreads();
+        if (tid < 2 * kD) {
+          float sum = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < kWaves; ++ww) sum += part[(ww * 2 + tid / kD) * kD + tid % kD];
+          dw_acc += sum;
+        }
+      }
       // the next chunk's hi/lo tiles overwrite the area
       const int t1 = t0 + kC;
       if (c + 1 < tl.nch && t1 + 2 * kC > p.T) __syncthreads();
     }
   }
+  if (kFuse && wgrad && tid < 2 * kD)
+    bp.wpart[((int64_t)(tid / kD) * kPrologueBlocks + blockIdx.x) * kD + tid % kD] = dw_acc;
 }
 
 // dq, dk from the gradients of the rotated, normalized rows (dqh, dkh): rotating
@@ -490,13 +526,16 @@ hipError_t launch_backward_chunks(const BackwardParams& bp, const PrefillPlan& p
   // weight gradients without weights are taken at weights of one
   const bool weights = p.qw != nullptr || p.kw != nullptr || bp.dq_w != nullptr || bp.dk_w != nullptr;
   const dim3 grid((unsigned)(plan.nwork * p.H));
-  // without norm-weight gradients the prologue backward runs inside the chunk kernel
-  if (bp.dq_w == nullptr && bp.dk_w == nullptr) {
-    if (p.qw != nullptr || p.kw != nullptr)
+  // the prologue backward runs inside the chunk kernel (its norm-weight gradient parts,
+  // one per workgroup, summed after) unless there are more workgroups than parts
+  if (grid.x <= (unsigned)kPrologueBlocks) {
+    if (weights)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<true, true>), grid, dim3(kBwdThreads), 0, stream, bp);
     else
       hipLaunchKernelGGL(HIP_KERNEL_NAME(la_backward_chunk_kernel<false, true>), grid, dim3(kBwdThreads), 0, stream,
                          bp);
+    if (bp.dq_w != nullptr || bp.dk_w != nullptr)
+      hipLaunchKernelGGL(la_weight_grad_kernel, dim3(1), dim3(256), 0, stream, bp, (int)grid.x);
     return hipGetLastError();
   }
   if (weights)

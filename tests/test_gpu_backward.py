@@ -98,14 +98,25 @@ def test_backward_rejects_bad_arguments(la):
         la.backward(q, k, v, g, d_o[:, :32].contiguous())
 
 
+def test_backward_with_more_workgroups_than_weight_parts(la):
+    """More (b, h, segment) workgroups than per-workgroup weight-gradient parts
+    (2048): the prologue backward runs in its own kernel."""
+    B, T, H = 17, 100, 128
+    print(f"backward case B={B} T={T} H={H} (separate prologue kernel)", flush=True)
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 93, 0.1, 0.1, True)
+    grads = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, pos0=11, q_norm_w=qw, k_norm_w=kw,
+                        weight_grads=True)
+    torch.cuda.synchronize()
+    _check(grads, q, k, v, g, d_o, S_in, dS_out, 11, qw, kw, True)
+
+
 @pytest.mark.parametrize("weights", [False, True])
-def test_fused_and_separate_prologue_backward_agree(la, weights):
-    """Without norm-weight gradients the prologue backward runs inside the chunk
-    kernel; with them, in its own kernel.  Both round dqh, dkh to bf16 at the same
-    point and share the row arithmetic; the compiler may contract it into fused
-    multiply-adds differently in the two kernels, so a rare element lands one bf16
-    step away: per row the two agree to one bf16 step (2^-8), and few elements
-    differ at all."""
+def test_backward_with_and_without_weight_gradients_agree(la, weights):
+    """Asking for the norm-weight gradients changes how the chunk kernel is
+    compiled (norm weights of one are then applied explicitly), not what it
+    computes; the compiler may contract the row arithmetic into fused multiply-adds
+    differently, so a rare element lands one bf16 step away: per row the two agree
+    to one bf16 step (2^-8), and few elements differ at all."""
     B, T, H = 2, 3000, 4
     q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 91, 0.1, 0.2, weights)
     fused = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, pos0=77, q_norm_w=qw, k_norm_w=kw)
