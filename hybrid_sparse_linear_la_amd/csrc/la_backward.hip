@@ -96,6 +96,20 @@ __device__ __forceinline__ void prologue_back_row(uint2 xl, uint2 xh, uint2 yl, 
   for (int e = 0; e < 8; ++e) dx[e] = w[e] * dn[e] * inv - xs[e] * k3;
 }
 
+// Norm weights of dims 4j..4j+3 and 64+4j..64+4j+3 from an LDS copy.
+__device__ __forceinline__ void lds_norm_weights(const float* w, int j, float (&out)[8]) {
+  const float4 lo = *reinterpret_cast<const float4*>(w + 4 * j);
+  const float4 hi = *reinterpret_cast<const float4*>(w + kHalf + 4 * j);
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = lo.z;
+  out[3] = lo.w;
+  out[4] = hi.x;
+  out[5] = hi.y;
+  out[6] = hi.z;
+  out[7] = hi.w;
+}
+
 __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const float (&v)[8]) {
   *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
   *reinterpret_cast<uint2*>(dst + kHalf + 4 * j) = make_uint2(pack2(v[4], v[5]), pack2(v[6], v[7]));
@@ -105,15 +119,23 @@ __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const flo
 // rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
 // (272-byte rows), q, k again from memory (cached since the chunk's staging).
 // dw receives the thread's norm-weight gradient terms (its two rows summed).
+template <bool kWeights>
 __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
                                                    int nv, int64_t rs, int rg, int j, const Rope& L, float2 (&E)[4],
-                                                   const uint8_t* sDq, const uint8_t* sDk, float (&dw)[2][8]) {
+                                                   const uint8_t* sDq, const uint8_t* sDk, const float (*sNW)[kD],
+                                                   float (&dw)[2][8]) {
   Rows<2> X[2];
   load_rows<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
   load_rows<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
   float w[2][8];
-  load_norm_weights(p.qw, j, w[0]);
-  load_norm_weights(p.kw, j, w[1]);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    if (kWeights) {
+      lds_norm_weights(sNW[a], j, w[a]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[a][e] = 1.0f;
+    }
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     if (m > 0) next_rotation(L, E);
@@ -152,6 +174,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   // S^T and G^T snapshots; during the scores of an exact chunk the lo tiles of qh,
   // kh and du live here instead
   __shared__ __attribute__((aligned(16))) uint8_t sX[2 * kSnapBytes];
+  __shared__ __attribute__((aligned(16))) float sNW[2][kD];  // norm weights of q and k (ones if absent)
   uint8_t* const sST = sX;
   uint8_t* const sGT = sX + kSnapBytes;
   uint8_t* const sQl = sX;
@@ -183,6 +206,10 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
         Gacc[rtk][r] = gst[state_elem(rtk, r, w, g4, n16)];
       }
   }
+  if (tid < 2 * kD) {
+    const float* nw = tid < kD ? p.qw : p.kw;
+    sNW[tid / kD][tid % kD] = nw ? nw[tid % kD] : 1.0f;
+  }
   const bool wgrad = kFuse && (bp.dq_w != nullptr || bp.dk_w != nullptr);
   float dw_acc = 0.f;  // with wgrad: thread tid < 256 sums dw[tid / 128][tid % 128] over the chunks
   // score tiles above the diagonal are never written
@@ -190,6 +217,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
     reinterpret_cast<uint4*>(sdP)[i] = make_uint4(0u, 0u, 0u, 0u);
   }
+  __syncthreads();  // the norm weights in LDS before the first staging
 
   for (int c = 0; c < tl.nch; ++c) {
     const int t0 = tl.t_begin + c * kC;
@@ -208,11 +236,11 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
       float2 E2[4] = {E[0], E[1], E[2], E[3]};
-      // norm weights are re-read each chunk (from cache) rather than held in registers
+      // norm weights are re-read each chunk (from LDS) rather than held in registers
       float wq[8], wk[8];
       if (kWeights) {
-        load_norm_weights(p.qw, j, wq);
-        load_norm_weights(p.kw, j, wk);
+        lds_norm_weights(sNW[0], j, wq);
+        lds_norm_weights(sNW[1], j, wk);
       }
       norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
       norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
@@ -394,7 +422,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
       float dw[2][8];
-      prologue_back_rows(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, dw);
+      prologue_back_rows<kWeights>(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, sNW, dw);
       if (wgrad) {
         // the wave's four row groups (lanes 16 apart) summed, then the 8 waves' parts in
         // the unused middle of the area, summed in a fixed order into dw_acc
