@@ -445,6 +445,45 @@ def bench_sparse(la, torch, workloads, hip, steps=5):
     return {"prefill": prefill, "decode": decode}
 
 
+def bench_stream(la, torch, workloads, hip, steps=3):
+    """The 1M-token streamed prefill: 16 calls of 65536 tokens with the state carried
+    in place (pos0 = 65536 s), and the same tokens in one call."""
+    w = workloads.STREAM_1M
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, w.D, w.seed, "cuda")
+    seg = w.T // w.segments
+    S = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    ws = torch.empty(max(la.prefill_workspace_bytes(w.B, seg, w.H), la.prefill_workspace_bytes(w.B, w.T, w.H)),
+                     dtype=torch.uint8, device="cuda")
+
+    def streamed():
+        for s in range(w.segments):
+            sl = slice(s * seg, (s + 1) * seg)
+            la.prefill(q[:, sl], k[:, sl], v[:, sl], g[:, sl], S_in=S if s else None, S_out=S, pos0=s * seg,
+                       out=o[:, sl], workspace=ws)
+
+    def single():
+        la.prefill(q, k, v, g, S_out=S, out=o, workspace=ws)
+
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"workload": w.name, "segments": w.segments, "steps": steps}
+    for name, fn in (("streamed", streamed), ("single_shot", single)):
+        fn()
+        e = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(e[0], stream)
+        for _ in range(steps):
+            fn()
+        hip.record(e[1], stream)
+        ms = hip.ms(e[0], e[1]) / steps
+        hip.destroy(e)
+        out[name] = {"ms": round(ms, 3), "tokens_per_s": round(w.B * w.T / (ms / 1e3), 1)}
+    comp = 1280 * w.B * w.T * w.H
+    out["hbm_roof_ms"] = round(comp / (HBM_PEAK_GBS * 1e9) * 1e3, 4)
+    del q, k, v, g, o, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +499,8 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the layer forward with its projections")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward of the 256K prefill")
     ap.add_argument("--no-sparse", action="store_true", help="skip the sparse layer (32K prefill, 128K decode)")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the 1M-token prefill (16 carried calls of 65536, and one call)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -494,6 +535,7 @@ def main():
     layer = None if args.no_layer else bench_layer(la, torch, workloads, hip, args)
     backward = None if args.no_backward else bench_backward(la, torch, workloads, hip, tensors)
     sparse = None if args.no_sparse else bench_sparse(la, torch, workloads, hip)
+    stream_1m = None if args.no_stream else bench_stream(la, torch, workloads, hip)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
@@ -518,6 +560,7 @@ def main():
         "layer": layer,
         "backward": backward,
         "sparse": sparse,
+        "stream_1m": stream_1m,
     }
     print(json.dumps(line), flush=True)
 
