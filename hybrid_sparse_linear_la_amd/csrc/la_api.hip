@@ -17,8 +17,16 @@ namespace la {
 namespace {
 
 constexpr int kDefaultChunk = 64;
-// Workgroups a prefill launch aims for: a multiple of the 256 compute units, so
-// the chunk-walking workgroups fill the chip in whole rounds.
+// Segment planning. The chunk-walking kernels run one workgroup per compute unit,
+// and each workgroup pays a pipeline fill and a state hand-off per segment. One
+// round of 256 workgroups is used while its segments stay within
+// kLongSegmentChunks 64-token chunks; longer inputs are cut into segments of that
+// length, up to kTargetWorkgroups workgroups (whole rounds), beyond which the
+// segments grow instead. Measured on the 32-head layer: 32K and 64K tokens run
+// about 9% faster in one round than in four, 128K-1M are as fast as or faster
+// than with any other round count tried.
+constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kLongSegmentChunks = 128;
 constexpr int64_t kTargetWorkgroups = 1024;
 // Launch-size limits (grid.x * block.x must stay below 2^32 work-items).
 constexpr int64_t kMaxWorkgroups = (int64_t)1 << 23;
@@ -51,6 +59,14 @@ bool finite_positive(float x) { return isfinite(x) && x > 0.0f; }
 
 }  // namespace
 
+// 64-token chunks per segment for `work` (sequence, head, chunk) items, a multiple of sub.
+static int64_t segment_chunks(int64_t work, int64_t sub) {
+  const int64_t one_round = (work + kComputeUnits - 1) / kComputeUnits;
+  const int64_t at_target = (work + kTargetWorkgroups - 1) / kTargetWorkgroups;
+  const int64_t cps = std::max(at_target, std::min(one_round, kLongSegmentChunks));
+  return std::max<int64_t>(sub, (cps + sub - 1) / sub * sub);
+}
+
 bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   if (B < 1 || T < 1 || H < 1) return false;
   const int C = chunk == 0 ? kDefaultChunk : chunk;
@@ -59,9 +75,7 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   const int64_t sub = C / 64;
   const int64_t bh = (int64_t)B * H;
   const int64_t nchunks = ((int64_t)T + 63) / 64;
-  int64_t cps = (bh * nchunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  cps = (cps + sub - 1) / sub * sub;
-  if (cps < sub) cps = sub;
+  int64_t cps = segment_chunks(bh * nchunks, sub);
   if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
   if (bh * nseg > kMaxWorkgroups || bh > kMaxHeads) return false;
@@ -99,8 +113,7 @@ la_status plan_varlen(int nseq, const int32_t* cu, const int64_t* pos0, int H, i
     if (len >= 2) sub_chunks += (len + 63) / 64;
   }
   const int64_t sub = C / 64;
-  int64_t cps = ((int64_t)H * sub_chunks + kTargetWorkgroups - 1) / kTargetWorkgroups;
-  cps = std::max<int64_t>(sub, (cps + sub - 1) / sub * sub);
+  const int64_t cps = segment_chunks((int64_t)H * sub_chunks, sub);
   vp->segs.clear();
   vp->seqs.assign(nseq, SeqDesc{0, 0, 0, 0});
   vp->decs.clear();

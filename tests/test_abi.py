@@ -45,9 +45,16 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    # one fp32 128x128 state per (b, h, segment); segments target ~1024 workgroups
-    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 0) == 32 * 32 * 128 * 128 * 4
-    assert lib.la_prefill_workspace_bytes(1, 32768, 32, 128, 64) == 32 * 32 * 128 * 128 * 4
+    # one fp32 128x128 state per (b, h, segment). One round of 256 workgroups while
+    # segments stay within 128 chunks of 64; then 128-chunk segments up to 1024
+    # workgroups; then longer segments.
+    st = 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 0) == 32 * 32 * st
+    assert lib.la_prefill_workspace_bytes(1, 32768, 32, 128, 64) == 32 * 8 * st     # 64-chunk segments
+    assert lib.la_prefill_workspace_bytes(1, 65536, 32, 128, 0) == 32 * 8 * st      # 128-chunk segments
+    assert lib.la_prefill_workspace_bytes(1, 131072, 32, 128, 0) == 32 * 16 * st    # 512 workgroups
+    assert lib.la_prefill_workspace_bytes(1, 1 << 20, 32, 128, 0) == 32 * 32 * st   # 512-chunk segments
+    assert lib.la_prefill_workspace_bytes(4, 8192, 32, 128, 0) == 128 * 2 * st
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 0) == 2 * 5 * 128 * 128 * 4
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 64, 0) == 0
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 96) == 0
