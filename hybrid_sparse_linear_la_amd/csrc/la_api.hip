@@ -592,7 +592,8 @@ size_t la_sparse_prefill_workspace_bytes(int B, int T, int H, int D, int block, 
   la_status st;
   if (!sparse_shape_ok(B, T, H, D, block, topk, &st)) return 0;
   const size_t means = (size_t)B * H * (T / kSparseBlock) * D * sizeof(float);
-  return round_up(means > 0 ? means : 1, 256);
+  const size_t choice = (size_t)B * H * ((T + kSparseBlock - 1) / kSparseBlock) * topk * sizeof(int32_t);
+  return round_up(means > 0 ? means : 1, 256) + round_up(choice, 256);
 }
 
 la_status la_sparse_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
@@ -602,7 +603,7 @@ la_status la_sparse_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v
   la_status st;
   if (!sparse_shape_ok(B, T, H, D, block, topk, &st)) return st;
   const int64_t nqb = (T + kSparseBlock - 1) / kSparseBlock;
-  if (nqb * H * B >= ((int64_t)1 << 31)) return LA_ERR_BAD_SHAPE;
+  if (nqb * H * B >= ((int64_t)1 << 31) - 8) return LA_ERR_BAD_SHAPE;  // work items, rounded up to 8 in int
   const void* ptrs[] = {q, k, v, gate_logits, o, sel, workspace};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
@@ -623,12 +624,17 @@ la_status la_sparse_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v
   p.g = gate_logits;
   p.o = o;
   p.kmean = static_cast<float*>(workspace);
-  p.sel = sel;
+  p.sel = nullptr;
   p.B = B;
   p.T = T;
   p.H = H;
   p.topk = topk;
-  return launch_sparse_prefill(p, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
+  // the block choice goes to sel when given, else to the workspace after the means
+  const size_t means = (size_t)B * H * (T / kSparseBlock) * D * sizeof(float);
+  int32_t* choice = sel ? sel
+                        : reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                                     round_up(means > 0 ? means : 1, 256));
+  return launch_sparse_prefill(p, choice, static_cast<hipStream_t>(stream)) == hipSuccess ? LA_OK : LA_ERR_HIP;
 }
 
 la_status la_sparse_block_means(const la_bf16* k_cache, float* means, int B, int Tmax, int H, int D, int block,

@@ -145,14 +145,16 @@ struct SparseParams {
   const uint16_t* g;   // shaped as q
   uint16_t* o;         // shaped as q
   float* kmean;        // [B][H][T / kSparseBlock][D] fp32 block means of k
-  int32_t* sel;        // prefill [B][H][nqb][topk], decode [B][H][topk], or nullptr
+  int32_t* sel;        // decode: [B][H][topk] output, or nullptr
   const int32_t* lens; // decode: valid tokens per sequence (the query is the last)
   int B, T, H, topk;
 };
 
 // Means of key blocks [first, first + nblocks) of every (b, h) of p.k into p.kmean.
 hipError_t launch_sparse_means(const SparseParams& p, int first, int nblocks, hipStream_t stream);
-hipError_t launch_sparse_prefill(const SparseParams& p, hipStream_t stream);
+// Key means, the block choice of every query block into sel ([B][H][nqb][topk]),
+// then the attention.
+hipError_t launch_sparse_prefill(const SparseParams& p, int32_t* sel, hipStream_t stream);
 hipError_t launch_sparse_decode(const SparseParams& p, hipStream_t stream);
 
 }  // namespace la

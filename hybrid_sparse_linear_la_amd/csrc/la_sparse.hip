@@ -13,19 +13,15 @@
 // With no more than topk earlier blocks this is dense causal attention.
 //
 // la_sparse_means_kernel: block means of k (fp32), one workgroup per (block, h, b).
-// la_sparse_prefill_kernel: one 256-thread workgroup per (query block, h, b).
-//   1. selection: the query-block mean, its scores against the key means (16 lanes
-//      per key block), top-k (a threshold from the maxima of 64 residue classes,
-//      then exact ranks among the candidates above it), sorted by block index;
-//   2. attention, flash style over the own block (first: every query sees at least
-//      itself, so the running max is finite from the start) and then the selected
-//      blocks, K and V tiles double-buffered in LDS with the next block's global
-//      loads in flight.  Wave w owns queries 16w .. 16w + 15.  Per key block:
-//      S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (lane holds 4 keys of one query),
-//      running max over the block's keys (two lane swaps across the 4 lane groups),
-//      P^T rounded to bf16 straight from the accumulators is the B operand of
-//      O^T += V^T P^T in the key order pi (V^T read transposed from LDS), so P never
-//      goes through LDS.
+// la_sparse_select_kernel: one wave per (query block, h, b): the query-block mean,
+//   its scores against the key means (16 lanes per key block), top-k (a threshold
+//   from the maxima of 64 residue classes, then exact ranks among the candidates
+//   above it), written in increasing block order.
+// la_sparse_attn_kernel: one wave per (query block, h, b), all 64 queries, flash
+//   style over the own block and the chosen blocks: S^T = K Q^T on
+//   v_mfma_f32_16x16x32_bf16 with K and Q in operand registers, P^T rounded to bf16
+//   straight from the accumulators as the B operand of O^T += V^T P^T (V^T read
+//   transposed from LDS), softmax against a per-query reference without rescaling.
 // la_sparse_decode_kernel: one workgroup per (b, h): scores, top-k, then the
 //   attention of the single query over the chosen tokens (16 lanes per key row).
 #include <limits.h>
@@ -39,10 +35,7 @@ namespace {
 
 constexpr int kSB = kSparseBlock;
 constexpr int kSparseThreads = 256;
-constexpr int kKRow = kD * 2 + 32;       // 288-byte K rows: the 16-byte row reads meet no bank conflicts
-constexpr int kKTile = kSB * kKRow;
 constexpr int kVTile = kSB * kRowBytes;  // 272-byte V rows, read transposed
-constexpr int kKVStage = kKTile + kVTile;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], uint4 u) {
@@ -285,184 +278,402 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-__global__ __launch_bounds__(kSparseThreads) void la_sparse_prefill_kernel(SparseParams p) {
-  // K/V tile stages; during the selection the first stage holds the scores and the
-  // second the partial sums of the query mean
-  __shared__ __attribute__((aligned(16))) uint8_t sKV[2][kKVStage];
-  __shared__ float sQm[kD];
-  __shared__ int sList[kSparseMaxTopk];
-  __shared__ SelectScratch ss;
-  static_assert(kSparseMaxBlocks * 4 <= kKVStage, "scores and survivor indices must each fit one tile stage");
-  static_assert(16 * kD * 4 <= kKVStage, "partial sums must fit one tile stage");
+// Work item of a workgroup when a launch hands its workgroups to the 8 XCDs in
+// turn (workgroup w to XCD w mod 8): XCD x takes the contiguous items
+// [x c, x c + c), c = ceil(n / 8), in order, so the workgroups sharing an XCD (and
+// its L2) work on the same head and reuse its most chosen key blocks.  The grid
+// has 8 c workgroups; items from n on do nothing.
+__device__ __forceinline__ int xcd_item(int n) {
+  const int c = (n + 7) / 8;
+  return (int)(blockIdx.x % 8) * c + (int)(blockIdx.x / 8);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
+// ---- prefill, selection: one wave per (query block, h, b).  The query-block mean
+// (16 lanes x 8 dims per row, 4 rows per step), its scores against the key means
+// (16 lanes per key block, kSelInFlight blocks per lane group in flight) into LDS,
+// then the top-k in one wave: the best of each of the 64 residue classes j mod 64,
+// the topk-th best of those as a threshold (reached by topk distinct candidates,
+// so every chosen block ranks at or above it), the candidates at or above it as
+// survivors, and exact ranks among them.  Writes the chosen blocks in increasing
+// order, then -1, to sel.  Dynamic LDS: scores (4 B) and survivor indices (2 B)
+// per key block.
+constexpr int kSelInFlight = 8;
+
+__global__ __launch_bounds__(64) void la_sparse_select_kernel(SparseParams p, int32_t* sel) {
+  extern __shared__ __attribute__((aligned(16))) float sel_lds[];
+  __shared__ int sTop[kSparseMaxTopk];
+  const int lane = threadIdx.x;
   const int nqb = (p.T + kSB - 1) / kSB, nkb = p.T / kSB;
-  const int i = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb, h = bh % p.H, b = bh / p.H;
+  const int item = xcd_item(nqb * p.H * p.B);
+  if (item >= nqb * p.H * p.B) return;
+  const int i = item % nqb;
+  const int bh = item / nqb, h = bh % p.H, b = bh / p.H;
+  const int n = min(i, nkb);
+  const int topk = p.topk;
+  int32_t* out = sel + ((int64_t)bh * nqb + i) * topk;
+  if (n <= topk) {
+    if (lane < topk) out[lane] = lane < n ? lane : -1;
+    return;
+  }
   const int64_t rs = (int64_t)p.H * kD;
   const int64_t base = (int64_t)b * p.T * rs + (int64_t)h * kD;
   const int r0 = i * kSB, nv = min(kSB, p.T - r0);
-  const int ncand = min(i, nkb);
+  const int c = lane & 15, rg = lane >> 4;
 
-  // ---- selection
-  int nlist;
-  if (ncand <= p.topk) {
-    nlist = select_topk(nullptr, ncand, p.topk, sList, nullptr, 0, &ss);
-  } else {
-    float* part = reinterpret_cast<float*>(sKV[1]);
-    {
-      const int rp = tid >> 4, c = tid & 15;
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int r = rp + 16 * m;
-        if (r < nv) add_bf16x8(acc, *reinterpret_cast<const uint4*>(p.q + base + (int64_t)(r0 + r) * rs + 8 * c));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part[rp * kD + 8 * c + e] = acc[e];
-    }
-    __syncthreads();
-    if (tid < kD) {
-      float s = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s += part[r * kD + tid];
-      sQm[tid] = s / (float)nv;
-    }
-    __syncthreads();
-    float* sc = reinterpret_cast<float*>(sKV[0]);
-    block_scores<4>(sQm, p.kmean + ((int64_t)b * p.H + h) * nkb * kD, ncand, sc);
-    __syncthreads();
-    nlist = select_topk(sc, ncand, p.topk, sList, reinterpret_cast<int*>(sKV[1]), kKVStage / 8, &ss);
-  }
-  if (p.sel != nullptr)
-    for (int x = tid; x < p.topk; x += kSparseThreads) {
-      // the chosen blocks in increasing order, then -1
-      int cnt = 0, val = -1;
-      for (int y = 0; y < nlist; ++y)
-        if (sList[y] >= 0) {
-          if (cnt == x) val = sList[y];
-          ++cnt;
-        }
-      p.sel[((int64_t)bh * nqb + i) * p.topk + x] = val;
-    }
-
-  // ---- attention: own block first, then the chosen blocks
-  const int nblk = 1 + nlist;
-  auto block_row0 = [&](int n) { return n == 0 ? r0 : sList[n - 1] * kSB; };
-  const int lr = tid >> 2, lq = tid & 3;  // loader: row lr, bytes 64 lq .. 64 lq + 63 of K and of V
-  uint4 rk[4], rv[4];
-  auto load_block = [&](int n) {
-    const int64_t row = min(block_row0(n) + lr, p.T - 1);
-    const uint16_t* ks = p.k + base + row * rs + 32 * lq;
-    const uint16_t* vs = p.v + base + row * rs + 32 * lq;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      rk[u] = *reinterpret_cast<const uint4*>(ks + 8 * u);
-      rv[u] = *reinterpret_cast<const uint4*>(vs + 8 * u);
-    }
-  };
-  auto store_block = [&](int buf) {
-    uint8_t* K = sKV[buf];
-    uint8_t* V = sKV[buf] + kKTile;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      lds_st<uint4>(K, lr * kKRow + 64 * lq + 16 * u, rk[u]);
-      lds_st<uint4>(V, lr * kRowBytes + 64 * lq + 16 * u, rv[u]);
-    }
-  };
-  // skip empty slots (only possible with non-finite scores)
-  auto next_valid = [&](int n) {
-    while (n < nblk && n > 0 && sList[n - 1] < 0) ++n;
-    return n;
-  };
-
-  const int qr = 16 * w + n16;  // this lane's query row in the block
-  bf16x8 Qf[4];
+  float qm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   {
-    const int64_t row = min(r0 + qr, p.T - 1);
+    uint4 x[16];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      Qf[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(p.q + base + row * rs + 32 * ks + 8 * g4));
+    for (int m = 0; m < 16; ++m) {
+      const int r = rg + 4 * m;
+      x[m] = r < nv ? *reinterpret_cast<const uint4*>(p.q + base + (int64_t)(r0 + r) * rs + 8 * c)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) add_bf16x8(qm, x[m]);
   }
-  f32x4 O[8];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) O[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int e = 0; e < 8; ++e) {
+    qm[e] += __shfl_xor(qm[e], 16);
+    qm[e] += __shfl_xor(qm[e], 32);
+    qm[e] /= (float)nv;
+  }
+
+  float* sc = sel_lds;
+  uint16_t* surv = reinterpret_cast<uint16_t*>(sel_lds + nkb);
+  const float* km = p.kmean + (int64_t)bh * nkb * kD + 8 * c;
+  for (int j0 = rg; j0 < n; j0 += 4 * kSelInFlight) {
+    float4 a[kSelInFlight], a2[kSelInFlight];
+#pragma unroll
+    for (int u = 0; u < kSelInFlight; ++u) {
+      const int j = min(j0 + 4 * u, n - 1);  // past n: a valid row, result unused
+      a[u] = *reinterpret_cast<const float4*>(km + (int64_t)j * kD);
+      a2[u] = *reinterpret_cast<const float4*>(km + (int64_t)j * kD + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kSelInFlight; ++u) {
+      float s = a[u].x * qm[0];
+      s = fmaf(a[u].y, qm[1], s);
+      s = fmaf(a[u].z, qm[2], s);
+      s = fmaf(a[u].w, qm[3], s);
+      s = fmaf(a2[u].x, qm[4], s);
+      s = fmaf(a2[u].y, qm[5], s);
+      s = fmaf(a2[u].z, qm[6], s);
+      s = fmaf(a2[u].w, qm[7], s);
+      s = row16_sum(s);  // the 16 lanes of a DPP row share j0, so all of them are active here
+      const int j = j0 + 4 * u;
+      if (c == 0 && j < n) sc[j] = s;
+    }
+  }
+  __syncthreads();
+
+  // threshold: the class best of rank topk - 1 (kept at -inf if none has it: non-finite scores)
+  float gm = -INFINITY;
+  int gi = INT_MAX;
+  for (int j = lane; j < n; j += 64) {
+    const float v = sc[j];
+    if (above(v, j, gm, gi)) {
+      gm = v;
+      gi = j;
+    }
+  }
+  int rank = 0;
+  for (int y = 0; y < 64; ++y) rank += above(lane_f(gm, y), __builtin_amdgcn_readlane(gi, y), gm, gi);
+  const uint64_t at = __ballot(rank == topk - 1);
+  float M = -INFINITY;
+  int jM = INT_MAX;
+  if (at != 0) {
+    const int l = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)at) - 1);
+    M = lane_f(gm, l);
+    jM = __builtin_amdgcn_readlane(gi, l);
+  }
+  // survivors, packed by a prefix sum of the per-lane counts
+  int cnt = 0;
+  for (int j = lane; j < n; j += 64) {
+    const float v = sc[j];
+    cnt += (v > M || (v == M && j <= jM)) ? 1 : 0;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  const int S = __shfl(incl, 63);
+  int pos = incl - cnt;
+  for (int j = lane; j < n; j += 64) {
+    const float v = sc[j];
+    if (v > M || (v == M && j <= jM)) surv[pos++] = (uint16_t)j;
+  }
+  __syncthreads();
+
+  bool chosen;
+  int jx, ord = 0;
+  if (S <= 64) {
+    // one survivor per lane; ranks and index-order places by reading one lane per step
+    const bool mine = lane < S;
+    const int jl = min((int)surv[min(lane, max(S - 1, 0))], n - 1);  // in bounds even with no survivor
+    jx = mine ? jl : INT_MAX;
+    const float vx = mine ? sc[jl] : -INFINITY;
+    int r = 0;
+    for (int y = 0; y < S; ++y) r += above(lane_f(vx, y), __builtin_amdgcn_readlane(jx, y), vx, jx);
+    chosen = mine && r < topk;
+    for (int y = 0; y < S; ++y) {
+      const int jy = __builtin_amdgcn_readlane(jx, y);
+      const int ry = __builtin_amdgcn_readlane(r, y);
+      ord += (ry < topk && jy < jx) ? 1 : 0;
+    }
+  } else {
+    // many survivors (a few classes hold most of the best scores): ranks from LDS
+    sTop[lane] = -1;
+    __syncthreads();
+    for (int x = lane; x < S; x += 64) {
+      const int jv = surv[x];
+      const float vv = sc[jv];
+      int r = 0;
+      for (int y = 0; y < S; ++y) {
+        const int jy = surv[y];
+        r += above(sc[jy], jy, vv, jv) ? 1 : 0;
+      }
+      if (r < topk) sTop[r] = jv;
+    }
+    __syncthreads();
+    jx = lane < topk ? sTop[lane] : -1;
+    chosen = jx >= 0;
+    for (int y = 0; y < topk; ++y) {
+      const int jy = __builtin_amdgcn_readlane(jx, y);
+      ord += (jy >= 0 && jy < jx) ? 1 : 0;
+    }
+  }
+  if (chosen) out[ord] = jx;
+  const int nch = __popcll(__ballot(chosen));
+  if (lane >= nch && lane < topk) out[lane] = -1;
+}
+
+// ---- prefill, attention: one wave per (query block, h, b), all 64 queries, over
+// the own block (first: every query sees at least itself, so the running maximum is
+// finite from the start) and the chosen blocks.  Per key block:
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (K and Q straight from global memory in
+//   the A and B operand layouts, Q loaded once): lane holds 4 keys of one query per
+//   (key tile, query tile);
+//   softmax in base 2 against a fixed reference per query, the own block's maximum;
+//   when a later block drives a lane's 16 numerators past 2^kRestart, the query
+//   block starts over from the own block with the reference raised by log2 of that
+//   sum (at least kRestart, so passes are few and, with ordinary logits, one; at
+//   most kMaxPasses).  So P stays within 2^kRestart, no block maximum is taken after
+//   the own block and the accumulators are never rescaled;
+//   O^T += V^T P^T with V^T read transposed from LDS (272-byte rows) and P^T rounded
+//   to bf16 straight from the accumulators in the key order pi; each V^T operand
+//   read feeds the four query tiles.
+// The next block's K and V loads are in flight while the current block computes;
+// V goes through one LDS tile (the wave's LDS operations run in order).
+constexpr float kRestart = 64.0f;  // base-2 units: P, l and O stay far inside the fp32 range
+constexpr float kRestartSum = 18446744073709551616.0f;  // 2^kRestart
+constexpr int kMaxPasses = 8;  // bounds the passes for non-finite logits
+
+__global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, const int32_t* sel) {
+  __shared__ __attribute__((aligned(16))) uint8_t sV[kVTile];
+  const int lane = threadIdx.x, n16 = lane & 15, g4 = lane >> 4;
+  const int nqb = (p.T + kSB - 1) / kSB;
+  const int item = xcd_item(nqb * p.H * p.B);
+  if (item >= nqb * p.H * p.B) return;
+  const int i = item % nqb;
+  const int bh = item / nqb, h = bh % p.H, b = bh / p.H;
+  const int64_t rs = (int64_t)p.H * kD;
+  const int64_t base = (int64_t)b * p.T * rs + (int64_t)h * kD;
+  const int r0 = i * kSB, nv = min(kSB, p.T - r0);
+  const uint32_t rsb = (uint32_t)rs * 2;  // bytes between rows (at most 64 rows are addressed from a block start)
+
+  // lane x < topk holds chosen block x (the chosen ones first, in increasing order)
+  const int myblk = lane < p.topk ? sel[((int64_t)bh * nqb + i) * p.topk + lane] : -1;
+  const int nblk = 1 + __popcll(__ballot(myblk >= 0));
+  auto block_row0 = [&](int n) -> int { return n == 0 ? r0 : kSB * __builtin_amdgcn_readlane(myblk, n - 1); };
+  // rows of block n that exist: the own block may end at T, and then its missing rows
+  // repeat its last row (finite values that the causal mask and the unstored query
+  // rows leave without effect)
+  auto block_rows = [&](int n) -> int { return n == 0 ? nv : kSB; };
+
+  // per-lane byte offsets from a block's first row
+  const uint32_t voff = (uint32_t)g4 * rsb + 16u * n16;  // row 4 u + g4, bytes 16 n16 ..
+  uint32_t koff[4];                                       // row 16 kt + n16, bytes 16 g4 ..
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) koff[kt] = (uint32_t)(16 * kt + n16) * rsb + 16u * g4;
+  auto row_ptr = [&](const uint16_t* x, int row0) {
+    return reinterpret_cast<const uint8_t*>(x + base + (int64_t)row0 * rs);
+  };
+
+  uint4 Vr[16];  // rows 4 u + g4, bytes 16 n16 .. 16 n16 + 15
+  auto load_rows = [&](const uint16_t* x, int row0, int rows) {
+    const uint8_t* src = row_ptr(x, row0);
+    if (rows == kSB) {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) Vr[u] = *reinterpret_cast<const uint4*>(src + voff + (uint32_t)(4 * u) * rsb);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t r = (uint32_t)min(4 * u + g4, rows - 1);
+        Vr[u] = *reinterpret_cast<const uint4*>(src + r * rsb + 16u * n16);
+      }
+    }
+  };
+  // B operand Q[16 qt + n16][32 ks + 8 g4 + e], held in registers (rows past the
+  // block's end repeat its last row; their outputs are not stored)
+  bf16x8 Qf[4][4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const uint32_t r = (uint32_t)min(16 * qt + n16, nv - 1);
+    const uint8_t* src = row_ptr(p.q, r0) + r * rsb + 16u * g4;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) Qf[qt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + 64 * ks));
+  }
+  auto q_operand = [&](int qt, int ks) { return Qf[qt][ks]; };
+  bf16x8 Kf[4][4];  // [key tile][k-step]: A operand, K[16 kt + n16][32 ks + 8 g4 + e]
+  auto load_k = [&](int n) {
+    const uint8_t* src = row_ptr(p.k, block_row0(n));
+    const int rows = block_rows(n);
+    if (rows == kSB) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + koff[kt] + 64 * ks));
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const uint32_t r = (uint32_t)min(16 * kt + n16, rows - 1);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + r * rsb + 16u * g4 + 64 * ks));
+      }
+    }
+  };
+  auto load_v = [&](int n) { load_rows(p.v, block_row0(n), block_rows(n)); };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) lds_st<uint4>(sV, (4 * u + g4) * kRowBytes + 16 * n16, Vr[u]);
+  };
+
+  f32x4 O[8][4];  // O^T[16 dt + 4 g4 + r][query 16 qt + n16]
+  float m_ref[4], l_run[4];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) m_ref[qt] = -INFINITY;
   const float cs = kLog2e * rsqrtf((float)kD);
 
-  int cur = 0;                       // block being computed
-  int nxt = next_valid(1);           // block staged next
-  load_block(cur);
-  store_block(0);
-  if (nxt < nblk) load_block(nxt);
-  __syncthreads();
-  for (int step = 0; cur < nblk; ++step) {
-    const uint8_t* K = sKV[step & 1];
-    const uint8_t* V = K + kKTile;
-    f32x4 S[4];
+  for (int pass = 0, again = 1; again; ++pass) {
+    // one pass over the blocks; a block far above the reference starts a new pass
+    again = 0;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int qt = 0; qt < 4; ++qt) {
+      l_run[qt] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        S[kt] = mma(as_bf16x8(lds_ld<uint4>(K, (16 * kt + n16) * kKRow + 64 * ks + 16 * g4)), Qf[ks], S[kt]);
+      for (int dt = 0; dt < 8; ++dt) O[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // lane holds S^T[key 16 kt + 4 g + r][query qr]
-    float mx = -INFINITY;
+    load_v(0);  // V before K, as in the loop: the waits stay partial across the back edge
+    load_k(0);
+    for (int n = 0; n < nblk; ++n) {
+      store_v();
+      if (n + 1 < nblk) load_v(n + 1);
+      // per query tile: S^T = K Q^T, then its softmax numerators (the next tile's
+      // products can run meanwhile)
+      bf16x8 P[4][2];  // B operand of O^T += V^T P^T, keys in order pi
+      float ls[4];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int qt = 0; qt < 4; ++qt) {
+        f32x4 S[4];  // S^T[16 kt + 4 g4 + r][16 qt + n16]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = S[kt][r] * cs;
-        if (cur == 0 && 16 * kt + 4 * g4 + r > qr) x = -INFINITY;
-        S[kt][r] = x;
-        mx = fmaxf(mx, x);
+        for (int kt = 0; kt < 4; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 qo = q_operand(qt, ks);
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt) S[kt] = mma(Kf[kt][ks], qo, S[kt]);
+        }
+        if (n == 0) {
+          // the own block: keys after the query are masked, and on the first pass its
+          // maximum becomes the query's reference
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * kt + 4 * g4 + r > 16 * qt + n16) S[kt][r] = -INFINITY;
+          if (pass == 0) {
+            float m = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                            fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
+            m = fmaxf(m, fmaxf(fmaxf(fmaxf(S[2][0], S[2][1]), fmaxf(S[2][2], S[2][3])),
+                               fmaxf(fmaxf(S[3][0], S[3][1]), fmaxf(S[3][2], S[3][3]))));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            m_ref[qt] = m * cs;
+          }
+        }
+        const float nm = -m_ref[qt];
+        float l = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(S[kt][r], cs, nm));
+            S[kt][r] = e;
+            l += e;
+          }
+        ls[qt] = l;
+        P[qt][0] = pack8(S[0], S[1]);
+        P[qt][1] = pack8(S[2], S[3]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float ls = 0.f;
+      if (n + 1 < nblk) load_k(n + 1);
+      // a lane's 16 numerators summing past 2^kRestart: a key far above the reference
+      bool need = false;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int qt = 0; qt < 4; ++qt) need |= !(ls[qt] <= kRestartSum);
+      if (__ballot(need) != 0 && pass < kMaxPasses - 1) {
+        // raise the reference of the queries concerned past their largest numerator
+        // (log2 of a lane's sum bounds it; non-finite sums raise it by the most a pass
+        // can) and start a new pass
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S[kt][r] = exp2f(S[kt][r] - m_new);
-        ls += S[kt][r];
+        for (int qt = 0; qt < 4; ++qt) {
+          float up = ls[qt] <= kRestartSum ? 0.f : fminf(__builtin_amdgcn_logf(ls[qt]), 2.f * kRestart);
+          up = isnan(up) ? 2.f * kRestart : up;
+          up = fmaxf(up, __shfl_xor(up, 16));
+          up = fmaxf(up, __shfl_xor(up, 32));
+          m_ref[qt] += up;
+        }
+        again = 1;
+        break;
       }
-    l_run = fmaf(l_run, alpha, ls);
-    const bf16x8 P0 = pack8(S[0], S[1]), P1 = pack8(S[2], S[3]);  // keys in order pi
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      O[dt] *= alpha;
-      O[dt] = mma(v_operand(V, 0, 16 * dt, g4, n16), P0, O[dt]);
-      O[dt] = mma(v_operand(V, 1, 16 * dt, g4, n16), P1, O[dt]);
+      for (int qt = 0; qt < 4; ++qt) l_run[qt] += ls[qt];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this block's V tile written
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x8 a0 = v_operand(sV, 0, 16 * dt, g4, n16);
+        const bf16x8 a1 = v_operand(sV, 1, 16 * dt, g4, n16);
+#pragma unroll
+        for (int qt = 0; qt < 4; ++qt) {
+          O[dt][qt] = mma(a0, P[qt][0], O[dt][qt]);
+          O[dt][qt] = mma(a1, P[qt][1], O[dt][qt]);
+        }
+      }
     }
-    cur = nxt;
-    if (cur < nblk) {
-      store_block((step + 1) & 1);
-      nxt = next_valid(cur + 1);
-      if (nxt < nblk) load_block(nxt);
-    }
-    __syncthreads();
   }
-  // lane holds O^T[16 dt + 4 g + r][query qr]: normalize, gate, store 4 consecutive values
-  float lt = l_run + __shfl_xor(l_run, 16);
-  lt += __shfl_xor(lt, 32);
-  const float inv = 1.0f / lt;
-  if (qr < nv) {
-    const int64_t orow = base + (int64_t)(r0 + qr) * rs;
+  // normalize, gate, store 4 consecutive values of a query row per lane
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + 4 * g4;
-      const uint2 gg = *reinterpret_cast<const uint2*>(p.g + orow + d);
-      const float o0 = O[dt][0] * inv * sigmoidf_(bf2f_lo(gg.x));
-      const float o1 = O[dt][1] * inv * sigmoidf_(bf2f_hi(gg.x));
-      const float o2 = O[dt][2] * inv * sigmoidf_(bf2f_lo(gg.y));
-      const float o3 = O[dt][3] * inv * sigmoidf_(bf2f_hi(gg.y));
-      *reinterpret_cast<uint2*>(p.o + orow + d) = make_uint2(pack2(o0, o1), pack2(o2, o3));
+  for (int qt = 0; qt < 4; ++qt) {
+    float lt = l_run[qt] + __shfl_xor(l_run[qt], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int qr = 16 * qt + n16;
+    if (qr < nv) {
+      const int64_t orow = base + (int64_t)(r0 + qr) * rs;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int d = 16 * dt + 4 * g4;
+        const uint2 gg = *reinterpret_cast<const uint2*>(p.g + orow + d);
+        const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(gg.x));
+        const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(gg.x));
+        const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(gg.y));
+        const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(gg.y));
+        *reinterpret_cast<uint2*>(p.o + orow + d) = make_uint2(pack2(o0, o1), pack2(o2, o3));
+      }
     }
   }
 }
@@ -604,12 +815,16 @@ hipError_t launch_sparse_means(const SparseParams& p, int first, int nblocks, hi
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_prefill(const SparseParams& p, hipStream_t stream) {
+hipError_t launch_sparse_prefill(const SparseParams& p, int32_t* sel, hipStream_t stream) {
   hipError_t e = launch_sparse_means(p, 0, p.T / kSB, stream);
   if (e != hipSuccess) return e;
   const int64_t nqb = (p.T + kSB - 1) / kSB;
-  hipLaunchKernelGGL(la_sparse_prefill_kernel, dim3((unsigned)(nqb * p.H * p.B)), dim3(kSparseThreads), 0, stream,
-                     p);
+  const unsigned grid = (unsigned)((nqb * p.H * p.B + 7) / 8 * 8);  // see xcd_item
+  const size_t sel_lds = (size_t)(p.T / kSB) * (sizeof(float) + sizeof(uint16_t)) + 16;
+  hipLaunchKernelGGL(la_sparse_select_kernel, dim3(grid), dim3(64), sel_lds, stream, p, sel);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(la_sparse_attn_kernel, dim3(grid), dim3(64), 0, stream, p, sel);
   return hipGetLastError();
 }
 

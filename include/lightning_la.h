@@ -254,8 +254,9 @@ la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
  * blocks per sequence (T or Tmax <= 524288), B and H <= 65535.
  */
 
-/* Workspace of la_sparse_prefill: the key-block means, fp32 [B, H, T / 64, D]
- * (0 for an unsupported shape). */
+/* Workspace of la_sparse_prefill: the key-block means, fp32 [B, H, T / 64, D],
+ * then (at the next 256-byte boundary) room for the block choice, int32
+ * [B, H, ceil(T / 64), topk], used when sel is NULL (0 for an unsupported shape). */
 size_t la_sparse_prefill_workspace_bytes(int B, int T, int H, int D, int block, int topk);
 
 /*

@@ -235,8 +235,9 @@ def test_backward_validation(lib):
 def test_sparse_validation(lib):
     vp = ctypes.c_void_p
     # workspace: fp32 means of the complete 64-token key blocks
-    assert lib.la_sparse_prefill_workspace_bytes(1, 32768, 32, 128, 0, 16) == 32 * 512 * 128 * 4
-    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 64, 16) == 2 * 4 * 128 * 4
+    # key means, then the block choice [B, H, ceil(T / 64), topk] int32, each rounded to 256 bytes
+    assert lib.la_sparse_prefill_workspace_bytes(1, 32768, 32, 128, 0, 16) == 32 * 512 * 128 * 4 + 32 * 512 * 16 * 4
+    assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 64, 16) == 2 * 4 * 128 * 4 + 768
     assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 32, 16) == 0     # block 64 only
     assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 0, 0) == 0       # topk in [1, 64]
     assert lib.la_sparse_prefill_workspace_bytes(1, 300, 2, 128, 0, 65) == 0

@@ -182,3 +182,27 @@ def test_sparse_rejects_bad_arguments(la):
         la.sparse_prefill(q, k, v, g, topk=65)
     with pytest.raises(ValueError):
         la.sparse_prefill(q, k[:, :50].contiguous(), v, g)
+
+
+def test_blocks_far_above_the_own_block_restart_the_pass(la):
+    """Keys of block 3 (6 q) and block 7 (9 q) give logits about 98 and 147 base-2
+    units above the own blocks' (small random keys): the attention must restart its
+    pass with a raised reference (twice for query blocks that choose both) and still
+    match the fp64 softmax."""
+    B, T, H, topk = 1, 20 * BLK, 1, 4
+    gen = workloads.generator(41, "cuda")
+    q = torch.ones((B, T, H, D), device="cuda")
+    k = 0.05 * torch.randn((B, T, H, D), generator=gen, device="cuda")
+    k[:, 3 * BLK:4 * BLK] = 6.0
+    k[:, 7 * BLK:8 * BLK] = 9.0
+    v, g = (torch.randn((B, T, H, D), generator=gen, device="cuda") for _ in range(2))
+    q, k, v, g = (x.to(torch.bfloat16) for x in (q, k, v, g))
+    o, sel = la.sparse_prefill(q, k, v, g, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    s = sel.cpu().numpy()
+    for i in range(8, T // BLK):
+        assert 3 in s[0, 0, i] and 7 in s[0, 0, i], (i, s[0, 0, i])
+    assert torch.isfinite(o.float()).all()
+    f = [to_np32(x) for x in (q, k, v, g)]
+    o_ref, _, _ = oracle.sparse_forward(*f, block=BLK, topk=topk, sel=s)
+    assert_o_close(to_np(o), o_ref, what="restarted passes")
