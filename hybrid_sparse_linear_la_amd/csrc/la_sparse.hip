@@ -34,7 +34,8 @@ namespace la {
 namespace {
 
 constexpr int kSB = kSparseBlock;
-constexpr int kSparseThreads = 256;
+constexpr int kSparseThreads = 256;  // block means
+constexpr int kDecodeThreads = 1024;  // decode: 16 waves keep enough of each sequence's reads in flight
 constexpr int kVTile = kSB * kRowBytes;  // 272-byte V rows, read transposed
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -86,10 +87,10 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_means_kernel(SparseP
 // Scores sc[j] = qm . kmean[j] for j < n: 16 lanes per key block (8 dims each),
 // kInFlight key blocks per lane group in flight.  qm is in LDS; every thread of the
 // workgroup calls it.
-template <int kInFlight>
+template <int kInFlight, int kT>
 __device__ __forceinline__ void block_scores(const float* qm, const float* kmean, int n, float* sc) {
   const int tid = threadIdx.x, grp = tid >> 4, c = tid & 15;
-  constexpr int kGroups = kSparseThreads / 16;
+  constexpr int kGroups = kT / 16;
   float q8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) q8[e] = qm[8 * c + e];
@@ -121,9 +122,10 @@ __device__ __forceinline__ void block_scores(const float* qm, const float* kmean
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
 // Scratch of select_topk in LDS.
+template <int kT>
 struct SelectScratch {
-  float gmax[kSparseThreads];  // per-thread best (score, index)
-  int gidx[kSparseThreads];
+  float gmax[kT];  // per-thread best (score, index)
+  int gidx[kT];
   int count;                   // survivors
   float thresh;                // the threshold candidate (score, index)
   int thresh_idx;
@@ -151,16 +153,17 @@ __device__ __forceinline__ float lane_f(float x, int l) {
 //      are ranked from LDS by all threads and then sorted.
 // surv holds 2 cap ints (cap pairs) and at least n ints.  Every thread calls it;
 // it ends on a barrier.
-__device__ int select_topk(const float* sc, int n, int topk, int* list, int* surv, int cap, SelectScratch* ss) {
+template <int kT>
+__device__ int select_topk(const float* sc, int n, int topk, int* list, int* surv, int cap, SelectScratch<kT>* ss) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (n <= topk) {
-    for (int x = tid; x < n; x += kSparseThreads) list[x] = x;
+    for (int x = tid; x < n; x += kT) list[x] = x;
     __syncthreads();
     return n;
   }
   float gm = -INFINITY;
   int gi = INT_MAX;
-  for (int j = tid; j < n; j += kSparseThreads)
+  for (int j = tid; j < n; j += kT)
     if (above(sc[j], j, gm, gi)) {
       gm = sc[j];
       gi = j;
@@ -174,7 +177,7 @@ __device__ int select_topk(const float* sc, int n, int topk, int* list, int* sur
     float c = ss->gmax[tid];
     int ci = ss->gidx[tid];
 #pragma unroll
-    for (int q = 1; q < 4; ++q)
+    for (int q = 1; q < kT / 64; ++q)
       if (above(ss->gmax[tid + 64 * q], ss->gidx[tid + 64 * q], c, ci)) {
         c = ss->gmax[tid + 64 * q];
         ci = ss->gidx[tid + 64 * q];
@@ -194,7 +197,7 @@ __device__ int select_topk(const float* sc, int n, int topk, int* list, int* sur
   __syncthreads();
   const float M = ss->thresh;
   const int jM = ss->thresh_idx;
-  for (int j = tid; j < n; j += kSparseThreads) {
+  for (int j = tid; j < n; j += kT) {
     const float v = sc[j];
     if (v > M || (v == M && j <= jM)) {
       const int x = atomicAdd(&ss->count, 1);
@@ -226,7 +229,7 @@ __device__ int select_topk(const float* sc, int n, int topk, int* list, int* sur
     return topk;
   }
   if (S <= cap) {
-    for (int x = tid; x < S; x += kSparseThreads) {
+    for (int x = tid; x < S; x += kT) {
       const float vx = __int_as_float(surv[2 * x]);
       const int jx = surv[2 * x + 1];
       int r = 0;
@@ -241,10 +244,10 @@ __device__ int select_topk(const float* sc, int n, int topk, int* list, int* sur
     // more survivors than pairs fit: indices only, scores read back
     if (tid == 0) ss->count = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += kSparseThreads)
+    for (int j = tid; j < n; j += kT)
       if (sc[j] > M || (sc[j] == M && j <= jM)) surv[atomicAdd(&ss->count, 1)] = j;
     __syncthreads();
-    for (int x = tid; x < S; x += kSparseThreads) {
+    for (int x = tid; x < S; x += kT) {
       const int jx = surv[x];
       const float vx = sc[jx];
       int r = 0;
@@ -679,14 +682,15 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
 }
 
 // ---- decode: one query per (b, h) against its cache
-__global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(SparseParams p) {
+__global__ __launch_bounds__(kDecodeThreads) void la_sparse_decode_kernel(SparseParams p) {
+  constexpr int kT = kDecodeThreads, kWaves = kT / 64, kGroups = kT / 16, kRowsInFlight = 8;
   __shared__ float sc[kSparseMaxBlocks];  // block scores, then the attention weights
   __shared__ float sQ[kD];
-  __shared__ float part[16][kD];
+  __shared__ float part[kGroups][kD];
   __shared__ int surv[2 * kSparseMaxBlocks];
   __shared__ int sList[kSparseMaxTopk];
-  __shared__ SelectScratch ss;
-  __shared__ float red_v[4];
+  __shared__ SelectScratch<kT> ss;
+  __shared__ float red_v[kWaves];
   static_assert((kSparseMaxTopk + 1) * kSB <= kSparseMaxBlocks, "weights must fit the score array");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -702,12 +706,12 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   if (ncand <= p.topk) {
     nlist = select_topk(nullptr, ncand, p.topk, sList, nullptr, 0, &ss);
   } else {
-    block_scores<8>(sQ, p.kmean + (int64_t)bh * (p.T / kSB) * kD, ncand, sc);
+    block_scores<8, kT>(sQ, p.kmean + (int64_t)bh * (p.T / kSB) * kD, ncand, sc);
     __syncthreads();
     nlist = select_topk(sc, ncand, p.topk, sList, surv, kSparseMaxBlocks, &ss);
   }
   if (p.sel != nullptr)
-    for (int x = tid; x < p.topk; x += kSparseThreads) {
+    for (int x = tid; x < p.topk; x += kT) {
       int cnt = 0, val = -1;
       for (int y = 0; y < nlist; ++y)
         if (sList[y] >= 0) {
@@ -731,18 +735,17 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
     float q8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) q8[e] = sQ[8 * c + e];
-    constexpr int kGroups = kSparseThreads / 16;
-    for (int n0 = grp; n0 < nk; n0 += 4 * kGroups) {  // four key rows per lane group in flight
-      uint4 u[4];
-      int row[4];
+    for (int n0 = grp; n0 < nk; n0 += kRowsInFlight * kGroups) {  // rows per lane group in flight
+      uint4 u[kRowsInFlight];
+      int row[kRowsInFlight];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < kRowsInFlight; ++x) {
         const int n = n0 + x * kGroups;
         row[x] = n < nk ? key_row(n) : -1;
         u[x] = *reinterpret_cast<const uint4*>(p.k + cbase + (int64_t)max(row[x], 0) * rs + 8 * c);
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < kRowsInFlight; ++x) {
         const int n = n0 + x * kGroups;
         const float s = row16_sum(dot_bf16x8(u[x], q8));
         if (c == 0 && n < nk) sc[n] = row[x] >= 0 ? s * cs : -INFINITY;
@@ -751,13 +754,15 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   }
   __syncthreads();
   float mx = -INFINITY;
-  for (int n = tid; n < nk; n += kSparseThreads) mx = fmaxf(mx, sc[n]);
+  for (int n = tid; n < nk; n += kT) mx = fmaxf(mx, sc[n]);
   mx = wave_max(mx);
   if (lane == 0) red_v[w] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red_v[0], red_v[1]), fmaxf(red_v[2], red_v[3]));
+  mx = red_v[0];
+#pragma unroll
+  for (int x = 1; x < kWaves; ++x) mx = fmaxf(mx, red_v[x]);
   float den = 0.f;
-  for (int n = tid; n < nk; n += kSparseThreads) {
+  for (int n = tid; n < nk; n += kT) {
     const float e = exp2f(sc[n] - mx);
     sc[n] = e;
     den += e;
@@ -766,23 +771,24 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   __syncthreads();  // every thread has read red_v (max) before it is reused
   if (lane == 0) red_v[w] = den;
   __syncthreads();
-  den = red_v[0] + red_v[1] + red_v[2] + red_v[3];
+  den = 0.f;
+#pragma unroll
+  for (int x = 0; x < kWaves; ++x) den += red_v[x];
   {
     const int kg = tid >> 4, c = tid & 15;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    constexpr int kGroups = kSparseThreads / 16;
-    for (int n0 = kg; n0 < nk; n0 += 4 * kGroups) {  // four value rows per lane group in flight
-      uint4 u[4];
-      float pn[4];
+    for (int n0 = kg; n0 < nk; n0 += kRowsInFlight * kGroups) {  // rows per lane group in flight
+      uint4 u[kRowsInFlight];
+      float pn[kRowsInFlight];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < kRowsInFlight; ++x) {
         const int n = n0 + x * kGroups;
         const int row = n < nk ? key_row(n) : -1;
         u[x] = *reinterpret_cast<const uint4*>(p.v + cbase + (int64_t)max(row, 0) * rs + 8 * c);
         pn[x] = row >= 0 ? sc[n] : 0.f;  // empty slots and rows past the list weigh nothing
       }
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
+      for (int x = 0; x < kRowsInFlight; ++x) {
         acc[0] = fmaf(pn[x], bf2f_lo(u[x].x), acc[0]);
         acc[1] = fmaf(pn[x], bf2f_hi(u[x].x), acc[1]);
         acc[2] = fmaf(pn[x], bf2f_lo(u[x].y), acc[2]);
@@ -800,7 +806,7 @@ __global__ __launch_bounds__(kSparseThreads) void la_sparse_decode_kernel(Sparse
   if (tid < kD) {
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += part[r][tid];
+    for (int r = 0; r < kGroups; ++r) s += part[r][tid];
     const float o = s / den * sigmoidf_(bf2f(p.g[qoff + tid]));
     p.o[qoff + tid] = (uint16_t)f2bf(o);
   }
@@ -829,7 +835,7 @@ hipError_t launch_sparse_prefill(const SparseParams& p, int32_t* sel, hipStream_
 }
 
 hipError_t launch_sparse_decode(const SparseParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(la_sparse_decode_kernel, dim3((unsigned)(p.B * p.H)), dim3(kSparseThreads), 0, stream, p);
+  hipLaunchKernelGGL(la_sparse_decode_kernel, dim3((unsigned)(p.B * p.H)), dim3(kDecodeThreads), 0, stream, p);
   return hipGetLastError();
 }
 
