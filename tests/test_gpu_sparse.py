@@ -18,6 +18,7 @@ from parity import assert_o_close, to_np, to_np32
 pytestmark = pytest.mark.gpu
 D = 128
 BLK = 64
+kMaxT = 8192 * BLK  # the most key blocks a sequence may have
 
 
 @pytest.fixture(scope="module")
@@ -206,3 +207,63 @@ def test_blocks_far_above_the_own_block_restart_the_pass(la):
     f = [to_np32(x) for x in (q, k, v, g)]
     o_ref, _, _ = oracle.sparse_forward(*f, block=BLK, topk=topk, sel=s)
     assert_o_close(to_np(o), o_ref, what="restarted passes")
+
+
+def _attend_rows(q, k, v, g, rows, keys, allowed):
+    """fp64 softmax attention of query rows over key rows (token indices), restricted
+    to allowed[row, key], gated: o = sigmoid(g) * softmax(q k / sqrt(D)) v."""
+    qd, kd, vd = (x.astype(np.float64) for x in (q, k, v))
+    logits = np.where(allowed, qd[rows] @ kd[keys].T / np.sqrt(D), -np.inf)
+    logits -= logits.max(axis=1, keepdims=True)
+    pr = np.exp(logits)
+    pr /= pr.sum(axis=1, keepdims=True)
+    return 1.0 / (1.0 + np.exp(-g[rows].astype(np.float64))) * (pr @ vd[keys])
+
+
+def test_sparse_prefill_at_the_largest_supported_length(la):
+    """8192 key blocks (T = 524288, one head), where the full fp64 oracle takes minutes:
+    on sampled query blocks (the last ones included) the GPU's choice is checked
+    against fp64 block scores and its output against fp64 softmax attention over that
+    choice, causal in the own block."""
+    B, T, H, topk = 1, kMaxT, 1, 16
+    q, k, v, g = workloads.activations(B, T, H, D, 61, "cuda")
+    o, sel = la.sparse_prefill(q, k, v, g, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    qn, kn, vn, gn = (to_np32(x)[0, :, 0] for x in (q, k, v, g))
+    on, s = to_np(o)[0, :, 0], sel.cpu().numpy()[0, 0]
+    kmean = kn.astype(np.float64).reshape(T // BLK, BLK, D).mean(axis=1)
+    nqb = T // BLK
+    for i in (1, 17, 1000, 4097, nqb - 2, nqb - 1):
+        qmean = qn[i * BLK:(i + 1) * BLK].astype(np.float64).mean(axis=0)
+        scores = (kmean[:i] @ qmean)[None, None, None, :]
+        _check_choice(s[i][None, None, None, :], scores, np.array([i]), topk, f"query block {i}")
+        rows = np.arange(i * BLK, (i + 1) * BLK)
+        keys = np.array([int(j) * BLK + u for j in s[i] if j >= 0 for u in range(BLK)] + list(rows))
+        allowed = (keys[None, :] < i * BLK) | (keys[None, :] <= rows[:, None])  # own block: causal
+        ref = _attend_rows(qn, kn, vn, gn, rows, keys, allowed)
+        assert_o_close(on[rows][None, :, None], ref[None, :, None], what=f"query block {i} of {nqb}")
+
+
+def test_sparse_decode_at_the_largest_supported_cache(la):
+    """A full 524288-token cache (8191 candidate blocks): the choice against fp64
+    scores, the output against fp64 softmax attention over it."""
+    B, Tmax, H, topk = 1, kMaxT, 2, 16
+    q, kc, vc, g = _caches(B, Tmax, H, seed=62)
+    means = la.sparse_block_means(kc)
+    lens = torch.tensor([Tmax], dtype=torch.int32, device="cuda")
+    o, sel = la.sparse_decode(q, kc, vc, means, g, lens, topk=topk, return_sel=True)
+    torch.cuda.synchronize()
+    t = Tmax - 1
+    own = t // BLK
+    for h in range(H):
+        qn, gn = to_np32(q)[0, h], to_np32(g)[0, h]
+        kn, vn = to_np32(kc)[0, :, h], to_np32(vc)[0, :, h]
+        kmean = kn[:own * BLK].astype(np.float64).reshape(own, BLK, D).mean(axis=1)
+        s = sel.cpu().numpy()[0, h]
+        _check_choice(s[None, :], (kmean @ qn.astype(np.float64))[None, :], np.array([own]), topk, f"head {h}")
+        keys = [int(j) * BLK + u for j in s if j >= 0 for u in range(BLK)] + list(range(own * BLK, t + 1))
+        logits = kn[keys].astype(np.float64) @ qn.astype(np.float64) / np.sqrt(D)
+        pr = np.exp(logits - logits.max())
+        pr /= pr.sum()
+        ref = (pr @ vn[keys].astype(np.float64)) / (1.0 + np.exp(-gn.astype(np.float64)))
+        assert_o_close(to_np(o)[0, h][None, None, None], ref[None, None, None], what=f"decode head {h}")
