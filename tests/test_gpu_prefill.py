@@ -163,3 +163,31 @@ def test_binding_rejects_bad_arguments(la):
     assert ei.value.status == 3
     with pytest.raises(ValueError):
         la.prefill(q, k[:, :32], v, g)
+
+
+def _random_cases(n, seed):
+    """Seeded random shapes: batch, length (any remainder modulo 64, several
+    segments for the longer ones), heads, start position, chunk, initial state and
+    norm weights."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 4))
+        T = int(rng.choice([rng.integers(1, 130), rng.integers(130, 1500), rng.integers(1500, 6000)]))
+        H = int(rng.integers(1, 9))
+        pos0 = int(rng.choice([0, rng.integers(1, 5000), rng.integers(200000, 1100000)]))
+        chunk = int(rng.choice([0, 64, 128, 256]))
+        S_std = float(rng.choice([0.0, 0.3]))
+        out.append((B, T, H, pos0, chunk, S_std, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,T,H,pos0,chunk,S_std,weights", _random_cases(12, 2024))
+def test_random_shapes_match_oracle(la, B, T, H, pos0, chunk, S_std, weights):
+    print(f"random case B={B} T={T} H={H} pos0={pos0} C={chunk} S_std={S_std} weights={weights}", flush=True)
+    q, k, v, g, S_in, qw, kw = _inputs(B, T, H, seed=31 + T + H, S_std=S_std, weights=weights)
+    o, S = la.prefill(q, k, v, g, S_in=S_in, pos0=pos0, chunk=chunk, q_norm_w=qw, k_norm_w=kw)
+    torch.cuda.synchronize()
+    o_ref, S_ref = _oracle(q, k, v, g, S_in, pos0, qw, kw)
+    assert_o_close(to_np(o), o_ref)
+    assert_S_close(to_np(S), S_ref)

@@ -267,3 +267,22 @@ def test_sparse_decode_at_the_largest_supported_cache(la):
         pr /= pr.sum()
         ref = (pr @ vn[keys].astype(np.float64)) / (1.0 + np.exp(-gn.astype(np.float64)))
         assert_o_close(to_np(o)[0, h][None, None, None], ref[None, None, None], what=f"decode head {h}")
+
+
+def _random_sparse_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 3))
+        T = int(rng.choice([rng.integers(1, 200), rng.integers(200, 3000), rng.integers(3000, 9000)]))
+        H = int(rng.integers(1, 5))
+        topk = int(rng.choice([1, 2, 7, 16, 33, 64]))
+        out.append((B, T, H, topk))
+    return out
+
+
+@pytest.mark.parametrize("B,T,H,topk", _random_sparse_cases(8, 77))
+def test_sparse_random_shapes_match_oracle(la, B, T, H, topk):
+    print(f"random sparse case B={B} T={T} H={H} topk={topk}", flush=True)
+    err, differ = _prefill_case(la, B, T, H, topk, seed=300 + T % 101 + topk)
+    print(f"  row error max {err['max']:.2e}, choices differing from the fp64 order: {differ}", flush=True)
