@@ -129,3 +129,30 @@ def test_backward_with_and_without_weight_gradients_agree(la, weights):
         assert rel.max().item() <= 2.0 ** -8, f"{name}: row difference {rel.max().item():.2e}"
         frac = (a != b).double().mean().item()
         assert frac <= 1e-4, f"{name}: {frac:.2e} of the elements differ"
+
+
+def _random_cases(n, seed):
+    """Seeded random shapes for the backward: batch, length, heads, start position,
+    initial state, final-state gradient, norm weights and their gradients."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        B = int(rng.integers(1, 3))
+        T = int(rng.choice([rng.integers(1, 130), rng.integers(130, 1200), rng.integers(1200, 4000)]))
+        H = int(rng.integers(1, 7))
+        pos0 = int(rng.choice([0, rng.integers(1, 3000), rng.integers(200000, 1000000)]))
+        S_std, dS_std = (float(rng.choice([0.0, 0.3])) for _ in range(2))
+        weights = bool(rng.integers(0, 2))
+        out.append((B, T, H, pos0, S_std, dS_std, weights, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("B,T,H,pos0,S_std,dS_std,weights,weight_grads", _random_cases(8, 515))
+def test_backward_random_shapes_match_oracle(la, B, T, H, pos0, S_std, dS_std, weights, weight_grads):
+    print(f"random backward case B={B} T={T} H={H} pos0={pos0} weights={weights} wgrad={weight_grads}",
+          flush=True)
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 700 + T, S_std, dS_std, weights)
+    grads = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, pos0=pos0, q_norm_w=qw, k_norm_w=kw,
+                        weight_grads=weight_grads)
+    torch.cuda.synchronize()
+    _check(grads, q, k, v, g, d_o, S_in, dS_out, pos0, qw, kw, weight_grads)

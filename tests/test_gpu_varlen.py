@@ -127,3 +127,28 @@ def test_varlen_rejects_bad_arguments(la):
         la.prefill_varlen(q, k, v, g, [0, 4, 3])      # decreasing offsets
     with pytest.raises(ValueError):
         la.prefill_varlen(q, k, v, g, cu, pos0=[0])   # pos0 of the wrong length
+
+
+def _random_batches(n, seed):
+    """Seeded random packed batches: 1-40 sequences mixing empty ones, decode steps
+    and prompts up to a few thousand tokens, random positions, heads and chunk."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        nseq = int(rng.integers(1, 41))
+        kinds = rng.integers(0, 4, nseq)
+        lengths = [int([0, 1, rng.integers(2, 200), rng.integers(200, 3000)][kd]) for kd in kinds]
+        pos0 = [int(rng.choice([0, rng.integers(1, 5000), rng.integers(200000, 900000)])) for _ in range(nseq)]
+        out.append((lengths, pos0, int(rng.integers(1, 7)), float(rng.choice([0.0, 0.3])),
+                    bool(rng.integers(0, 2)), int(rng.choice([0, 128, 256]))))
+    return out
+
+
+@pytest.mark.parametrize("lengths,pos0,H,S_std,weights,chunk", _random_batches(6, 99))
+def test_varlen_random_batches_match_oracle(la, lengths, pos0, H, S_std, weights, chunk):
+    print(f"random varlen case nseq={len(lengths)} total={sum(lengths)} H={H} chunk={chunk}", flush=True)
+    q, k, v, g, S_in, qw, kw, cu = _packed(lengths, H, seed=61 + len(lengths) + H, S_std=S_std,
+                                           weights=weights)
+    o, S_out = la.prefill_varlen(q, k, v, g, cu, pos0=pos0, S_in=S_in, chunk=chunk, q_norm_w=qw, k_norm_w=kw)
+    torch.cuda.synchronize()
+    _check_against_oracle(o, S_out, q, k, v, g, S_in, cu, pos0, qw, kw)
