@@ -75,3 +75,16 @@ def test_decode_rejects_bad_arguments(la):
         la.decode_step(q, q, q, q, S[:1], 0)
     with pytest.raises(TypeError):
         la.decode_step(q.float(), q, q, q, S, 0)
+
+
+def _random_decode(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(1, 70)), int(rng.integers(1, 40)), int(rng.integers(1, 4)),
+             int(rng.choice([0, rng.integers(1, 5000), rng.integers(200000, 1 << 21)])),
+             float(rng.choice([0.0, 0.02, 0.5])), bool(rng.integers(0, 2))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("B,H,steps,pos,S_std,weights", _random_decode(8, 717))
+def test_decode_random_shapes_match_oracle(la, B, H, steps, pos, S_std, weights):
+    """Seeded random batches, heads, positions (up to 2^21), states and norm weights."""
+    test_decode_matches_oracle(la, B, H, steps, pos, S_std, weights)

@@ -121,3 +121,21 @@ def test_linear_rejects_bad_shapes(la):
         la.linear(x, torch.zeros((100, 128), dtype=torch.bfloat16, device="cuda"))   # N % 256
     with pytest.raises(ValueError):
         la.linear(x, torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda"))    # K mismatch
+
+
+def _random_linear(n, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.choice([rng.integers(1, 64), rng.integers(64, 700), rng.integers(700, 3000)])),
+             256 * int(rng.integers(1, 9)), 64 * int(rng.integers(1, 40))) for _ in range(n)]
+
+
+@pytest.mark.parametrize("M,N,K", _random_linear(8, 313))
+def test_linear_random_shapes_match_float64(la, M, N, K):
+    """Seeded random shapes: any M (ragged last row tile), N a multiple of 256, K of 64."""
+    print(f"random linear case M={M} N={N} K={K}", flush=True)
+    gen = workloads.generator(200 + M + K, "cuda")
+    x = torch.randn((M, K), generator=gen, device="cuda").to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=gen, device="cuda") / K ** 0.5).to(torch.bfloat16)
+    y = la.linear(x, w)
+    torch.cuda.synchronize()
+    _linear_close(to_np(y), oracle.linear(to_np(x), to_np(w)), f"linear {M}x{N}x{K}")
