@@ -258,6 +258,21 @@ def cpu_baseline(tensors, args):
                       f"(fp64 token-by-token recurrence, {dt:.1f} s)"}
 
 
+def cpu_decode_baseline(workloads, steps=5):
+    """The oracle's decode step on the batched-decode workload (64 sequences x 32
+    heads), a few consecutive steps timed on the host."""
+    import oracle
+    w = workloads.DECODE_B64
+    S0, q, k, v, g = (t.double().numpy() for t in workloads.decode_inputs(w, steps=steps, device="cpu"))
+    S = S0
+    t0 = time.perf_counter()
+    for n in range(steps):
+        _, S = oracle.decode_step(q[n], k[n], v[n], g[n], S, w.pos0 + n)
+    dt = time.perf_counter() - t0
+    return {"value": round(dt / steps * 1e6, 1), "unit": "us/step", "cores": oracle.get_threads(),
+            "kind": "oracle", "sample": f"{steps} consecutive steps of the {w.B} x {w.H}-head batch ({dt:.1f} s)"}
+
+
 def bench_varlen(la, torch, workloads, hip, args, steps=5):
     """The serving mix as one la_prefill_varlen call, and the same work as one
     equal-length la_prefill over the prompts plus one la_decode_step."""
@@ -537,6 +552,8 @@ def main():
     sparse = None if args.no_sparse else bench_sparse(la, torch, workloads, hip)
     stream_1m = None if args.no_stream else bench_stream(la, torch, workloads, hip)
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
+    if decode is not None and not args.no_cpu_baseline:
+        decode["cpu_baseline"] = cpu_decode_baseline(workloads)
     line = {
         "metric": "linear-attn prefill tokens/s @256K (MFMA util %) + decode step us & GB/s",
         "value": round(tps, 1),
