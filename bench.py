@@ -506,7 +506,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--decode-steps", type=int, default=1000)
-    ap.add_argument("--cpu-tokens", type=int, default=49152)
+    ap.add_argument("--cpu-tokens", type=int, default=65536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
