@@ -22,7 +22,7 @@
 //   v_mfma_f32_16x16x32_bf16 with K and Q in operand registers, P^T rounded to bf16
 //   straight from the accumulators as the B operand of O^T += V^T P^T (V^T read
 //   transposed from LDS), softmax against a per-query reference without rescaling.
-// la_sparse_decode_kernel: one workgroup per (b, h): scores, top-k, then the
+// la_sparse_decode_kernel: one 1024-thread workgroup per (b, h): scores, top-k, then the
 //   attention of the single query over the chosen tokens (16 lanes per key row).
 #include <limits.h>
 
