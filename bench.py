@@ -435,7 +435,7 @@ def bench_sparse(la, torch, workloads, hip, steps=5):
     flops = 4 * w.D * sparse_prefill_keys(w.T, w.topk) * w.B * w.H
     tf = flops / (pre_ms / 1e3) / 1e12
     prefill = {"workload": w.name, "ms": round(pre_ms, 4), "tokens_per_s": round(w.B * w.T / (pre_ms / 1e3), 1),
-               "flops": flops, "roofline": {"bound": "mfma", "kernel": "la_sparse_prefill (means + attention)",
+               "flops": flops, "roofline": {"bound": "mfma", "kernel": "la_sparse_prefill (means + selection + attention)",
                                             "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                                             "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4)}}
     del q, k, v, g, o, ws
