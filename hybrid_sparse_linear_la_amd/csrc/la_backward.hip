@@ -36,17 +36,47 @@ namespace la {
 namespace {
 
 constexpr int kBwdThreads = 512;
-constexpr int kSnapBytes = kD * kRowBytes;  // [128][128] bf16, 272-byte rows
 
 // The chunk's q, k, v and du tiles use the TilePi layout (288-byte rows, key
 // dims stored in order pi); the S^T, G^T snapshots and the score tiles are
 // row-major with natural columns.
 constexpr int kPiTileBytes = kC * TilePi::kRow;
 
-// Column operand of a snapshot ([128][128], 272-byte rows) in order pi over its
-// rows: lane n16 gets X[32kk + 4g + 16(e/4) + e%4][c0 + n16].
+// The snapshot area ([128][128] bf16 S^T and G^T; later the chunk's dqh and dkh
+// tiles) has 280-byte rows: the 8-byte stores of an MFMA result (16 rows x 4 lane
+// groups) are conflict-free there, where 272-byte rows cost 8 conflict cycles per
+// store (gfx950 counters).  With it the kernel's LDS is exactly 160 KiB.
+constexpr int kSnapRow = kD * 2 + 24;
+constexpr int kSnapBytes = kD * kSnapRow;
+__device__ __forceinline__ int snap_off(int t, int d) { return t * kSnapRow + 2 * d; }
+
+// Column operand of a snapshot in order pi over its rows: lane n16 gets
+// X[32kk + 4g + 16(e/4) + e%4][c0 + n16].
 __device__ __forceinline__ bf16x8 snap_col(const uint8_t* snap, int kk, int c0, int g4, int n16) {
-  return v_operand(snap, kk, c0, g4, n16);
+  const int t0 = 32 * kk + 4 * g4 + (n16 >> 2), c = c0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(snap, snap_off(t0, c)), lds_tr(snap, snap_off(t0 + 16, c)));
+}
+
+// The q and k norm weights (ones if absent) live in the 32 padding bytes of rows
+// 0..31 of the q tile, which no tile access touches: weight i of tensor a at row
+// (128a + i) / 8, byte 256 + 4 ((128a + i) % 8).
+__device__ __forceinline__ int norm_weight_off(int a, int i) {
+  const int f = kD * a + i;
+  return (f >> 3) * TilePi::kRow + kD * 2 + 4 * (f & 7);
+}
+
+// Norm weights of dims 4j..4j+3 and 64+4j..64+4j+3 of tensor a (0: q, 1: k).
+__device__ __forceinline__ void pad_norm_weights(const uint8_t* sQ, int a, int j, float (&out)[8]) {
+  const float4 lo = lds_ld<float4>(sQ, norm_weight_off(a, 4 * j));
+  const float4 hi = lds_ld<float4>(sQ, norm_weight_off(a, kHalf + 4 * j));
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = lo.z;
+  out[3] = lo.w;
+  out[4] = hi.x;
+  out[5] = hi.y;
+  out[6] = hi.z;
+  out[7] = hi.w;
 }
 
 __device__ __forceinline__ bf16x8 negate(bf16x8 x) {
@@ -96,20 +126,6 @@ __device__ __forceinline__ void prologue_back_row(uint2 xl, uint2 xh, uint2 yl, 
   for (int e = 0; e < 8; ++e) dx[e] = w[e] * dn[e] * inv - xs[e] * k3;
 }
 
-// Norm weights of dims 4j..4j+3 and 64+4j..64+4j+3 from an LDS copy.
-__device__ __forceinline__ void lds_norm_weights(const float* w, int j, float (&out)[8]) {
-  const float4 lo = *reinterpret_cast<const float4*>(w + 4 * j);
-  const float4 hi = *reinterpret_cast<const float4*>(w + kHalf + 4 * j);
-  out[0] = lo.x;
-  out[1] = lo.y;
-  out[2] = lo.z;
-  out[3] = lo.w;
-  out[4] = hi.x;
-  out[5] = hi.y;
-  out[6] = hi.z;
-  out[7] = hi.w;
-}
-
 __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const float (&v)[8]) {
   *reinterpret_cast<uint2*>(dst + 4 * j) = make_uint2(pack2(v[0], v[1]), pack2(v[2], v[3]));
   *reinterpret_cast<uint2*>(dst + kHalf + 4 * j) = make_uint2(pack2(v[4], v[5]), pack2(v[6], v[7]));
@@ -117,12 +133,12 @@ __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const flo
 
 // The prologue backward of one chunk inside the chunk kernel: thread (rg, j) takes
 // rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
-// (272-byte rows), q, k again from memory (cached since the chunk's staging).
+// (the snapshot area's rows), q, k again from memory (cached since the chunk's staging).
 // dw receives the thread's norm-weight gradient terms (its two rows summed).
 template <bool kWeights>
 __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
                                                    int nv, int64_t rs, int rg, int j, const Rope& L, float2 (&E)[4],
-                                                   const uint8_t* sDq, const uint8_t* sDk, const float (*sNW)[kD],
+                                                   const uint8_t* sDq, const uint8_t* sDk, const uint8_t* sQ,
                                                    float (&dw)[2][8]) {
   Rows<2> X[2];
   load_rows<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
@@ -131,7 +147,7 @@ __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const
 #pragma unroll
   for (int a = 0; a < 2; ++a)
     if (kWeights) {
-      lds_norm_weights(sNW[a], j, w[a]);
+      pad_norm_weights(sQ, a, j, w[a]);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[a][e] = 1.0f;
@@ -144,8 +160,8 @@ __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const
     for (int a = 0; a < 2; ++a) {
       const uint8_t* Y = a ? sDk : sDq;
       float dx[8], dn[8], x[8], inv;
-      prologue_back_row(X[a].lo[m], X[a].hi[m], lds_ld<uint2>(Y, tile_off(t, 4 * j)),
-                        lds_ld<uint2>(Y, tile_off(t, kHalf + 4 * j)), w[a], E, p.eps, dx, dn, x, inv);
+      prologue_back_row(X[a].lo[m], X[a].hi[m], lds_ld<uint2>(Y, snap_off(t, 4 * j)),
+                        lds_ld<uint2>(Y, snap_off(t, kHalf + 4 * j)), w[a], E, p.eps, dx, dn, x, inv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) dw[a][e] = (m > 0 ? dw[a][e] : 0.f) + (t < nv ? dn[e] * x[e] * inv : 0.f);
       if (t < nv) store_row_pieces((a ? bp.dk : bp.dq) + base + (int64_t)t * rs, j, dx);
@@ -174,7 +190,6 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   // S^T and G^T snapshots; during the scores of an exact chunk the lo tiles of qh,
   // kh and du live here instead
   __shared__ __attribute__((aligned(16))) uint8_t sX[2 * kSnapBytes];
-  __shared__ __attribute__((aligned(16))) float sNW[2][kD];  // norm weights of q and k (ones if absent)
   uint8_t* const sST = sX;
   uint8_t* const sGT = sX + kSnapBytes;
   uint8_t* const sQl = sX;
@@ -208,7 +223,7 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
   }
   if (tid < 2 * kD) {
     const float* nw = tid < kD ? p.qw : p.kw;
-    sNW[tid / kD][tid % kD] = nw ? nw[tid % kD] : 1.0f;
+    lds_st<float>(sQ, norm_weight_off(tid / kD, tid % kD), nw ? nw[tid % kD] : 1.0f);
   }
   const bool wgrad = kFuse && (bp.dq_w != nullptr || bp.dk_w != nullptr);
   float dw_acc = 0.f;  // with wgrad: thread tid < 256 sums dw[tid / 128][tid % 128] over the chunks
@@ -239,8 +254,8 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       // norm weights are re-read each chunk (from LDS) rather than held in registers
       float wq[8], wk[8];
       if (kWeights) {
-        lds_norm_weights(sNW[0], j, wq);
-        lds_norm_weights(sNW[1], j, wk);
+        pad_norm_weights(sQ, 0, j, wq);
+        pad_norm_weights(sQ, 1, j, wk);
       }
       norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
       norm_rope_rows<kWeights, 2, 32, kC, TilePi>(Kr, wk, p.eps, E2, L, rg, j, sK, exact ? sKl : nullptr);
@@ -287,14 +302,14 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     {
       bf16x8 nU[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_nat<TilePi>(sU, kk, 16 * w, g4, n16));
-      accumulate_nat(Gacc, sQ, nU, g4, n16);
+      for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_il<TilePi>(sU, kk, 16 * w, g4, n16));
+      accumulate_il(Gacc, sQ, nU, g4, n16);
     }
     __syncthreads();
     // ---- snapshots S^T[j][i] (S before the chunk) and G^T[j][i] (G after it), bf16
 #pragma unroll
     for (int rtk = 0; rtk < 8; ++rtk) {
-      const int off = tile_off(16 * w + n16, 16 * rtk + 4 * g4);
+      const int off = snap_off(16 * w + n16, 16 * rtk + 4 * g4);
       lds_st<uint2>(sST, off, make_uint2(pack2(Sacc[rtk][0], Sacc[rtk][1]), pack2(Sacc[rtk][2], Sacc[rtk][3])));
       lds_st<uint2>(sGT, off, make_uint2(pack2(Gacc[rtk][0], Gacc[rtk][1]), pack2(Gacc[rtk][2], Gacc[rtk][3])));
     }
@@ -354,16 +369,16 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat<TilePi>(sU, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_il<TilePi>(sU, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sP, kk, 16 * rt, g4, n16), acc[rt]);
+        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col_il(sP, kk, 16 * rt, g4, n16), acc[rt]);
       }
       store_rows4(bp.dv, acc, tl.base, t0, rs, col, nv, n16);
       // S before the next chunk: S += Kh^T V (dQh below reads S before the chunk from its snapshot)
       bf16x8 Vf[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_nat<TilePi>(sV, kk, 16 * w, g4, n16);
-      accumulate_nat(Sacc, sK, Vf, g4, n16);
+      for (int kk = 0; kk < 2; ++kk) Vf[kk] = col_il<TilePi>(sV, kk, 16 * w, g4, n16);
+      accumulate_il(Sacc, sK, Vf, g4, n16);
       // dKh = V G^T + (dP^T Qh)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -375,9 +390,9 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 a = col_nat<TilePi>(sQ, kk, 16 * w, g4, n16);
+        const bf16x8 a = col_il<TilePi>(sQ, kk, 16 * w, g4, n16);
 #pragma unroll
-        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col(sdP, kk, 16 * rt, g4, n16), acc[rt]);
+        for (int rt = 0; rt < 2 * kk + 2; ++rt) acc[rt] = mma(a, score_col_il(sdP, kk, 16 * rt, g4, n16), acc[rt]);
       }
       if (kFuse) {
 #pragma unroll
@@ -414,15 +429,15 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       const int col = 16 * w + 4 * g4;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        lds_st<uint2>(sX, tile_off(16 * rt + n16, col), dqp[rt]);
-        lds_st<uint2>(sX + kSnapBytes, tile_off(16 * rt + n16, col), dkp[rt]);
+        lds_st<uint2>(sX, snap_off(16 * rt + n16, col), dqp[rt]);
+        lds_st<uint2>(sX + kSnapBytes, snap_off(16 * rt + n16, col), dkp[rt]);
       }
       __syncthreads();
       float2 E[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
       float dw[2][8];
-      prologue_back_rows<kWeights>(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, sNW, dw);
+      prologue_back_rows<kWeights>(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, sQ, dw);
       if (wgrad) {
         // the wave's four row groups (lanes 16 apart) summed, then the 8 waves' parts in
         // the unused middle of the area, summed in a fixed order into dw_acc
@@ -435,9 +450,9 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
             x += __shfl_xor(x, 32);
             dw[a][e] = x;
           }
-        // [8 waves][2][128] between the dqh tile (first 17 KiB) and the dkh tile
-        float* part = reinterpret_cast<float*>(sX + kTileBytes);
-        static_assert(kTileBytes + kWaves * 2 * kD * 4 <= kSnapBytes, "weight parts overlap the dkh tile");
+        // [8 waves][2][128] between the dqh tile (the first 64 rows) and the dkh tile
+        float* part = reinterpret_cast<float*>(sX + kC * kSnapRow);
+        static_assert(kC * kSnapRow + kWaves * 2 * kD * 4 <= kSnapBytes, "weight parts overlap the dkh tile");
         if (lane < 16)
 #pragma unroll
           for (int a = 0; a < 2; ++a)

@@ -366,24 +366,43 @@ __device__ __forceinline__ bf16x8 score_row(const uint8_t* sP, int t, int kk, in
   return as_bf16x8(lds_ld<uint4>(sP, score_off(t, 32 * kk + 8 * g4)));
 }
 
-// Score column operand, tokens in natural order: lane n16 gets P[32kk + 8g + e][s0 + n16].
-__device__ __forceinline__ bf16x8 score_col(const uint8_t* sP, int kk, int s0, int g4, int n16) {
-  const int t0 = 32 * kk + 8 * g4 + (n16 >> 2), c = s0 + 4 * (n16 & 3);
-  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 4, c)));
+// ---- operands with tokens in interleaved order
+//
+// A contraction over the chunk's tokens may take them in any order that both of
+// its operands share.  For transposed reads the interleaved order is cheaper: lane
+// group g's K elements e = 0..7 are tokens 8g + 2(e % 4) + e / 4 of the 32-token
+// block, so each of the two transposed reads takes rows 8g, 8g+2, 8g+4, 8g+6 (or the
+// odd ones).  Rows two apart fall on different banks both in the 288-byte TilePi
+// tiles (whose 4-dim pieces lie 16 bytes apart) and in the 144-byte score tiles,
+// while four consecutive rows collide.  gfx950's conflict counter gives, per
+// transposed read, 6 cycles (natural order) against 2 (interleaved) on a TilePi
+// tile and 2 against 0 on a score tile.
+
+// Column operand, tokens interleaved: lane n16 gets X[32kk + 8g + 2(e%4) + e/4][c0 + n16].
+template <class Lay>
+__device__ __forceinline__ bf16x8 col_il(const uint8_t* tile, int kk, int c0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + 2 * (n16 >> 2), c = c0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(tile, Lay::off(t0, c)), lds_tr(tile, Lay::off(t0 + 1, c)));
+}
+
+// Score column operand, tokens interleaved: lane n16 gets P[32kk + 8g + 2(e%4) + e/4][s0 + n16].
+__device__ __forceinline__ bf16x8 score_col_il(const uint8_t* sP, int kk, int s0, int g4, int n16) {
+  const int t0 = 32 * kk + 8 * g4 + 2 * (n16 >> 2), c = s0 + 4 * (n16 & 3);
+  return as_bf16x8(lds_tr(sP, score_off(t0, c)), lds_tr(sP, score_off(t0 + 1, c)));
 }
 
 // acc[rtk] (rows 16 rtk .. + 16 of X = A^T B, this wave's 16 columns) += over one
 // chunk, A a TilePi tile whose 128 columns are the rows of X, B the chunk's column
-// operand (col_nat, tokens in natural order).
-__device__ __forceinline__ void accumulate_nat(f32x4 (&acc)[8], const uint8_t* A, const bf16x8 (&Bop)[2],
-                                               int g4, int n16) {
+// operand with tokens interleaved (col_il).
+__device__ __forceinline__ void accumulate_il(f32x4 (&acc)[8], const uint8_t* A, const bf16x8 (&Bop)[2],
+                                              int g4, int n16) {
 #pragma unroll
   for (int kk = 0; kk < kC / 32; ++kk) {
-    const int t0 = 32 * kk + 8 * g4 + (n16 >> 2);
+    const int t0 = 32 * kk + 8 * g4 + 2 * (n16 >> 2);
 #pragma unroll
     for (int rtk = 0; rtk < 8; ++rtk) {
       const int c = 16 * rtk + 4 * (n16 & 3);
-      const bf16x8 a = as_bf16x8(lds_tr(A, TilePi::off(t0, c)), lds_tr(A, TilePi::off(t0 + 4, c)));
+      const bf16x8 a = as_bf16x8(lds_tr(A, TilePi::off(t0, c)), lds_tr(A, TilePi::off(t0 + 1, c)));
       acc[rtk] = mma(a, Bop[kk], acc[rtk]);
     }
   }
