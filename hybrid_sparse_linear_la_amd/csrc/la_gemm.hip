@@ -10,7 +10,7 @@
 // nsplit] tensors (the fused q/k/v/gate projection writes q, k, v, g directly).
 // Requires K % 64 == 0 and (N / nsplit) % 256 == 0; M is arbitrary.
 //
-// Workgroup tile 256 x 256, K step 64, LDS double-buffered (144 KiB).  Eight
+// Workgroup tile 256 x 256, K step 64, LDS double-buffered (160 KiB).  Eight
 // waves, wave (wm, wn) computes rows [64 wm, 64 wm + 64) x columns
 // [128 wn, 128 wn + 128) of the tile as 4 x 8 accumulator tiles of
 // v_mfma_f32_16x16x32_bf16.  Both operands are K-contiguous, so every MFMA
@@ -25,7 +25,10 @@ namespace {
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kGemmThreads = 512;
-constexpr int kLdsRow = kBK * 2 + 16;          // 144-byte LDS rows: 16 rows hit distinct banks
+// 160-byte LDS rows: the operand reads (16 rows x 4 lane groups, 16 bytes each) are
+// conflict-free there, while 144-byte rows cost 4 conflict cycles per read (gfx950
+// counters); the 16-byte staging stores cost the same at both strides.
+constexpr int kLdsRow = kBK * 2 + 32;
 constexpr int kLdsTile = kBM * kLdsRow;        // one 256 x 64 bf16 tile
 constexpr int kChunksPerThread = kBM * kBK / 8 / kGemmThreads;  // 16-byte pieces of a tile per thread (4)
 
