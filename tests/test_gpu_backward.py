@@ -98,6 +98,26 @@ def test_backward_rejects_bad_arguments(la):
         la.backward(q, k, v, g, d_o[:, :32].contiguous())
 
 
+@pytest.mark.parametrize("given", ["q", "k"])
+@pytest.mark.parametrize("weight_grads", [False, True])
+def test_backward_with_one_norm_weight(la, given, weight_grads):
+    """Only one of the two norm weights given: the other acts as ones (the chunk
+    kernel keeps both vectors in LDS and fills the absent one with ones)."""
+    B, T, H = 1, 700, 4
+    print(f"backward case B={B} T={T} H={H} only {given}_norm_w weight_grads={weight_grads}", flush=True)
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 95, 0.2, 0.3, True)
+    if given == "q":
+        kw = None
+    else:
+        qw = None
+    grads = la.backward(q, k, v, g, d_o, S_in=S_in, dS_out=dS_out, pos0=33, q_norm_w=qw, k_norm_w=kw,
+                        weight_grads=weight_grads)
+    torch.cuda.synchronize()
+    ref_qw = qw if qw is not None else torch.ones(D, device="cuda")
+    ref_kw = kw if kw is not None else torch.ones(D, device="cuda")
+    _check(grads, q, k, v, g, d_o, S_in, dS_out, 33, ref_qw, ref_kw, weight_grads)
+
+
 def test_backward_with_more_workgroups_than_weight_parts(la):
     """More (b, h, segment) workgroups than per-workgroup weight-gradient parts
     (2048): the prologue backward runs in its own kernel."""
