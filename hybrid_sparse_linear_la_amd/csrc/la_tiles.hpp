@@ -24,10 +24,15 @@ constexpr int kExactRows = 16;              // rows whose scores use the hi/lo s
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 
-// [64][128] bf16 row tile with 272-byte rows: consecutive rows start 16 bytes
-// apart in the bank space, so the 8-byte operand reads (16 rows x 4 lane
-// groups), the transposed reads (4 rows x 4 groups) and the staging writes all
-// spread over the banks, and every offset is linear (immediate offsets).
+// [64][128] bf16 row tile with 272-byte rows (16-byte aligned, linear offsets).
+// Measured on gfx950 at this stride: staging writes (16 lanes per row) and
+// transposed reads are near conflict-free (0 and 2 conflict cycles per
+// instruction), 8-byte stores of an MFMA result (16 rows x 4 lane groups) cost 8,
+// and 8- and 16-byte reads in that row pattern take about twice and 1.5 times
+// their conflict-free time.  No stride suits every access: 16-byte row reads are
+// conflict-free only at strides of 32 mod 64 bytes (288), where the 8-byte row
+// accesses conflict heavily, and 280 serves the 8-byte accesses but breaks the
+// 16-byte alignment.
 __device__ __forceinline__ int tile_off(int t, int d) { return t * kRowBytes + 2 * d; }
 
 // Row-tile layouts for the staging helpers.  TileNat is the tile above.  TilePi
