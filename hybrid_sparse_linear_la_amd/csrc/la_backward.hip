@@ -305,7 +305,8 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       for (int kk = 0; kk < 2; ++kk) nU[kk] = negate(col_il<TilePi>(sU, kk, 16 * w, g4, n16));
       accumulate_il(Gacc, sQ, nU, g4, n16);
     }
-    __syncthreads();
+    // the snapshot area holds an exact chunk's lo tiles until every wave's scores are done
+    if (exact) __syncthreads();
     // ---- snapshots S^T[j][i] (S before the chunk) and G^T[j][i] (G after it), bf16
 #pragma unroll
     for (int rtk = 0; rtk < 8; ++rtk) {
