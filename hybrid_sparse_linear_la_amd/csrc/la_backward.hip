@@ -23,9 +23,10 @@
 // the segment's first token, from the suffix scan) and subtracts Qh^T dU from G
 // chunk by chunk.  Wave w owns columns [16w, 16w + 16) of every output and of the
 // S, G accumulators; S and G are also written to LDS as bf16 (transposed) so the
-// S^T and G^T products can read any row.  dqh, dkh leave in bf16 for
-// la_prologue_backward_kernel, which rotates them back and applies the RMSNorm
-// Jacobian.  Chunks at the start and end of a sequence form their scores from a
+// S^T and G^T products can read any row.  dqh and dkh, rounded to bf16, go
+// through the prologue backward (rotated back, then the RMSNorm Jacobian): inside
+// this kernel for grids of up to 2048 workgroups, else in
+// la_prologue_backward_kernel.  Chunks at the start and end of a sequence form their scores from a
 // hi/lo split of qh, kh and du: rows there sum few scores, and the bf16 rounding
 // of the operands would otherwise dominate their error.
 #include "la_device.hpp"
