@@ -95,10 +95,14 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_kernel(LinearParams p)
       for (int j = 0; j < 8; ++j)
         wb[j] = as_bf16x8(lds_ld<uint4>(sB[buf], (128 * wn + 16 * j + n16) * kLdsRow + 64 * kk + 16 * g4));
       // D[4 g + r][n16] = sum_k W[col 4 g + r][k] x[row n16][k] = y[row n16][col 4 g + r]
+      // The wave issuing its MFMA block takes issue priority over the SIMD's other wave
+      // (then busy with LDS reads, loads or stores): 5-6% on the projection shapes.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[j], xa[i], acc[i][j]);
+      __builtin_amdgcn_s_setprio(0);
     }
     if (kt + 1 < nk) stage(buf ^ 1);
     __syncthreads();
