@@ -39,6 +39,7 @@ SPARSE_BLOCK = 64
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
     4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",
+    8: "LA_ERR_CAPTURING",
 }
 
 _vp = ctypes.c_void_p
@@ -117,6 +118,10 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _on_gpu(t) -> bool:
+    return t.is_cuda
+
+
 def _act(name, t, ndim):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -124,15 +129,37 @@ def _act(name, t, ndim):
         raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
     if t.dim() != ndim or t.shape[-1] != HEAD_DIM:
         raise ValueError(f"{name} must have {ndim} dims with last dim {HEAD_DIM}, got {tuple(t.shape)}")
-    if not t.is_cuda or not t.is_contiguous():
+    if not _on_gpu(t) or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous GPU tensor")
 
 
-def _f32(name, t, shape):
+def _like(name, t, ref, dtype=torch.bfloat16):
+    """An output the caller supplies: the library writes as many bytes as ``ref``
+    describes, so its dtype, shape and device must be exactly ``ref``'s."""
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(ref.shape) \
+            or t.device != ref.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(ref.shape)} "
+                         f"on {ref.device}")
+
+
+def _f32(name, t, shape, device):
     if t is None:
         return
-    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_cuda or not t.is_contiguous():
-        raise ValueError(f"{name} must be a contiguous fp32 GPU tensor of shape {tuple(shape)}")
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) \
+            or not _on_gpu(t) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {tuple(shape)} on {device}")
+
+
+def _workspace(t, need, device):
+    """The caller's workspace if it is a large enough contiguous buffer on the
+    device, else a new one."""
+    if t is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    if not isinstance(t, torch.Tensor) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if t.numel() * t.element_size() < need:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    return t
 
 
 def prefill_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, chunk: int = 0) -> int:
@@ -153,23 +180,23 @@ def prefill(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: 
         if t.shape != q.shape or t.device != q.device:
             raise ValueError(f"{n} must match q's shape and device")
     B, T, H, D = q.shape
-    _f32("S_in", S_in, (B, H, D, D))
-    _f32("q_norm_w", q_norm_w, (D,))
-    _f32("k_norm_w", k_norm_w, (D,))
+    dev = q.device
+    _f32("S_in", S_in, (B, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _act("out", out, 4)
+        _like("out", out, q)
     if S_out is None:
-        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     else:
-        _f32("S_out", S_out, (B, H, D, D))
+        _f32("S_out", S_out, (B, H, D, D), dev)
     need = int(lib.la_prefill_workspace_bytes(B, T, H, D, chunk))
     if need == 0:
         status = 3 if (D != HEAD_DIM or chunk not in SUPPORTED_CHUNKS) else 2
         raise LAError(status, lib.la_status_string(status).decode())
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(S_out), _ptr(out),
             B, T, H, D, int(pos0), int(chunk), float(rope_base), float(rms_eps),
             _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
@@ -214,23 +241,23 @@ def prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None, chunk: int =
     nseq = len(cu_seqlens) - 1
     cu = _host_array("cu_seqlens", cu_seqlens, ctypes.c_int32, nseq + 1)
     p0 = None if pos0 is None else _host_array("pos0", pos0, ctypes.c_int64, nseq)
-    _f32("S_in", S_in, (nseq, H, D, D))
-    _f32("q_norm_w", q_norm_w, (D,))
-    _f32("k_norm_w", k_norm_w, (D,))
+    dev = q.device
+    _f32("S_in", S_in, (nseq, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _act("out", out, 3)
+        _like("out", out, q)
     if S_out is None:
-        S_out = torch.empty((nseq, H, D, D), dtype=torch.float32, device=q.device)
+        S_out = torch.empty((nseq, H, D, D), dtype=torch.float32, device=dev)
     else:
-        _f32("S_out", S_out, (nseq, H, D, D))
+        _f32("S_out", S_out, (nseq, H, D, D), dev)
     need = int(lib.la_prefill_varlen_workspace_bytes(nseq, cu, H, D, chunk))
     if need == 0:
         status = 3 if (D != HEAD_DIM or chunk not in SUPPORTED_CHUNKS) else 2
         raise LAError(status, lib.la_status_string(status).decode())
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.la_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), cu, p0, _ptr(S_in), _ptr(S_out),
                                  _ptr(out), nseq, total_T, H, D, int(chunk), float(rope_base),
                                  float(rms_eps), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
@@ -239,7 +266,7 @@ def prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None, chunk: int =
 
 
 def _bf16_2d(name, t):
-    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not _on_gpu(t) or not t.is_contiguous():
         raise ValueError(f"{name} must be a contiguous bf16 GPU tensor")
 
 
@@ -249,14 +276,16 @@ def linear(x, w, out=None):
     _bf16_2d("w", w)
     if w.dim() != 2 or x.shape[-1] != w.shape[1]:
         raise ValueError(f"x [..., K] and w [N, K] do not match: {tuple(x.shape)}, {tuple(w.shape)}")
+    if w.device != x.device:
+        raise ValueError("x and w must be on the same device")
     N, K = w.shape
     M = x.numel() // K
     if out is None:
         out = torch.empty(tuple(x.shape[:-1]) + (N,), dtype=torch.bfloat16, device=x.device)
     else:
         _bf16_2d("out", out)
-        if out.numel() != M * N:
-            raise ValueError("out has the wrong size")
+        if out.numel() != M * N or out.shape[-1] != N or out.device != x.device:
+            raise ValueError(f"out must hold [..., {N}] with {M * N} elements on {x.device}")
     _check(library().la_linear(_ptr(x), _ptr(w), _ptr(out), M, N, K, _stream(x.device)))
     return out
 
@@ -280,22 +309,24 @@ def layer_forward(x, w_qkvg, w_o, S_in=None, pos0: int = 0, chunk: int = 0, rope
     if HD % HEAD_DIM or tuple(w_qkvg.shape) != (4 * HD, hidden) or tuple(w_o.shape) != (hidden, HD):
         raise ValueError("weights must be w_qkvg [4 H 128, hidden] and w_o [hidden, H 128]")
     H, D = HD // HEAD_DIM, HEAD_DIM
-    _f32("S_in", S_in, (B, H, D, D))
-    _f32("q_norm_w", q_norm_w, (D,))
-    _f32("k_norm_w", k_norm_w, (D,))
+    dev = x.device
+    if w_qkvg.device != dev or w_o.device != dev:
+        raise ValueError("x and the weights must be on the same device")
+    _f32("S_in", S_in, (B, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
     if out is None:
         out = torch.empty_like(x)
     else:
-        _bf16_2d("out", out)
+        _like("out", out, x)
     if S_out is None:
-        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=x.device)
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
     else:
-        _f32("S_out", S_out, (B, H, D, D))
+        _f32("S_out", S_out, (B, H, D, D), dev)
     need = int(lib.la_layer_workspace_bytes(B, T, H, D, chunk))
     if need == 0:
         raise LAError(2, lib.la_status_string(2).decode())
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.la_layer_forward(_ptr(x), _ptr(w_qkvg), _ptr(w_o), _ptr(S_in), _ptr(S_out), _ptr(out), B, T,
                                 hidden, H, D, int(pos0), int(chunk), float(rope_base), float(rms_eps),
                                 _ptr(q_norm_w), _ptr(k_norm_w), _ptr(workspace),
@@ -320,10 +351,11 @@ def backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0: int = 0, chunk: i
         if t.shape != q.shape or t.device != q.device:
             raise ValueError(f"{n} must match q's shape and device")
     B, T, H, D = q.shape
-    _f32("S_in", S_in, (B, H, D, D))
-    _f32("dS_out", dS_out, (B, H, D, D))
-    _f32("q_norm_w", q_norm_w, (D,))
-    _f32("k_norm_w", k_norm_w, (D,))
+    dev = q.device
+    _f32("S_in", S_in, (B, H, D, D), dev)
+    _f32("dS_out", dS_out, (B, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
     out = {n: torch.empty_like(q) for n in ("dq", "dk", "dv", "dgate")}
     out["dS_in"] = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
     if weight_grads:
@@ -333,8 +365,7 @@ def backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0: int = 0, chunk: i
     if need == 0:
         status = 3 if (D != HEAD_DIM or chunk not in (0, 64)) else 2
         raise LAError(status, lib.la_status_string(status).decode())
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, dev)
     _check(lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(d_o), _ptr(dS_out),
                            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
                            _ptr(out["dS_in"]), _ptr(out.get("dq_norm_w")), _ptr(out.get("dk_norm_w")), B, T, H, D,
@@ -354,13 +385,16 @@ def decode_step(q, k, v, gate, S, pos: int, rope_base: float = 10000.0, rms_eps:
         if t.shape != q.shape or t.device != q.device:
             raise ValueError(f"{n} must match q's shape and device")
     B, H, D = q.shape
-    _f32("S", S, (B, H, D, D))
-    _f32("q_norm_w", q_norm_w, (D,))
-    _f32("k_norm_w", k_norm_w, (D,))
+    dev = q.device
+    if S is None:
+        raise ValueError("S must be given (it is updated in place)")
+    _f32("S", S, (B, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
     if out is None:
         out = torch.empty_like(q)
     else:
-        _act("out", out, 3)
+        _like("out", out, q)
     _check(lib.la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S), _ptr(out), B, H, D,
                               int(pos), float(rope_base), float(rms_eps), _ptr(q_norm_w),
                               _ptr(k_norm_w), _stream(q.device)))
@@ -384,14 +418,13 @@ def sparse_prefill(q, k, v, gate, topk: int = 16, return_sel: bool = False, out=
             raise ValueError(f"{n} must match q's shape and device")
     B, T, H, D = q.shape
     o = torch.empty_like(q) if out is None else out
-    _act("out", o, 4)
+    _like("out", o, q)
     nqb = -(-T // SPARSE_BLOCK)
     sel = torch.empty((B, H, nqb, topk), dtype=torch.int32, device=q.device) if return_sel else None
     need = int(lib.la_sparse_prefill_workspace_bytes(B, T, H, D, 0, topk))
     if need == 0:
         raise LAError(3, lib.la_status_string(3).decode())
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
     _check(lib.la_sparse_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(o), _ptr(sel), B, T, H, D, 0,
                                  int(topk), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(q.device)))
@@ -407,7 +440,7 @@ def sparse_block_means(k_cache, means=None, first_block: int = 0, nblocks=None):
     shape = (B, H, Tmax // SPARSE_BLOCK, D)
     if means is None:
         means = torch.zeros(shape, dtype=torch.float32, device=k_cache.device)
-    _f32("means", means, shape)
+    _f32("means", means, shape, k_cache.device)
     if nblocks is None:
         nblocks = Tmax // SPARSE_BLOCK - first_block
     _check(lib.la_sparse_block_means(_ptr(k_cache), _ptr(means), B, Tmax, H, D, 0, int(first_block), int(nblocks),
@@ -427,12 +460,17 @@ def sparse_decode(q, k_cache, v_cache, means, gate, lens, topk: int = 16, return
     _act("k_cache", k_cache, 4)
     _act("v_cache", v_cache, 4)
     B, Tmax, H, D = k_cache.shape
+    dev = q.device
     if v_cache.shape != k_cache.shape or q.shape != (B, H, D) or gate.shape != q.shape:
         raise ValueError("shapes of q, gate, k_cache, v_cache disagree")
-    _f32("means", means, (B, H, Tmax // SPARSE_BLOCK, D))
-    if lens.dtype != torch.int32 or tuple(lens.shape) != (B,) or not lens.is_cuda:
-        raise ValueError("lens must be an int32 GPU tensor of shape [B]")
+    if any(t.device != dev for t in (gate, k_cache, v_cache)):
+        raise ValueError("q, gate, k_cache and v_cache must be on the same device")
+    _f32("means", means, (B, H, Tmax // SPARSE_BLOCK, D), dev)
+    if not isinstance(lens, torch.Tensor) or lens.dtype != torch.int32 or tuple(lens.shape) != (B,) \
+            or lens.device != dev or not lens.is_contiguous():
+        raise ValueError(f"lens must be a contiguous int32 tensor of shape [{B}] on {dev}")
     o = torch.empty_like(q) if out is None else out
+    _like("out", o, q)
     sel = torch.empty((B, H, topk), dtype=torch.int32, device=q.device) if return_sel else None
     _check(lib.la_sparse_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(means), _ptr(gate), _ptr(lens),
                                 _ptr(o), _ptr(sel), B, Tmax, H, D, 0, int(topk), _stream(q.device)))

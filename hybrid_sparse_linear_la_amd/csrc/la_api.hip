@@ -154,7 +154,7 @@ using namespace la;
 
 extern "C" {
 
-int la_version(void) { return 100; }
+int la_version(void) { return 200; }
 
 const char* la_status_string(la_status s) {
   switch (s) {
@@ -166,6 +166,7 @@ const char* la_status_string(la_status s) {
     case LA_ERR_ALIASING: return "LA_ERR_ALIASING: an output overlaps another argument";
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
     case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
+    case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
   }
   return "unknown la_status";
 }
@@ -327,13 +328,20 @@ la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v
     if (overlaps(workspace, vp.plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
   if (workspace_bytes < vp.plan.ws_bytes) return LA_ERR_WORKSPACE;
 
+  // The table copy below reads host memory owned by this call; a graph captured
+  // around it would replay the copy from freed memory, so a capturing stream is
+  // refused before anything is enqueued.
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &capture) != hipSuccess) return LA_ERR_HIP;
+  if (capture != hipStreamCaptureStatusNone) return LA_ERR_CAPTURING;
+
   // the tables go to the front of the workspace, in stream order
   std::vector<uint8_t> tables(vp.table_bytes, 0);
   if (!vp.segs.empty()) memcpy(tables.data(), vp.segs.data(), vp.segs.size() * sizeof(SegDesc));
   memcpy(tables.data() + vp.seq_off, vp.seqs.data(), vp.seqs.size() * sizeof(SeqDesc));
   if (!vp.decs.empty()) memcpy(tables.data() + vp.dec_off, vp.decs.data(), vp.decs.size() * sizeof(DecDesc));
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const hipStream_t s = static_cast<hipStream_t>(stream);
   if (hipMemcpyAsync(ws, tables.data(), tables.size(), hipMemcpyHostToDevice, s) != hipSuccess) return LA_ERR_HIP;
 
   RopeFreqs freqs;

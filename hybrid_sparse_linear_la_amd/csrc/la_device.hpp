@@ -35,14 +35,6 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          false);
 }
 
-// Two floats -> packed f16 (round toward zero), and back.
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
-__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
-
 // D = A(16x32) * B(32x16) + C with bf16 inputs and fp32 accumulation.
 // Lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16] for
 // e = 0..7, and receives D[4 (l / 16) + r][l % 16] for r = 0..3.

@@ -15,7 +15,7 @@
 //      (plus S_in) in place, and the final state -> S_out.
 //   3. la_chunk_output_kernel: one workgroup per (b, h, segment) starts from its
 //      segment's prefix state and walks the chunks.  Eight producer waves apply
-//      QK-RMSNorm + RoPE to q, k and the sigmoid to the gate of chunk c+1 and
+//      QK-RMSNorm + RoPE to q, k and the sigmoid to the gate of chunk c+1 (bf16) and
 //      stage the tiles into one half of a ping-pong LDS buffer (their global
 //      loads run two chunks further ahead), while four consumer waves run all
 //      the MFMA work of chunk c from the other half: the masked scores
@@ -302,8 +302,8 @@ __device__ __forceinline__ void consume_phase_b(const uint8_t* K, const uint8_t*
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       const uint2 sg = lds_ld<uint2>(G, tile_off(t, 32 * w + 16 * dt + 4 * g4));
-      const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * f16_lo(sg.x), Oacc[dt][rt][1] * f16_hi(sg.x)),
-                                   pack2(Oacc[dt][rt][2] * f16_lo(sg.y), Oacc[dt][rt][3] * f16_hi(sg.y)));
+      const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * bf2f_lo(sg.x), Oacc[dt][rt][1] * bf2f_hi(sg.x)),
+                                   pack2(Oacc[dt][rt][2] * bf2f_lo(sg.y), Oacc[dt][rt][3] * bf2f_hi(sg.y)));
       if (t < nv) *reinterpret_cast<uint2*>(dst + 16 * dt) = out;
     }
   }
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kOutThreads) void la_chunk_output_kernel(PrefillPar
   __shared__ __attribute__((aligned(16))) uint8_t sQ[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), f16
+  __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), bf16
   __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];

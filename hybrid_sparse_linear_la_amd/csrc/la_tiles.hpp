@@ -106,17 +106,18 @@ __device__ __forceinline__ void store_rows_masked(uint8_t* tile, const Rows<M>& 
   }
 }
 
-// sigmoid of the gate logits, staged as f16 (the value lies in (0, 1); f16 keeps
-// 11 significant bits, round toward zero).
+// sigmoid of the gate logits, staged as bf16 (round to nearest even: relative
+// error at most 2^-9, and bf16 keeps fp32's exponent range, so gates down to the
+// fp32 underflow of the sigmoid keep their relative precision).
 template <int M, int kStep>
 __device__ __forceinline__ void sigmoid_stage(uint8_t* tile, const Rows<M>& R, int rg, int j) {
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     const uint2 a = R.lo[m], b = R.hi[m];
-    const uint2 lo = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(a.x)), sigmoidf_(bf2f_hi(a.x))),
-                                pack_f16x2(sigmoidf_(bf2f_lo(a.y)), sigmoidf_(bf2f_hi(a.y))));
-    const uint2 hi = make_uint2(pack_f16x2(sigmoidf_(bf2f_lo(b.x)), sigmoidf_(bf2f_hi(b.x))),
-                                pack_f16x2(sigmoidf_(bf2f_lo(b.y)), sigmoidf_(bf2f_hi(b.y))));
+    const uint2 lo = make_uint2(pack2(sigmoidf_(bf2f_lo(a.x)), sigmoidf_(bf2f_hi(a.x))),
+                                pack2(sigmoidf_(bf2f_lo(a.y)), sigmoidf_(bf2f_hi(a.y))));
+    const uint2 hi = make_uint2(pack2(sigmoidf_(bf2f_lo(b.x)), sigmoidf_(bf2f_hi(b.x))),
+                                pack2(sigmoidf_(bf2f_lo(b.y)), sigmoidf_(bf2f_hi(b.y))));
     lds_st<uint2>(tile, tile_off(rg + kStep * m, 4 * j), lo);
     lds_st<uint2>(tile, tile_off(rg + kStep * m, kHalf + 4 * j), hi);
   }

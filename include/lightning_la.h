@@ -44,6 +44,9 @@
  * other than LA_OK nothing was launched and no output was touched (except
  * LA_ERR_HIP, returned when a launch itself fails; device faults surface at
  * the caller's synchronization).  No C++ exception crosses this interface.
+ * Graph capture: every entry point except la_prefill_varlen only enqueues
+ * kernels and can be captured into a HIP graph; la_prefill_varlen refuses a
+ * capturing stream with LA_ERR_CAPTURING.
  */
 #ifndef LIGHTNING_LA_H
 #define LIGHTNING_LA_H
@@ -64,7 +67,8 @@ typedef enum {
   LA_ERR_ALIGNMENT = 4,   /* a pointer is not 16-byte aligned                          */
   LA_ERR_ALIASING = 5,    /* o overlaps an input, or S_out overlaps an activation      */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_prefill_workspace_bytes */
-  LA_ERR_HIP = 7          /* a kernel launch failed                                    */
+  LA_ERR_HIP = 7,         /* a kernel launch failed                                    */
+  LA_ERR_CAPTURING = 8    /* la_prefill_varlen on a stream that is capturing a graph   */
 } la_status;
 
 typedef uint16_t la_bf16; /* raw bfloat16 bits */
@@ -148,6 +152,11 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
  * of the workspace with hipMemcpyAsync on `stream` before the kernels, so it
  * returns once that (pageable) copy has been staged.  Errors as for la_prefill;
  * LA_ERR_BAD_SHAPE also covers malformed cu_seqlens.
+ * Graph capture: the table copy reads host memory that lives only for the
+ * call, so the call cannot be captured into a HIP graph.  On a stream that is
+ * capturing (hipStreamIsCapturing) it returns LA_ERR_CAPTURING after the other
+ * checks and enqueues nothing.  Every other entry point only enqueues kernels
+ * (and reads no host memory at run time), so those can be captured.
  */
 size_t la_prefill_varlen_workspace_bytes(int nseq, const int32_t* cu_seqlens, int H, int D, int chunk);
 

@@ -34,12 +34,13 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.la_version() == 100
+    assert lib.la_version() == 200
 
 
 def test_status_strings(lib):
     for s, name in ((0, b"LA_OK"), (1, b"LA_ERR_NULL_PTR"), (2, b"LA_ERR_BAD_SHAPE"), (3, b"LA_ERR_UNSUPPORTED"),
-                    (4, b"LA_ERR_ALIGNMENT"), (5, b"LA_ERR_ALIASING"), (6, b"LA_ERR_WORKSPACE"), (7, b"LA_ERR_HIP")):
+                    (4, b"LA_ERR_ALIGNMENT"), (5, b"LA_ERR_ALIASING"), (6, b"LA_ERR_WORKSPACE"), (7, b"LA_ERR_HIP"),
+                    (8, b"LA_ERR_CAPTURING")):
         assert lib.la_status_string(s).startswith(name)
     assert lib.la_status_string(99) == b"unknown la_status"
 
