@@ -8,6 +8,7 @@ runs in the library's HIP kernels; there is no fallback path.  If the library
 is missing, every call raises.
 
     o, S_out = prefill(q, k, v, gate, S_in=None, pos0=0)
+    o, S_out = prefill_noalloc(q, k, v, gate, S_in=None, pos0=0)   # no workspace
     o = decode_step(q, k, v, gate, S, pos)        # S updated in place
     o, S_out = prefill_varlen(q, k, v, gate, cu_seqlens, pos0=None, S_in=None)
     y = linear(x, w)                              # y = x w^T
@@ -21,7 +22,7 @@ import os
 
 import torch
 
-__all__ = ["prefill", "decode_step", "prefill_varlen", "linear", "layer_forward", "backward",
+__all__ = ["prefill", "prefill_noalloc", "decode_step", "prefill_varlen", "linear", "layer_forward", "backward",
            "prefill_workspace_bytes", "backward_workspace_bytes",
            "layer_workspace_bytes",
            "prefill_varlen_workspace_bytes", "LAError", "library", "lib_path",
@@ -39,7 +40,7 @@ SPARSE_BLOCK = 64
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
     4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",
-    8: "LA_ERR_CAPTURING",
+    8: "LA_ERR_CAPTURING", 9: "LA_ERR_SCRATCH",
 }
 
 _vp = ctypes.c_void_p
@@ -71,6 +72,9 @@ def library():
         lib.la_prefill_profiled.restype = ctypes.c_int
         lib.la_prefill_profiled.argtypes = lib.la_prefill.argtypes + [ctypes.POINTER(ctypes.c_void_p),
                                                                       ctypes.c_int]
+        lib.la_prefill_noalloc.restype = ctypes.c_int
+        lib.la_prefill_noalloc.argtypes = [_vp] * 7 + [ctypes.c_int] * 4 + [
+            ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
         lib.la_prefill_varlen_workspace_bytes.restype = ctypes.c_size_t
         lib.la_prefill_varlen_workspace_bytes.argtypes = [ctypes.c_int, _vp, ctypes.c_int, ctypes.c_int,
                                                           ctypes.c_int]
@@ -206,6 +210,36 @@ def prefill(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: 
     else:
         arr = (ctypes.c_void_p * len(events))(*events)
         _check(lib.la_prefill_profiled(*args, arr, len(events)))
+    return out, S_out
+
+
+def prefill_noalloc(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: float = 10000.0,
+                    rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None, out=None, S_out=None):
+    """``prefill`` through la_prefill_noalloc: no workspace, the library's static
+    device scratch instead (B * H <= 1024).  Pass ``out`` and ``S_out`` to make the
+    call allocate nothing at all (e.g. under graph capture).  Calls that overlap in
+    time on one GPU share that scratch and race."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
+        _act(n, t, 4)
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{n} must match q's shape and device")
+    B, T, H, D = q.shape
+    dev = q.device
+    _f32("S_in", S_in, (B, H, D, D), dev)
+    _f32("q_norm_w", q_norm_w, (D,), dev)
+    _f32("k_norm_w", k_norm_w, (D,), dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _like("out", out, q)
+    if S_out is None:
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    else:
+        _f32("S_out", S_out, (B, H, D, D), dev)
+    _check(lib.la_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(S_out), _ptr(out),
+                                  B, T, H, D, int(pos0), int(chunk), float(rope_base), float(rms_eps),
+                                  _ptr(q_norm_w), _ptr(k_norm_w), _stream(dev)))
     return out, S_out
 
 

@@ -6,6 +6,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -88,6 +90,24 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   return true;
 }
 
+// A plan whose workspace holds at most max_states segment states: the planner's
+// segments, or fewer and longer ones when those would not fit.  False when even
+// one segment per (b, h) does not fit.
+bool cap_plan(int B, int H, int64_t max_states, PrefillPlan* plan) {
+  const int64_t bh = (int64_t)B * H;
+  if (bh > max_states) return false;
+  if (bh * plan->nseg <= max_states) return true;
+  const int64_t sub = plan->C / 64;
+  const int64_t max_seg = max_states / bh;
+  int64_t cps = (plan->nchunks + max_seg - 1) / max_seg;
+  cps = (cps + sub - 1) / sub * sub;
+  plan->cps = (int)cps;
+  plan->nseg = (int)((plan->nchunks + cps - 1) / cps);
+  plan->nwork = (int64_t)B * plan->nseg;
+  plan->ws_bytes = (size_t)(bh * plan->nseg) * kHeadDim * kHeadDim * sizeof(float);
+  return true;
+}
+
 // Host plan of a variable-length batch: the segment, sequence and single-token
 // tables and where they and the segment states sit in the workspace.
 struct VarlenPlan {
@@ -167,6 +187,7 @@ const char* la_status_string(la_status s) {
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
     case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
     case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
+    case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: B * H exceeds the 1024 states of la_prefill_noalloc's static scratch";
   }
   return "unknown la_status";
 }
@@ -182,13 +203,17 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
                               la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
                               float rope_base, float rms_eps, const float* q_norm_w,
                               const float* k_norm_w, void* workspace, size_t workspace_bytes,
-                              void* stream, hipEvent_t const* events) {
+                              void* stream, hipEvent_t const* events,
+                              const PrefillPlan* given_plan = nullptr) {
   if (!q || !k || !v || !gate_logits || !S_out || !o || !workspace) return LA_ERR_NULL_PTR;
   if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
   if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
   if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
   PrefillPlan plan;
-  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  if (given_plan != nullptr)
+    plan = *given_plan;
+  else if (!plan_prefill(B, T, H, chunk, &plan))
+    return LA_ERR_BAD_SHAPE;
   const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
@@ -252,6 +277,78 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
   return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
                       rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream,
                       reinterpret_cast<hipEvent_t const*>(events));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Scratch of la_prefill_noalloc: a static device array holding up to
+// kScratchStates fp32 D x D segment states.  Every GPU the library runs on holds
+// its own copy at its own address, for the life of the process.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is passed to kernels.
+namespace la {
+namespace {
+constexpr int64_t kScratchStates = 1024;
+constexpr size_t kScratchBytes = (size_t)kScratchStates * kHeadDim * kHeadDim * sizeof(float);  // 64 MiB
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+}  // namespace la
+
+static __device__ __align__(256) uint8_t scratch[la::kScratchBytes];
+
+namespace la {
+namespace {
+// The device address of this device's scratch, for the device `stream` belongs
+// to (the current device for the null stream).
+la_status scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return LA_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return LA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return LA_ERR_HIP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return LA_ERR_HIP;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return LA_ERR_HIP;
+      const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (cur != dev && hipSetDevice(cur) != hipSuccess) return LA_ERR_HIP;
+      if (err != hipSuccess || p == nullptr) return LA_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LA_OK;
+}
+}  // namespace
+}  // namespace la
+
+extern "C" {
+
+la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                             const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
+                             int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
+                             float rms_eps, const float* q_norm_w, const float* k_norm_w, void* stream) {
+  if (!q || !k || !v || !gate_logits || !S_out || !o) return LA_ERR_NULL_PTR;
+  if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  if (!cap_plan(B, H, kScratchStates, &plan)) return LA_ERR_SCRATCH;
+  void* ws = nullptr;
+  const la_status got = scratch_address(static_cast<hipStream_t>(stream), &ws);
+  if (got != LA_OK) return got;
+  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base, rms_eps,
+                      q_norm_w, k_norm_w, ws, kScratchBytes, stream, nullptr, &plan);
 }
 
 la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,

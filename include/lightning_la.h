@@ -35,7 +35,8 @@
  *
  * Ownership and asynchrony: every pointer (except where noted) is a device
  * pointer owned by the caller.  The library allocates no memory and keeps no
- * mutable global state; calls are re-entrant.  A call validates its arguments,
+ * mutable global state (except la_prefill_noalloc's static scratch, below);
+ * calls are re-entrant.  A call validates its arguments,
  * enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL = the
  * null stream) and returns; results are valid once the caller synchronizes
  * that stream.
@@ -68,7 +69,8 @@ typedef enum {
   LA_ERR_ALIASING = 5,    /* o overlaps an input, or S_out overlaps an activation      */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_prefill_workspace_bytes */
   LA_ERR_HIP = 7,         /* a kernel launch failed                                    */
-  LA_ERR_CAPTURING = 8    /* la_prefill_varlen on a stream that is capturing a graph   */
+  LA_ERR_CAPTURING = 8,   /* la_prefill_varlen on a stream that is capturing a graph   */
+  LA_ERR_SCRATCH = 9      /* la_prefill_noalloc: B * H above its static scratch (1024) */
 } la_status;
 
 typedef uint16_t la_bf16; /* raw bfloat16 bits */
@@ -125,6 +127,30 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
                               float rope_base, float rms_eps, const float* q_norm_w,
                               const float* k_norm_w, void* workspace, size_t workspace_bytes,
                               void* stream, void* const* events, int n_events);
+
+/*
+ * la_prefill without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid allocation.  Same arguments, results and
+ * errors as la_prefill otherwise.
+ * The segment states live in a static device array of the library ("scratch",
+ * 64 MiB = 1024 fp32 128 x 128 states; each GPU the library runs on holds its own
+ * copy from the first call on it until the process ends).  The call allocates
+ * nothing: the first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it.  When la_prefill's plan would need more
+ * than 1024 segment states, the call cuts each (b, h) into fewer, longer
+ * segments (same closed form; the fp32 state sums are grouped differently, so
+ * results may differ from la_prefill's by rounding); B * H above 1024 returns
+ * LA_ERR_SCRATCH before anything is enqueued.
+ * Every call on a GPU shares that GPU's scratch: calls that overlap in time on
+ * one GPU (on different streams, or from several threads without ordering)
+ * race and must not be issued; calls ordered on one stream are safe.  The
+ * scratch needs no clearing: each call writes every state it reads.
+ */
+la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                             const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
+                             int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
+                             float rms_eps, const float* q_norm_w, const float* k_norm_w, void* stream);
 
 /*
  * Variable-length batch ("varlen"): nseq sequences packed along the token axis,

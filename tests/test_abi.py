@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
+         "la_prefill_noalloc",
          "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_linear", "la_layer_workspace_bytes",
          "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_decode_step",
          "la_sparse_prefill_workspace_bytes", "la_sparse_prefill", "la_sparse_block_means", "la_sparse_decode"])
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     for s, name in ((0, b"LA_OK"), (1, b"LA_ERR_NULL_PTR"), (2, b"LA_ERR_BAD_SHAPE"), (3, b"LA_ERR_UNSUPPORTED"),
                     (4, b"LA_ERR_ALIGNMENT"), (5, b"LA_ERR_ALIASING"), (6, b"LA_ERR_WORKSPACE"), (7, b"LA_ERR_HIP"),
-                    (8, b"LA_ERR_CAPTURING")):
+                    (8, b"LA_ERR_CAPTURING"), (9, b"LA_ERR_SCRATCH")):
         assert lib.la_status_string(s).startswith(name)
     assert lib.la_status_string(99) == b"unknown la_status"
 

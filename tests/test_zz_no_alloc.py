@@ -1,0 +1,84 @@
+"""la_prefill_noalloc (the workspace-free prefill, for callers that cannot
+allocate) through the C ABI, against la_prefill: two calls in a row, the second
+smaller, each bit-identical to la_prefill on the same inputs (both use the same
+segment plan); a shape whose plan needs more states than the static scratch
+holds, cut into longer segments and checked against la_prefill and the oracle;
+and the B * H limit refused before anything runs."""
+import ctypes
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_o_close, assert_S_close, o_row_errors, to_np, to_np32
+
+pytestmark = pytest.mark.gpu
+D = 128
+
+
+@pytest.fixture(scope="module")
+def la():
+    import hybrid_sparse_linear_la_amd as la
+    la.library()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return la
+
+
+def _noalloc(la, q, k, v, g, S_in, o, S_out, pos0, chunk):
+    """Direct C-ABI call with caller-owned outputs."""
+    B, T, H, _ = q.shape
+    p = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    return la.library().la_prefill_noalloc(p(q), p(k), p(v), p(g), p(S_in), p(S_out), p(o), B, T, H, D,
+                                           pos0, chunk, 10000.0, 1e-6, None, None,
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+
+
+@pytest.mark.parametrize("chunk", (0, 128))
+def test_noalloc_equals_prefill_two_calls(la, chunk):
+    print(f"no-alloc prefill, chunk {chunk}: a large call then a smaller one", flush=True)
+    gen = workloads.generator(501, "cuda")
+    for (B, T, H, pos0) in ((2, 9000, 16, 3), (1, 300, 4, 262144)):
+        q, k, v, g = workloads.activations(B, T, H, D, 0, "cuda", gen=gen)
+        S_in = workloads.state(B, H, D, 0.1, gen, "cuda")
+        o_ref, S_ref = la.prefill(q, k, v, g, S_in=S_in, pos0=pos0, chunk=chunk)
+        o = torch.full_like(q, float("nan"))
+        S = torch.full_like(S_in, float("nan"))
+        assert _noalloc(la, q, k, v, g, S_in, o, S, pos0, chunk) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(S, S_ref), (B, T, H)
+        print(f"  B={B} T={T} H={H}: bit-identical to la_prefill", flush=True)
+
+
+def test_noalloc_capped_plan(la):
+    """640 heads x 12800 tokens: la_prefill would use 1280 segment states, more
+    than the scratch's 1024, so the call uses one segment per head."""
+    print("no-alloc prefill with a capped plan (B*H = 640)", flush=True)
+    B, T, H = 1, 12800, 640
+    assert la.prefill_workspace_bytes(B, T, H) > 1024 * D * D * 4
+    gen = workloads.generator(502, "cuda")
+    q, k, v, g = workloads.activations(B, T, H, D, 0, "cuda", gen=gen)
+    o_ref, S_ref = la.prefill(q, k, v, g, pos0=11)
+    o = torch.empty_like(q)
+    S = torch.empty_like(S_ref)
+    assert _noalloc(la, q, k, v, g, None, o, S, 11, 0) == 0
+    torch.cuda.synchronize()
+    e = o_row_errors(to_np(o[:, -2048:]), to_np(o_ref[:, -2048:]))
+    assert e["max"] <= 2e-2 and e["median"] <= 2e-3, e
+    rel = float(torch.linalg.norm(S - S_ref) / torch.linalg.norm(S_ref))
+    assert rel <= 1e-5, rel
+    for h in (0, 639):
+        sl = lambda t: to_np32(t[:, :, h:h + 1])  # noqa: E731
+        o_or, S_or = oracle.forward(sl(q), sl(k), sl(v), sl(g), pos0=11)
+        assert_o_close(to_np(o[:, :, h:h + 1]), o_or, what=f"head {h}")
+        assert_S_close(to_np(S[:, h:h + 1]), S_or, what=f"head {h}")
+
+
+def test_noalloc_refuses_too_many_heads(la):
+    q = torch.zeros((1, 1, 1025, D), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    S = torch.empty((1, 1025, D, D), device="cuda")
+    assert _noalloc(la, q, q, q, q, None, o, S, 0, 0) == 9
+    with pytest.raises(la.LAError) as ei:
+        la.prefill_noalloc(q, q, q, q, out=o, S_out=S)
+    assert ei.value.status == 9
