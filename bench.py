@@ -11,7 +11,7 @@ before any timed region; nothing is skipped inside it.
 
 Prints one JSON line (rank 0, N = 1):
   value     prefill tokens/s (B * T * K / wall time of the K steps)
-  roofline  the dominant kernel (the chunk-output kernel) against HBM bandwidth,
+  roofline  the dominant kernel (the single-pass prefill kernel) against HBM bandwidth,
             from HIP events recorded on the library's stream around each kernel
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample
   prefill_detail.chunk_sweep  the same prefill at chunk 64, 128 and 256
@@ -108,7 +108,7 @@ def bench_prefill(la, torch, workloads, hip, args):
     o = torch.empty_like(q)
     S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     ws = torch.empty(la.prefill_workspace_bytes(B, T, H, D, args.chunk), dtype=torch.uint8, device="cuda")
-    plan_nseg = ws.numel() // (B * H * STATE_BYTES)
+    plan_nseg = ws.numel() // (B * H * STATE_BYTES)  # three-kernel form only (chunk 128, 256)
     chunk = args.chunk or la.DEFAULT_CHUNK
 
     for _ in range(args.warmup):
@@ -120,8 +120,11 @@ def bench_prefill(la, torch, workloads, hip, args):
         la.prefill(q, k, v, g, chunk=args.chunk, out=o, S_out=S_out, workspace=ws, events=evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ("chunk_state", "state_scan", "chunk_output")
+    single = chunk == la.DEFAULT_CHUNK
+    # event intervals: chunk 64 = (flag clear, -, single pass); else (state sums, scan, output)
+    names = ("sync_clear", "none", "single_pass") if single else ("chunk_state", "state_scan", "chunk_output")
     per = {n: sum(hip.ms(e[i], e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    per.pop("none", None)
     gpu_ms = sum(hip.ms(e[0], e[3]) for e in evs) / args.steps
     for e in evs:
         hip.destroy(e)
@@ -129,29 +132,39 @@ def bench_prefill(la, torch, workloads, hip, args):
     tokens = B * T
     step_s = wall / args.steps
     comp_bytes = TOKEN_HEAD_BYTES * B * T * H
-    out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
-    state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
-    scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
     flops = (4 * D * D + 2 * D * (chunk + 1)) * B * T * H
-    out_s = per["chunk_output"] / 1e3
-    traffic = measured_traffic(tokens) if chunk == la.DEFAULT_CHUNK else None
+    if single:
+        # the single-pass kernel: compulsory activation bytes plus S_in and S_out
+        main = "single_pass"
+        kernel = "la_fused_prefill_kernel"
+        out_bytes = comp_bytes + 2 * STATE_BYTES * B * H
+        gbps = {"single_pass": round(out_bytes / (per[main] / 1e3) / 1e9, 1)}
+    else:
+        main = "chunk_output"
+        kernel = "la_chunk_output_wide_kernel"
+        out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
+        state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
+        scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
+        gbps = {"chunk_state": round(state_bytes / (per["chunk_state"] / 1e3) / 1e9, 1),
+                "state_scan": round(scan_bytes / (per["state_scan"] / 1e3) / 1e9, 1),
+                "chunk_output": round(out_bytes / (per[main] / 1e3) / 1e9, 1)}
+    out_s = per[main] / 1e3
+    traffic = measured_traffic(tokens) if single else None
     roofline = {
         "bound": "hbm",
-        "kernel": "la_chunk_output_kernel" if chunk == la.DEFAULT_CHUNK else "la_chunk_output_wide_kernel",
+        "kernel": kernel,
         "achieved": round(out_bytes / out_s / 1e9, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(out_bytes / out_s / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "algorithmic_bytes_per_launch": out_bytes,
-        "avg_launch_ms": round(per["chunk_output"], 4),
+        "avg_launch_ms": round(per[main], 4),
     }
     t_roof = comp_bytes / (HBM_PEAK_GBS * 1e9)
     detail = {
         "kernels_ms": {n: round(x, 4) for n, x in per.items()},
-        "kernels_GBps": {"chunk_state": round(state_bytes / (per["chunk_state"] / 1e3) / 1e9, 1),
-                         "state_scan": round(scan_bytes / (per["state_scan"] / 1e3) / 1e9, 1),
-                         "chunk_output": roofline["achieved"]},
+        "kernels_GBps": gbps,
         "gpu_ms_per_step_events": round(gpu_ms, 4),
         "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / step_s, 4),
                           "compulsory_bytes": comp_bytes,
@@ -160,7 +173,7 @@ def bench_prefill(la, torch, workloads, hip, args):
                  "achieved_tflops": round(flops / step_s / 1e12, 2),
                  "frac_of_bf16_peak": round(flops / step_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                  "ceiling_frac_at_hbm_roof": round(flops / t_roof / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
-        "segments_per_head": plan_nseg,
+        "workspace_bytes": ws.numel(),
         "chunk": chunk,
     }
     if not args.no_chunk_sweep:
@@ -188,7 +201,7 @@ def chunk_sweep(la, torch, hip, tensors, o, S_out, steps=3):
         del ws
         res[str(c)] = {"gpu_ms": round(ms, 4), "output_kernel_ms": round(out_ms, 4),
                        "tokens_per_s": round(B * T / (ms / 1e3), 1),
-                       "kernel": "la_chunk_output_kernel" if c == 64 else "la_chunk_output_wide_kernel"}
+                       "kernel": "la_fused_prefill_kernel" if c == 64 else "la_chunk_output_wide_kernel"}
     return res
 
 

@@ -3,6 +3,7 @@
 // error status leaves the outputs untouched.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -69,7 +70,32 @@ static int64_t segment_chunks(int64_t work, int64_t sub) {
   return std::max<int64_t>(sub, (cps + sub - 1) / sub * sub);
 }
 
-bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
+// Single-pass segments: 64-token chunks per segment once the call fills more
+// than one round of workgroups.  A segment's k and v are read twice, the second
+// time one segment's state pass later, so a segment is kept short enough that
+// its second read finds them in the memory-side cache.
+static int64_t fused_segment_chunks() {
+  static const int64_t v = [] {
+    const char* e = getenv("LA_FUSED_CHUNKS");  // tuning override
+    const long x = e ? strtol(e, nullptr, 10) : 0;
+    return x >= 1 && x <= 4096 ? (int64_t)x : (int64_t)16;
+  }();
+  return v;
+}
+
+size_t fused_sync_bytes(int64_t slots) {
+  return (size_t)(kSyncHeader + slots * kHandoffWaves) * sizeof(uint32_t);
+}
+
+// Workspace of the single-pass kernel: with more than one segment per (b, h),
+// two fp32 D x D hand-off slots per (b, h) and their flags; else the sync header.
+static void fused_workspace(PrefillPlan* plan, int64_t bh) {
+  const int64_t slots = plan->nseg > 1 ? 2 * bh : 0;
+  plan->state_bytes = (size_t)slots * kHeadDim * kHeadDim * sizeof(float);
+  plan->ws_bytes = plan->state_bytes + fused_sync_bytes(slots);
+}
+
+bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool single_pass) {
   if (B < 1 || T < 1 || H < 1) return false;
   const int C = chunk == 0 ? kDefaultChunk : chunk;
   if (C != 64 && C != 128 && C != 256) return false;
@@ -77,7 +103,15 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   const int64_t sub = C / 64;
   const int64_t bh = (int64_t)B * H;
   const int64_t nchunks = ((int64_t)T + 63) / 64;
-  int64_t cps = segment_chunks(bh * nchunks, sub);
+  const bool fused = single_pass && C == 64;
+  int64_t cps;
+  if (fused) {
+    const int64_t work = bh * nchunks;
+    cps = work <= kComputeUnits * fused_segment_chunks() ? (work + kComputeUnits - 1) / kComputeUnits
+                                                         : fused_segment_chunks();
+  } else {
+    cps = segment_chunks(bh * nchunks, sub);
+  }
   if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
   if (bh * nseg > kMaxWorkgroups || bh > kMaxHeads) return false;
@@ -86,25 +120,41 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan) {
   plan->cps = (int)cps;
   plan->nseg = (int)nseg;
   plan->nwork = (int64_t)B * nseg;
-  plan->ws_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
+  plan->fused = fused;
+  if (fused) {
+    fused_workspace(plan, bh);
+  } else {
+    plan->state_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
+    plan->ws_bytes = plan->state_bytes;
+  }
   return true;
 }
 
-// A plan whose workspace holds at most max_states segment states: the planner's
-// segments, or fewer and longer ones when those would not fit.  False when even
-// one segment per (b, h) does not fit.
-bool cap_plan(int B, int H, int64_t max_states, PrefillPlan* plan) {
+// A plan whose workspace fits max_bytes: the planner's, or, when that does not
+// fit, the single-pass kernel with one segment per (b, h) (no hand-off slots),
+// or the three-kernel form with fewer, longer segments.  False when even one
+// segment state per (b, h) does not fit (three-kernel form only).
+bool cap_plan(int B, int H, size_t max_bytes, PrefillPlan* plan) {
+  if (plan->ws_bytes <= max_bytes) return true;
   const int64_t bh = (int64_t)B * H;
-  if (bh > max_states) return false;
-  if (bh * plan->nseg <= max_states) return true;
   const int64_t sub = plan->C / 64;
-  const int64_t max_seg = max_states / bh;
+  if (plan->fused) {
+    plan->cps = (int)((plan->nchunks + sub - 1) / sub * sub);
+    plan->nseg = 1;
+    plan->nwork = B;
+    fused_workspace(plan, bh);
+    return plan->ws_bytes <= max_bytes;
+  }
+  const int64_t state = (int64_t)kHeadDim * kHeadDim * sizeof(float);
+  const int64_t max_seg = (int64_t)(max_bytes / state) / bh;
+  if (max_seg < 1) return false;
   int64_t cps = (plan->nchunks + max_seg - 1) / max_seg;
   cps = (cps + sub - 1) / sub * sub;
   plan->cps = (int)cps;
   plan->nseg = (int)((plan->nchunks + cps - 1) / cps);
   plan->nwork = (int64_t)B * plan->nseg;
-  plan->ws_bytes = (size_t)(bh * plan->nseg) * kHeadDim * kHeadDim * sizeof(float);
+  plan->state_bytes = (size_t)(bh * plan->nseg) * state;
+  plan->ws_bytes = plan->state_bytes;
   return true;
 }
 
@@ -187,14 +237,14 @@ const char* la_status_string(la_status s) {
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
     case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
     case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
-    case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: B * H exceeds the 1024 states of la_prefill_noalloc's static scratch";
+    case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: la_prefill_noalloc needs more than its 64 MiB static scratch (chunk 128 or 256 with B * H > 1024)";
   }
   return "unknown la_status";
 }
 
 size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk) {
   PrefillPlan plan;
-  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan)) return 0;
+  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan, true)) return 0;
   return plan.ws_bytes;
 }
 
@@ -212,7 +262,7 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
   PrefillPlan plan;
   if (given_plan != nullptr)
     plan = *given_plan;
-  else if (!plan_prefill(B, T, H, chunk, &plan))
+  else if (!plan_prefill(B, T, H, chunk, &plan, true))
     return LA_ERR_BAD_SHAPE;
   const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
   for (const void* ptr : ptrs)
@@ -231,13 +281,14 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
     if (overlaps(workspace, plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
   if (workspace_bytes < plan.ws_bytes) return LA_ERR_WORKSPACE;
 
-  PrefillParams p;
+  PrefillParams p{};
   p.q = q;
   p.k = k;
   p.v = v;
   p.g = gate_logits;
   p.o = o;
   p.ws = static_cast<float*>(workspace);
+  p.sync = plan.fused ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + plan.state_bytes) : nullptr;
   p.segs = nullptr;
   p.seqs = nullptr;
   p.S_in = S_in;
@@ -291,7 +342,9 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
 namespace la {
 namespace {
 constexpr int64_t kScratchStates = 1024;
-constexpr size_t kScratchBytes = (size_t)kScratchStates * kHeadDim * kHeadDim * sizeof(float);  // 64 MiB
+// 1024 fp32 D x D states (64 MiB) and the single-pass sync area for as many slots
+constexpr size_t kScratchBytes =
+    (size_t)kScratchStates * kHeadDim * kHeadDim * sizeof(float) + (kSyncHeader + kScratchStates * kHandoffWaves) * 4;
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
@@ -342,8 +395,8 @@ la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* 
   if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
   if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
   PrefillPlan plan;
-  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
-  if (!cap_plan(B, H, kScratchStates, &plan)) return LA_ERR_SCRATCH;
+  if (!plan_prefill(B, T, H, chunk, &plan, true)) return LA_ERR_BAD_SHAPE;
+  if (!cap_plan(B, H, kScratchBytes, &plan)) return LA_ERR_SCRATCH;
   void* ws = nullptr;
   const la_status got = scratch_address(static_cast<hipStream_t>(stream), &ws);
   if (got != LA_OK) return got;
@@ -444,7 +497,7 @@ la_status la_prefill_varlen(const la_bf16* q, const la_bf16* k, const la_bf16* v
   RopeFreqs freqs;
   rope_freqs(rope_base, &freqs);
   if (vp.plan.scan || vp.plan.nwork > 0) {
-    PrefillParams p;
+    PrefillParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -515,7 +568,7 @@ la_status la_linear(const la_bf16* x, const la_bf16* w, la_bf16* y, int64_t M, i
 
 size_t la_layer_workspace_bytes(int B, int T, int H, int D, int chunk) {
   PrefillPlan plan;
-  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan)) return 0;
+  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan, true)) return 0;
   const size_t act = (size_t)B * T * H * D * sizeof(la_bf16);
   return 5 * round_up(act, 256) + plan.ws_bytes;
 }
@@ -530,7 +583,7 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
   if (hidden % 256 != 0 || (H * D) % 256 != 0) return LA_ERR_UNSUPPORTED;
   if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
   PrefillPlan plan;
-  if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
+  if (!plan_prefill(B, T, H, chunk, &plan, true)) return LA_ERR_BAD_SHAPE;
   const void* ptrs[] = {x, w_qkvg, w_o, S_in, S_out, y, workspace, q_norm_w, k_norm_w};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;

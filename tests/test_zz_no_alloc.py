@@ -51,8 +51,9 @@ def test_noalloc_equals_prefill_two_calls(la, chunk):
 
 
 def test_noalloc_capped_plan(la):
-    """640 heads x 12800 tokens: la_prefill would use 1280 segment states, more
-    than the scratch's 1024, so the call uses one segment per head."""
+    """640 heads x 12800 tokens: la_prefill's plan needs two 64 KiB hand-off
+    states per head (80 MiB), more than the 64 MiB scratch, so the call runs one
+    segment per head instead."""
     print("no-alloc prefill with a capped plan (B*H = 640)", flush=True)
     B, T, H = 1, 12800, 640
     assert la.prefill_workspace_bytes(B, T, H) > 1024 * D * D * 4
@@ -74,11 +75,19 @@ def test_noalloc_capped_plan(la):
         assert_S_close(to_np(S[:, h:h + 1]), S_or, what=f"head {h}")
 
 
-def test_noalloc_refuses_too_many_heads(la):
-    q = torch.zeros((1, 1, 1025, D), dtype=torch.bfloat16, device="cuda")
+def test_noalloc_many_heads_and_limit(la):
+    """Chunk 64 serves any B * H (one segment per head when the hand-off states
+    would not fit); chunks 128 and 256 keep one state per (b, h, segment), so
+    B * H above 1024 is refused before anything runs."""
+    gen = workloads.generator(503, "cuda")
+    q, k, v, g = workloads.activations(1, 70, 1100, D, 0, "cuda", gen=gen)
+    o_ref, S_ref = la.prefill(q, k, v, g)
     o = torch.empty_like(q)
-    S = torch.empty((1, 1025, D, D), device="cuda")
-    assert _noalloc(la, q, q, q, q, None, o, S, 0, 0) == 9
+    S = torch.empty_like(S_ref)
+    assert _noalloc(la, q, k, v, g, None, o, S, 0, 0) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+    assert _noalloc(la, q, k, v, g, None, o, S, 0, 128) == 9
     with pytest.raises(la.LAError) as ei:
-        la.prefill_noalloc(q, q, q, q, out=o, S_out=S)
+        la.prefill_noalloc(q, k, v, g, chunk=256, out=o, S_out=S)
     assert ei.value.status == 9
