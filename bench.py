@@ -11,7 +11,7 @@ before any timed region; nothing is skipped inside it.
 
 Prints one JSON line (rank 0, N = 1):
   value     prefill tokens/s (B * T * K / wall time of the K steps)
-  roofline  the dominant kernel (the single-pass prefill kernel) against HBM bandwidth,
+  roofline  the dominant kernel (the chunk-output kernel) against HBM bandwidth,
             from HIP events recorded on the library's stream around each kernel
   cpu_baseline  the fp64 oracle timed on this host on a bounded sample
   prefill_detail.chunk_sweep  the same prefill at chunk 64, 128 and 256
@@ -25,9 +25,12 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -108,7 +111,7 @@ def bench_prefill(la, torch, workloads, hip, args):
     o = torch.empty_like(q)
     S_out = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
     ws = torch.empty(la.prefill_workspace_bytes(B, T, H, D, args.chunk), dtype=torch.uint8, device="cuda")
-    plan_nseg = ws.numel() // (B * H * STATE_BYTES)  # three-kernel form only (chunk 128, 256)
+    plan_nseg = ws.numel() // (B * H * STATE_BYTES)
     chunk = args.chunk or la.DEFAULT_CHUNK
 
     for _ in range(args.warmup):
@@ -120,52 +123,41 @@ def bench_prefill(la, torch, workloads, hip, args):
         la.prefill(q, k, v, g, chunk=args.chunk, out=o, S_out=S_out, workspace=ws, events=evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    single = chunk == la.DEFAULT_CHUNK
-    # event intervals: chunk 64 = (flag clear, -, single pass); else (state sums, scan, output)
-    names = ("sync_clear", "none", "single_pass") if single else ("chunk_state", "state_scan", "chunk_output")
+    names = ("chunk_state", "state_scan", "chunk_output")
     per = {n: sum(hip.ms(e[i], e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
-    per.pop("none", None)
-    gpu_ms = sum(hip.ms(e[0], e[3]) for e in evs) / args.steps
+    step_ms = [hip.ms(e[0], e[3]) for e in evs]
+    gpu_ms = sum(step_ms) / args.steps
     for e in evs:
         hip.destroy(e)
 
     tokens = B * T
     step_s = wall / args.steps
     comp_bytes = TOKEN_HEAD_BYTES * B * T * H
+    out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
+    state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
+    scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
     flops = (4 * D * D + 2 * D * (chunk + 1)) * B * T * H
-    if single:
-        # the single-pass kernel: compulsory activation bytes plus S_in and S_out
-        main = "single_pass"
-        kernel = "la_fused_prefill_kernel"
-        out_bytes = comp_bytes + 2 * STATE_BYTES * B * H
-        gbps = {"single_pass": round(out_bytes / (per[main] / 1e3) / 1e9, 1)}
-    else:
-        main = "chunk_output"
-        kernel = "la_chunk_output_wide_kernel"
-        out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
-        state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
-        scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
-        gbps = {"chunk_state": round(state_bytes / (per["chunk_state"] / 1e3) / 1e9, 1),
-                "state_scan": round(scan_bytes / (per["state_scan"] / 1e3) / 1e9, 1),
-                "chunk_output": round(out_bytes / (per[main] / 1e3) / 1e9, 1)}
-    out_s = per[main] / 1e3
-    traffic = measured_traffic(tokens) if single else None
+    out_s = per["chunk_output"] / 1e3
+    traffic = measured_traffic(tokens) if chunk == la.DEFAULT_CHUNK else None
     roofline = {
         "bound": "hbm",
-        "kernel": kernel,
+        "kernel": "la_chunk_output_kernel" if chunk == la.DEFAULT_CHUNK else "la_chunk_output_wide_kernel",
         "achieved": round(out_bytes / out_s / 1e9, 1),
         "peak": HBM_PEAK_GBS,
         "unit": "GB/s",
         "frac": round(out_bytes / out_s / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": traffic,
         "algorithmic_bytes_per_launch": out_bytes,
-        "avg_launch_ms": round(per[main], 4),
+        "avg_launch_ms": round(per["chunk_output"], 4),
     }
     t_roof = comp_bytes / (HBM_PEAK_GBS * 1e9)
     detail = {
         "kernels_ms": {n: round(x, 4) for n, x in per.items()},
-        "kernels_GBps": gbps,
+        "kernels_GBps": {"chunk_state": round(state_bytes / (per["chunk_state"] / 1e3) / 1e9, 1),
+                         "state_scan": round(scan_bytes / (per["state_scan"] / 1e3) / 1e9, 1),
+                         "chunk_output": roofline["achieved"]},
         "gpu_ms_per_step_events": round(gpu_ms, 4),
+        "gpu_ms_per_step_median": round(statistics.median(step_ms), 4),
         "path_roofline": {"t_roof_ms": round(t_roof * 1e3, 4), "frac": round(t_roof / step_s, 4),
                           "compulsory_bytes": comp_bytes,
                           "achieved_GBps": round(comp_bytes / step_s / 1e9, 1)},
@@ -173,7 +165,7 @@ def bench_prefill(la, torch, workloads, hip, args):
                  "achieved_tflops": round(flops / step_s / 1e12, 2),
                  "frac_of_bf16_peak": round(flops / step_s / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
                  "ceiling_frac_at_hbm_roof": round(flops / t_roof / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)},
-        "workspace_bytes": ws.numel(),
+        "segments_per_head": plan_nseg,
         "chunk": chunk,
     }
     if not args.no_chunk_sweep:
@@ -201,7 +193,7 @@ def chunk_sweep(la, torch, hip, tensors, o, S_out, steps=3):
         del ws
         res[str(c)] = {"gpu_ms": round(ms, 4), "output_kernel_ms": round(out_ms, 4),
                        "tokens_per_s": round(B * T / (ms / 1e3), 1),
-                       "kernel": "la_fused_prefill_kernel" if c == 64 else "la_chunk_output_wide_kernel"}
+                       "kernel": "la_chunk_output_kernel" if c == 64 else "la_chunk_output_wide_kernel"}
     return res
 
 
@@ -512,6 +504,167 @@ def bench_stream(la, torch, workloads, hip, steps=3):
     return out
 
 
+def timed_calls(torch, hip, fn, n, warm=2):
+    """GPU ms of each of n calls of fn (HIP events on the current stream around
+    each call), after `warm` untimed calls."""
+    for _ in range(warm):
+        fn()
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = [hip.create(2) for _ in range(n)]
+    torch.cuda.synchronize()
+    for e in evs:
+        hip.record(e[0], stream)
+        fn()
+        hip.record(e[1], stream)
+    times = [hip.ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        hip.destroy(e)
+    return times
+
+
+def bench_prefill_32k(la, torch, workloads, hip, n=50):
+    """The 32K-token prefill (one layer's 32 heads) alone: median of n calls."""
+    w = workloads.PREFILL_32K
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, w.D, w.seed, "cuda")
+    o = torch.empty_like(q)
+    S_out = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(la.prefill_workspace_bytes(w.B, w.T, w.H), dtype=torch.uint8, device="cuda")
+    ts = timed_calls(torch, hip, lambda: la.prefill(q, k, v, g, out=o, S_out=S_out, workspace=ws), n)
+    med = statistics.median(ts)
+    comp = TOKEN_HEAD_BYTES * w.B * w.T * w.H
+    return {"workload": w.name, "calls": n, "median_ms": round(med, 4), "min_ms": round(min(ts), 4),
+            "max_ms": round(max(ts), 4), "tokens_per_s": round(w.B * w.T / (med / 1e3), 1),
+            "hbm_roof_ms": round(comp / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+            "path_frac": round(comp / (HBM_PEAK_GBS * 1e9) / (med / 1e3), 4)}
+
+
+def bench_batched_prefill(la, torch, workloads, hip, n=10):
+    """8 prompts of 32K tokens (256 sequence-heads, as many tokens as the 256K
+    prefill): one segment per (b, h), so one kernel reads k and v once."""
+    w = workloads.PREFILL_B8_32K
+    q, k, v, g = workloads.activations(w.B, w.T, w.H, w.D, w.seed, "cuda")
+    o = torch.empty_like(q)
+    S_out = torch.empty((w.B, w.H, w.D, w.D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(la.prefill_workspace_bytes(w.B, w.T, w.H), dtype=torch.uint8, device="cuda")
+    ts = timed_calls(torch, hip, lambda: la.prefill(q, k, v, g, out=o, S_out=S_out, workspace=ws), n)
+    med = statistics.median(ts)
+    comp = TOKEN_HEAD_BYTES * w.B * w.T * w.H
+    out = {"workload": w.name, "calls": n, "median_ms": round(med, 4),
+           "tokens_per_s": round(w.B * w.T / (med / 1e3), 1), "one_segment_per_head": ws.numel() == 256,
+           "hbm_roof_ms": round(comp / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
+           "path_frac": round(comp / (HBM_PEAK_GBS * 1e9) / (med / 1e3), 4),
+           "achieved_GBps": round(comp / (med / 1e3) / 1e9, 1)}
+    del q, k, v, g, o, ws
+    return out
+
+
+def _decode_steps_us(la, torch, hip, S0, q, k, v, g, pos):
+    """µs per step of consecutive decode steps (plain launches) from S0 at pos."""
+    S = S0.clone()
+    out = torch.empty_like(q)
+    steps = q.shape[0]
+    for n in range(min(3, steps)):
+        la.decode_step(q[n], k[n], v[n], g[n], S, pos + n, out=out[n])
+    S.copy_(S0)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = hip.create(2)
+    torch.cuda.synchronize()
+    hip.record(ev[0], stream)
+    for n in range(steps):
+        la.decode_step(q[n], k[n], v[n], g[n], S, pos + n, out=out[n])
+    hip.record(ev[1], stream)
+    us = hip.ms(ev[0], ev[1]) * 1e3 / steps
+    hip.destroy(ev)
+    return us
+
+
+def bench_decode_more(la, torch, workloads, hip, steps=200):
+    """Decode step time at three positions (a step's cost must not depend on it),
+    and at 256 sequences, whose 512 MiB of states exceed the 256 MB memory-side
+    cache, so every step streams its state from DRAM."""
+    w = workloads.DECODE_B64
+    S0, q, k, v, g = workloads.decode_inputs(w, steps=steps, device="cuda")
+    pos = {str(p): round(_decode_steps_us(la, torch, hip, S0, q, k, v, g, p), 3) for p in (0, 262144, 1048575)}
+    vals = list(pos.values())
+    del S0, q, k, v, g
+    w2 = workloads.DECODE_B256
+    S0, q, k, v, g = workloads.decode_inputs(w2, steps=w2.steps, device="cuda")
+    us = _decode_steps_us(la, torch, hip, S0, q, k, v, g, w2.pos0)
+    bytes_step = 2 * w2.B * w2.H * STATE_BYTES + 5 * w2.B * w2.H * w2.D * 2
+    gbs = bytes_step / (us * 1e-6) / 1e9
+    del S0, q, k, v, g
+    return {
+        "us_per_step_by_position": pos, "position_max_over_min": round(max(vals) / min(vals), 4),
+        "b256": {"workload": w2.name, "steps": w2.steps, "us_per_step": round(us, 3), "bytes_per_step": bytes_step,
+                 "state_bytes": w2.B * w2.H * STATE_BYTES,
+                 "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": round(gbs, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                              "note": "the 512 MiB of states exceed the 256 MB memory-side cache: "
+                                      "each step reads and writes them in DRAM"}},
+    }
+
+
+def _sclk_files():
+    files = []
+    for d in sorted(glob.glob("/sys/class/drm/card*/device")):
+        f = os.path.join(d, "pp_dpm_sclk")
+        try:
+            if open(os.path.join(d, "vendor")).read().strip() == "0x1002" and os.access(f, os.R_OK):
+                files.append(f)
+        except OSError:
+            pass
+    return files
+
+
+def _sclk_levels(path):
+    """(current MHz, highest MHz) from a pp_dpm_sclk listing (current marked '*')."""
+    cur, top = None, None
+    for line in open(path):
+        m = re.search(r"(\d+)\s*mhz", line, re.I)
+        if not m:
+            continue
+        mhz = int(m.group(1))
+        top = mhz if top is None else max(top, mhz)
+        if "*" in line:
+            cur = mhz
+    return cur, top
+
+
+def environment(torch, workloads, busy_fn):
+    """Host and GPU facts for the record, with the GPU clock sampled while busy_fn's
+    work (enqueued, not yet finished) keeps the GPU busy."""
+    cpu = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    files = _sclk_files()
+    busy_fn()
+    samples, top = [], None
+    for _ in range(10):
+        for f in files:
+            try:
+                cur, t = _sclk_levels(f)
+            except OSError:
+                continue
+            if cur is not None:
+                samples.append(cur)
+            top = t if top is None else max(top, t or 0)
+        time.sleep(0.005)
+    torch.cuda.synchronize()
+    seeds = {w.name: w.seed for w in (*workloads.ALL, workloads.PREFILL_B8_32K, workloads.DECODE_B256,
+                                      workloads.SERVING_MIX, workloads.LAYER_32K, workloads.SPARSE_32K,
+                                      workloads.SPARSE_DECODE)}
+    return {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip,
+            "cpu_model": cpu, "nproc": os.cpu_count(),
+            "cpus_usable": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "sclk_mhz_while_busy": samples or None, "sclk_mhz_max_level": top,
+            "sclk_source": files[0] if files else None, "seeds": seeds}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -531,6 +684,8 @@ def main():
                     help="skip the 1M-token prefill (16 carried calls of 65536, and one call)")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip timing the prefill at the other chunk sizes")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the 32K prefill alone, the batched prefill and the extra decode timings")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="first run one plain device-to-device copy of this many MiB (a kernel of "
                          "known traffic, used to scale rocprofv3 FETCH_SIZE/WRITE_SIZE counters)")
@@ -558,12 +713,32 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     w, tps, step_s, roofline, detail, tensors = bench_prefill(la, torch, workloads, hip, args)
+    q256, k256, v256, g256 = tensors
+    o256 = torch.empty_like(q256)
+    ws256 = torch.empty(la.prefill_workspace_bytes(*q256.shape[:3]), dtype=torch.uint8, device="cuda")
+    env = environment(torch, workloads, lambda: [la.prefill(q256, k256, v256, g256, out=o256, workspace=ws256)
+                                                 for _ in range(30)])
+    del o256, ws256
+    prefill_32k = None if args.no_extra else bench_prefill_32k(la, torch, workloads, hip)
+    batched = None if args.no_extra else bench_batched_prefill(la, torch, workloads, hip)
     decode = None if args.no_decode else bench_decode(la, torch, workloads, hip, args)
+    if decode is not None and not args.no_extra:
+        decode.update(bench_decode_more(la, torch, workloads, hip))
     varlen = None if args.no_varlen else bench_varlen(la, torch, workloads, hip, args)
     layer = None if args.no_layer else bench_layer(la, torch, workloads, hip, args)
     backward = None if args.no_backward else bench_backward(la, torch, workloads, hip, tensors)
     sparse = None if args.no_sparse else bench_sparse(la, torch, workloads, hip)
     stream_1m = None if args.no_stream else bench_stream(la, torch, workloads, hip)
+    invariants = {"description": "linear-time prefill and constant-cost decode: time ratios of the GPU "
+                                 "medians (ideal 8 and 4 for the prefill, 1 for decode positions)"}
+    t256 = detail["gpu_ms_per_step_median"]
+    if prefill_32k is not None:
+        invariants["t_256k_over_t_32k"] = round(t256 / prefill_32k["median_ms"], 4)
+    if stream_1m is not None:
+        invariants["t_1m_single_over_t_256k"] = round(stream_1m["single_shot"]["ms"] / t256, 4)
+        invariants["t_1m_streamed_over_t_256k"] = round(stream_1m["streamed"]["ms"] / t256, 4)
+    if decode is not None and "position_max_over_min" in decode:
+        invariants["decode_position_max_over_min"] = decode["position_max_over_min"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(tensors, args)
     if decode is not None and not args.no_cpu_baseline:
         decode["cpu_baseline"] = cpu_decode_baseline(workloads)
@@ -585,6 +760,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill_detail": detail,
+        "prefill_32k": prefill_32k,
+        "batched_prefill": batched,
+        "invariants": invariants,
+        "environment": env,
         "decode": decode,
         "varlen": varlen,
         "layer": layer,

@@ -40,7 +40,7 @@ SPARSE_BLOCK = 64
 STATUS = {
     0: "LA_OK", 1: "LA_ERR_NULL_PTR", 2: "LA_ERR_BAD_SHAPE", 3: "LA_ERR_UNSUPPORTED",
     4: "LA_ERR_ALIGNMENT", 5: "LA_ERR_ALIASING", 6: "LA_ERR_WORKSPACE", 7: "LA_ERR_HIP",
-    8: "LA_ERR_CAPTURING", 9: "LA_ERR_SCRATCH",
+    8: "LA_ERR_CAPTURING",
 }
 
 _vp = ctypes.c_void_p
@@ -216,9 +216,9 @@ def prefill(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: 
 def prefill_noalloc(q, k, v, gate, S_in=None, pos0: int = 0, chunk: int = 0, rope_base: float = 10000.0,
                     rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None, out=None, S_out=None):
     """``prefill`` through la_prefill_noalloc: no workspace, the library's static
-    device scratch instead (B * H <= 1024).  Pass ``out`` and ``S_out`` to make the
-    call allocate nothing at all (e.g. under graph capture).  Calls that overlap in
-    time on one GPU share that scratch and race."""
+    device scratch instead.  Pass ``out`` and ``S_out`` to make the call allocate
+    nothing at all (e.g. under graph capture).  Calls that overlap in time on one
+    GPU share that scratch and race."""
     lib = library()
     for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate)):
         _act(n, t, 4)

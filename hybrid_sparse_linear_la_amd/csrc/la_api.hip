@@ -3,7 +3,6 @@
 // error status leaves the outputs untouched.
 #include <math.h>
 #include <stdint.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -70,32 +69,29 @@ static int64_t segment_chunks(int64_t work, int64_t sub) {
   return std::max<int64_t>(sub, (cps + sub - 1) / sub * sub);
 }
 
-// Single-pass segments: 64-token chunks per segment once the call fills more
-// than one round of workgroups.  A segment's k and v are read twice, the second
-// time one segment's state pass later, so a segment is kept short enough that
-// its second read finds them in the memory-side cache.
-static int64_t fused_segment_chunks() {
-  static const int64_t v = [] {
-    const char* e = getenv("LA_FUSED_CHUNKS");  // tuning override
-    const long x = e ? strtol(e, nullptr, 10) : 0;
-    return x >= 1 && x <= 4096 ? (int64_t)x : (int64_t)16;
-  }();
-  return v;
+// Whether one workgroup per (b, h), walking the whole sequence, keeps the compute
+// units busy: at least one full round, and the last round at least a quarter
+// full of the rounds' capacity (bh >= 3/4 of the rounds' slots).  Then the
+// segmented form's second read of k and v (in the state pass) buys nothing.
+static bool heads_fill_device(int64_t bh) {
+  const int64_t rounds = (bh + kComputeUnits - 1) / kComputeUnits;
+  return bh >= kComputeUnits && 4 * bh >= 3 * kComputeUnits * rounds;
 }
 
-size_t fused_sync_bytes(int64_t slots) {
-  return (size_t)(kSyncHeader + slots * kHandoffWaves) * sizeof(uint32_t);
+// Workspace of a direct plan: no segment states are kept; a minimum size keeps
+// 0 meaning "invalid shape".
+constexpr size_t kDirectWorkspaceBytes = 256;
+
+static void set_direct(PrefillPlan* plan, int B) {
+  const int64_t sub = plan->C / 64;
+  plan->cps = (int)((plan->nchunks + sub - 1) / sub * sub);
+  plan->nseg = 1;
+  plan->nwork = B;
+  plan->direct = true;
+  plan->ws_bytes = kDirectWorkspaceBytes;
 }
 
-// Workspace of the single-pass kernel: with more than one segment per (b, h),
-// two fp32 D x D hand-off slots per (b, h) and their flags; else the sync header.
-static void fused_workspace(PrefillPlan* plan, int64_t bh) {
-  const int64_t slots = plan->nseg > 1 ? 2 * bh : 0;
-  plan->state_bytes = (size_t)slots * kHeadDim * kHeadDim * sizeof(float);
-  plan->ws_bytes = plan->state_bytes + fused_sync_bytes(slots);
-}
-
-bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool single_pass) {
+bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool direct_ok) {
   if (B < 1 || T < 1 || H < 1) return false;
   const int C = chunk == 0 ? kDefaultChunk : chunk;
   if (C != 64 && C != 128 && C != 256) return false;
@@ -103,15 +99,7 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool single
   const int64_t sub = C / 64;
   const int64_t bh = (int64_t)B * H;
   const int64_t nchunks = ((int64_t)T + 63) / 64;
-  const bool fused = single_pass && C == 64;
-  int64_t cps;
-  if (fused) {
-    const int64_t work = bh * nchunks;
-    cps = work <= kComputeUnits * fused_segment_chunks() ? (work + kComputeUnits - 1) / kComputeUnits
-                                                         : fused_segment_chunks();
-  } else {
-    cps = segment_chunks(bh * nchunks, sub);
-  }
+  int64_t cps = segment_chunks(bh * nchunks, sub);
   if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
   if (bh * nseg > kMaxWorkgroups || bh > kMaxHeads) return false;
@@ -120,42 +108,32 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool single
   plan->cps = (int)cps;
   plan->nseg = (int)nseg;
   plan->nwork = (int64_t)B * nseg;
-  plan->fused = fused;
-  if (fused) {
-    fused_workspace(plan, bh);
-  } else {
-    plan->state_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
-    plan->ws_bytes = plan->state_bytes;
-  }
+  plan->direct = false;
+  plan->ws_bytes = (size_t)(bh * nseg) * kHeadDim * kHeadDim * sizeof(float);
+  if (direct_ok && (nseg == 1 || heads_fill_device(bh))) set_direct(plan, B);
   return true;
 }
 
-// A plan whose workspace fits max_bytes: the planner's, or, when that does not
-// fit, the single-pass kernel with one segment per (b, h) (no hand-off slots),
-// or the three-kernel form with fewer, longer segments.  False when even one
-// segment state per (b, h) does not fit (three-kernel form only).
-bool cap_plan(int B, int H, size_t max_bytes, PrefillPlan* plan) {
-  if (plan->ws_bytes <= max_bytes) return true;
+// A plan whose workspace fits max_bytes: the planner's, or fewer and longer
+// segments, or (when not even one segment state per (b, h) fits) the direct
+// form, which keeps no states.
+void cap_plan(int B, int H, size_t max_bytes, PrefillPlan* plan) {
+  if (plan->ws_bytes <= max_bytes) return;
   const int64_t bh = (int64_t)B * H;
   const int64_t sub = plan->C / 64;
-  if (plan->fused) {
-    plan->cps = (int)((plan->nchunks + sub - 1) / sub * sub);
-    plan->nseg = 1;
-    plan->nwork = B;
-    fused_workspace(plan, bh);
-    return plan->ws_bytes <= max_bytes;
-  }
   const int64_t state = (int64_t)kHeadDim * kHeadDim * sizeof(float);
   const int64_t max_seg = (int64_t)(max_bytes / state) / bh;
-  if (max_seg < 1) return false;
+  if (max_seg < 2) {
+    set_direct(plan, B);
+    return;
+  }
   int64_t cps = (plan->nchunks + max_seg - 1) / max_seg;
   cps = (cps + sub - 1) / sub * sub;
   plan->cps = (int)cps;
   plan->nseg = (int)((plan->nchunks + cps - 1) / cps);
   plan->nwork = (int64_t)B * plan->nseg;
-  plan->state_bytes = (size_t)(bh * plan->nseg) * state;
-  plan->ws_bytes = plan->state_bytes;
-  return true;
+  plan->ws_bytes = (size_t)(bh * plan->nseg) * state;
+  if (plan->nseg == 1) set_direct(plan, B);
 }
 
 // Host plan of a variable-length batch: the segment, sequence and single-token
@@ -237,7 +215,6 @@ const char* la_status_string(la_status s) {
     case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
     case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
     case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
-    case LA_ERR_SCRATCH: return "LA_ERR_SCRATCH: la_prefill_noalloc needs more than its 64 MiB static scratch (chunk 128 or 256 with B * H > 1024)";
   }
   return "unknown la_status";
 }
@@ -288,7 +265,6 @@ static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16*
   p.g = gate_logits;
   p.o = o;
   p.ws = static_cast<float*>(workspace);
-  p.sync = plan.fused ? reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + plan.state_bytes) : nullptr;
   p.segs = nullptr;
   p.seqs = nullptr;
   p.S_in = S_in;
@@ -342,9 +318,7 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
 namespace la {
 namespace {
 constexpr int64_t kScratchStates = 1024;
-// 1024 fp32 D x D states (64 MiB) and the single-pass sync area for as many slots
-constexpr size_t kScratchBytes =
-    (size_t)kScratchStates * kHeadDim * kHeadDim * sizeof(float) + (kSyncHeader + kScratchStates * kHandoffWaves) * 4;
+constexpr size_t kScratchBytes = (size_t)kScratchStates * kHeadDim * kHeadDim * sizeof(float);  // 64 MiB
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 std::atomic<void*> g_scratch_ptr[kMaxDevices];
@@ -396,7 +370,7 @@ la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* 
   if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
   PrefillPlan plan;
   if (!plan_prefill(B, T, H, chunk, &plan, true)) return LA_ERR_BAD_SHAPE;
-  if (!cap_plan(B, H, kScratchBytes, &plan)) return LA_ERR_SCRATCH;
+  cap_plan(B, H, kScratchBytes, &plan);
   void* ws = nullptr;
   const la_status got = scratch_address(static_cast<hipStream_t>(stream), &ws);
   if (got != LA_OK) return got;

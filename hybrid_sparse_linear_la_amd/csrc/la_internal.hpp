@@ -27,22 +27,14 @@ struct PrefillPlan {
   int nseg = 0;     // segments per (b, h) (equal-length batches)
   int64_t nwork = 0;  // segment workgroups per head: B * nseg, or the table's segments
   bool scan = true;   // launch the state scan
-  bool fused = false; // single-pass kernel (chunk 64, equal-length batches)
-  size_t state_bytes = 0;  // segment states at the front of the workspace
+  bool direct = false;  // one segment per (b, h): the output kernel alone, S_in -> S_out
   size_t ws_bytes = 0;
 };
 
-// single_pass: plan la_prefill's single-pass kernel (chunk 64 only); otherwise the
-// three-kernel form (state sums, scan, output) that the backward also uses.
-bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool single_pass = false);
-
-// Single-pass prefill (chunk 64, equal-length batches): the sync area that
-// follows the segment states in the workspace.  Word 0 is the item ticket, word 1
-// the error word (nonzero if a hand-off wait gave up), then one flag per
-// (segment item, consumer wave), from word kSyncHeader on.
-constexpr int kSyncHeader = 64;
-constexpr int kHandoffWaves = 4;
-size_t fused_sync_bytes(int64_t items);
+// direct_ok: la_prefill's plan, which may use one segment per (b, h) with no
+// state pass; otherwise the segmented form (state sums, scan, output) that the
+// backward also uses.
+bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool direct_ok = false);
 
 // Variable-length batches (packed [total_T, H, D] activations).  The host cuts
 // every sequence of two or more tokens into segments and sends the tables below
@@ -80,7 +72,6 @@ struct PrefillParams {
   const float* qw;    // [D] or nullptr
   const float* kw;    // [D] or nullptr
   const uint16_t* dout;  // backward only: gradient of o, [B][T][H][D]
-  uint32_t* sync;     // single-pass prefill: ticket, error word and per-wave hand-off flags
   int B, T, H, nseg, cps;
   int64_t pos0;
   float eps;

@@ -8,7 +8,10 @@
 //     S_pre <- S_pre + Kh^T V
 // which is the recurrence regrouped (sum the update over the chunk).
 //
-// Three launches on the caller's stream:
+// With one segment per (b, h) ("direct": the (b, h) alone fill the compute
+// units) only the output kernel runs, starting from S_in and writing S_out from
+// its carried state, so k and v are read once.  Otherwise three launches on the
+// caller's stream:
 //   1. la_chunk_state_kernel : one workgroup per (b, h, segment of cps chunks)
 //      sums Kh^T V over its segment (bf16 MFMA, fp32 accumulate) -> workspace.
 //   2. la_state_scan_kernel  : per state element, exclusive prefix over segments
@@ -39,10 +42,12 @@
 #include "la_internal.hpp"
 #include "la_tiles.hpp"
 
-#include <algorithm>
-
 namespace la {
 namespace {
+
+// One segment per (b, h) of an equal-length batch: the output kernels start from
+// S_in and write S_out themselves.
+__device__ __forceinline__ bool is_direct(const PrefillParams& p) { return p.segs == nullptr && p.nseg == 1; }
 
 // --------------------------------------------------------------------------
 // Kh^T V summed over each segment.  LDS is double-buffered, so one barrier per
@@ -332,15 +337,18 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
   const int64_t rs = (int64_t)p.H * kD;
 
   // prefix state of this segment: S[:, 32w + 16 dt .. + 16) in accumulator tiles
+  // (direct: S_in, or zero)
+  const bool direct = is_direct(p);
+  const int64_t bh = (int64_t)tl.b * p.H + tl.h;
   f32x4 Sacc[2][8];
   {
-    const float* src = tl.state;
+    const float* src = direct ? (p.S_in ? p.S_in + bh * kD * kD : nullptr) : tl.state;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int rtk = 0; rtk < 8; ++rtk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Sacc[dt][rtk][r] = src[state_elem(rtk, r, 2 * w + dt, g4, n16)];
+        for (int r = 0; r < 4; ++r) Sacc[dt][rtk][r] = src ? src[state_elem(rtk, r, 2 * w + dt, g4, n16)] : 0.0f;
   }
   // this lane's output pointer at chunk-relative row n16, column 32 w + 4 g
   uint16_t* const obase = p.o + tl.base + (int64_t)n16 * rs + 32 * w + 4 * g4;
@@ -368,6 +376,15 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
     consume_phase_b(K, V, G, sP, Sacc, Oacc, nv, obase + (int64_t)t0 * rs, rs, w, g4, n16);
     __syncthreads();
   }
+  if (direct) {
+    float* dst = p.S_out + bh * kD * kD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[state_elem(rtk, r, 2 * w + dt, g4, n16)] = Sacc[dt][rtk][r];
+  }
 }
 
 template <bool kWeights>
@@ -388,289 +405,6 @@ __global__ __launch_bounds__(kOutThreads) void la_chunk_output_kernel(PrefillPar
     consume(p, tl, sQ, sK, sV, sG, sQl, sKl, sP);
 }
 
-
-// --------------------------------------------------------------------------
-// Single-pass prefill (C = 64, equal-length batches).  One workgroup per
-// (b, h, segment) item.  With more than one segment per (b, h), items are taken
-// in ticket order, segment-major (item t: segment t / (B H), sequence-head
-// t % (B H)), so an item only ever waits for one with a lower ticket, whose
-// workgroup already runs: every wait ends.  An item that is not its sequence's
-// last first sums Kh^T V over its segment (phase 1: the producer waves stage k
-// and v only, the consumers accumulate).  Then consumer wave w takes the
-// previous segment's inclusive state for its 32 value columns (a chained scan
-// over the segments of one (b, h)), publishes its own inclusive state and walks
-// the segment again from the prefix (phase 2: the output kernel's loop).  The
-// second read of k and v follows the first by one segment's phase 1, so it is
-// mostly served from the memory-side cache.
-//
-// Hand-off: each (b, h) has two state slots; segment s publishes its inclusive
-// state in slot s % 2, which segment s + 1 reads.  Segment s + 2 overwrites the
-// slot only after it has received segment s + 1's state, which segment s + 1
-// published after its read, so two slots suffice.  A slot is in accumulator
-// order (wave w, element e = 8 dt + rtk, lane: 16 bytes at ((w 16 + e) 64 +
-// lane) 16), written and read with device-coherent buffer accesses (sc1); one
-// flag per (slot, wave) holds s + 1 once the wave's slice of segment s's state
-// has been written, set by a device-scope store after the wave's slice stores
-// have completed.  No cache-wide write-back or invalidate is needed.  A wait gives
-// up after kSpinLimit polls, sets the error word and continues from NaN, so a
-// broken hand-off cannot hang the kernel and shows in the outputs.
-constexpr uint32_t kSpinLimit = 1u << 20;
-constexpr int kSc1 = 16;  // buffer-access cache policy: device scope
-constexpr int kSliceBytes = 16 * 64 * 16;  // one wave's 32 columns of a D x D fp32 state
-typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
-
-// Buffer resource of segment state `idx` (wave-uniform, so the resource sits in
-// scalar registers).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const PrefillParams& p, int64_t idx) {
-  const int i = __builtin_amdgcn_readfirstlane((int)idx);
-  return __builtin_amdgcn_make_buffer_rsrc(p.ws + (int64_t)i * kD * kD, (short)0, kHandoffWaves * kSliceBytes,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ void load_slice(__amdgpu_buffer_rsrc_t r, int w, int lane, f32x4 (&S)[2][8]) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const u32x4v x = __builtin_amdgcn_raw_buffer_load_b128(r, ((w * 16 + e) * 64 + lane) * 16, 0, kSc1);
-    S[e >> 3][e & 7] = __builtin_bit_cast(f32x4, x);
-  }
-}
-
-__device__ __forceinline__ void store_slice(__amdgpu_buffer_rsrc_t r, int w, int lane, const f32x4 (&S)[2][8]) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, S[e >> 3][e & 7]), r,
-                                           ((w * 16 + e) * 64 + lane) * 16, 0, kSc1);
-}
-
-// Work item -> tile: segment `seg` of sequence-head bh = b H + h.
-__device__ __forceinline__ Tile item_tile(const PrefillParams& p, int bh, int seg) {
-  Tile tl;
-  bh = __builtin_amdgcn_readfirstlane(bh);
-  seg = __builtin_amdgcn_readfirstlane(seg);
-  tl.b = __builtin_amdgcn_readfirstlane(bh / p.H);
-  tl.h = bh - tl.b * p.H;
-  tl.seg = seg;
-  tl.t_begin = seg * p.cps * kC;
-  tl.t_end = min(p.T, tl.t_begin + p.cps * kC);
-  tl.base = ((int64_t)tl.b * p.T * p.H + tl.h) * kD;
-  tl.pos_base = p.pos0;
-  tl.state = nullptr;  // hand-off slots: state_rsrc
-  tl.nch = (tl.t_end - tl.t_begin + kC - 1) / kC;
-  return tl;
-}
-
-// Phase 1, producer side: k (prologue) and v of every chunk into the double buffer.
-template <bool kWeights>
-__device__ __forceinline__ void produce_state(const PrefillParams& p, const Tile& tl, uint8_t (*sK)[kTileBytes],
-                                              uint8_t (*sV)[kTileBytes], float2 (*sRot)[kHalf]) {
-  __builtin_amdgcn_s_setprio(1);
-  const int ptid = threadIdx.x - kConsumers;
-  const int j = ptid & 15, rg = ptid >> 4;
-  const int64_t rs = (int64_t)p.H * kD;
-  float wk[8];
-  load_norm_weights(p.kw, j, wk);
-  Rope L;
-  rope_init<32>(p, ptid, rg, j, L);
-  struct KV {
-    Rows<2> k, v;
-  };
-  KV X, Y;
-  auto load_chunk = [&](int c, KV& R) {
-    const int t = tl.t_begin + c * kC;
-    const int nv = min(kC, tl.t_end - t);
-    const int64_t off = tl.base + (int64_t)t * rs;
-    load_rows<2, 32>(p.k + off, rs, nv, rg, j, R.k);
-    load_rows<2, 32>(p.v + off, rs, nv, rg, j, R.v);
-  };
-  auto stage = [&](int c, const KV& R) {
-    const int b = c & 1;
-    const int nv = min(kC, tl.t_end - (tl.t_begin + c * kC));
-    norm_rope_stage<kWeights, 2, 32>(R.k, wk, p.eps, sRot[b], L, rg, j, sK[b]);
-    store_rows_masked<2, 32>(sV[b], R.v, nv, rg, j);
-  };
-  auto step = [&](int c, KV& R) {
-    if (c + 1 < tl.nch) {
-      stage(c + 1, R);
-      if (c + 3 < tl.nch) load_chunk(c + 3, R);
-      if (c + 2 < tl.nch && ptid < kHalf)
-        sRot[c & 1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + (c + 2) * kC, L.base_rev);
-    }
-    __syncthreads();
-  };
-  load_chunk(0, Y);
-  if (tl.nch > 1) load_chunk(1, X);
-  if (ptid < kHalf) {
-    sRot[0][ptid] = rope_rotation(tl.pos_base + tl.t_begin, L.base_rev);
-    if (tl.nch > 1) sRot[1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + kC, L.base_rev);
-  }
-  __syncthreads();
-  stage(0, Y);
-  if (tl.nch > 2) load_chunk(2, Y);
-  __syncthreads();
-  for (int c = 0; c < tl.nch; c += 2) {
-    step(c, X);
-    if (c + 1 < tl.nch) step(c + 1, Y);
-  }
-}
-
-// Phase 1, consumer side: this wave's columns of Kh^T V over the segment.
-__device__ __forceinline__ void consume_state(uint8_t (*sK)[kTileBytes], uint8_t (*sV)[kTileBytes], int nch,
-                                              f32x4 (&Sacc)[2][8], int w, int g4, int n16) {
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int a = 0; a < 8; ++a) Sacc[dt][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const uint8_t* K = sK[c & 1];
-    const uint8_t* V = sV[c & 1];
-    bf16x8 Vf[2][2];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Vf[dt][kk] = v_operand(V, kk, 32 * w + 16 * dt, g4, n16);
-#pragma unroll
-    for (int kk = 0; kk < kC / 32; ++kk) {
-      const int tr0 = 32 * kk + 4 * g4 + (n16 >> 2);
-#pragma unroll
-      for (int rtk = 0; rtk < 8; ++rtk) {
-        const int col = 16 * rtk + 4 * (n16 & 3);
-        const bf16x8 a = as_bf16x8(lds_tr(K, tile_off(tr0, col)), lds_tr(K, tile_off(tr0 + 16, col)));
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) Sacc[dt][rtk] = mma(a, Vf[dt][kk], Sacc[dt][rtk]);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Phase 2, consumer side: the prefix state from the previous segment (or S_in),
-// the inclusive state published for the next one, then the output loop; the last
-// segment of a sequence-head writes the final state.
-__device__ __forceinline__ void consume_fused(const PrefillParams& p, const Tile& tl, bool chained,
-                                              bool last, f32x4 (&Sacc)[2][8], uint8_t (*sQ)[kTileBytes],
-                                              uint8_t (*sK)[kTileBytes], uint8_t (*sV)[kTileBytes],
-                                              uint8_t (*sG)[kTileBytes], const uint8_t* sQl,
-                                              const uint8_t* sKl, uint8_t* sP) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
-  const int64_t rs = (int64_t)p.H * kD;
-  const int64_t bh = (int64_t)tl.b * p.H + tl.h;
-  uint16_t* const obase = p.o + tl.base + (int64_t)n16 * rs + 32 * w + 4 * g4;
-  for (int i = tid; i < kC * kScoreRowBytes / 16; i += kConsumers)
-    reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
-  __syncthreads();
-  __syncthreads();
-
-  // prefix state of this segment
-  f32x4 P[2][8];
-  if (tl.seg == 0) {
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int rtk = 0; rtk < 8; ++rtk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          P[dt][rtk][r] = p.S_in ? p.S_in[bh * kD * kD + state_elem(rtk, r, 2 * w + dt, g4, n16)] : 0.0f;
-  } else {
-    // slot (seg - 1) % 2 holds segment seg - 1's state once its flag reads seg
-    const int64_t slot = 2 * bh + ((tl.seg - 1) & 1);
-    uint32_t* flag = p.sync + kSyncHeader + slot * kHandoffWaves + w;
-    const uint32_t want = (uint32_t)tl.seg;
-    uint32_t seen = 0, polls = 0;
-    while ((seen = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < want && ++polls < kSpinLimit)
-      __builtin_amdgcn_s_sleep(2);
-    if (seen >= want) {
-      load_slice(state_rsrc(p, slot), w, lane, P);
-    } else {
-      __hip_atomic_store(p.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-        for (int a = 0; a < 8; ++a) P[dt][a] = f32x4{__builtin_nanf(""), 0.f, 0.f, 0.f};
-    }
-  }
-  if (chained && !last) {
-    // the inclusive state P + (this segment's Kh^T V), formed in place
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int a = 0; a < 8; ++a) Sacc[dt][a] = P[dt][a] + Sacc[dt][a];
-    const int64_t slot = 2 * bh + (tl.seg & 1);
-    store_slice(state_rsrc(p, slot), w, lane, Sacc);
-    __builtin_amdgcn_s_waitcnt(0);  // the slice is written before the flag
-    if (lane == 0)
-      __hip_atomic_store(p.sync + kSyncHeader + slot * kHandoffWaves + w, (uint32_t)tl.seg + 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  }
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int a = 0; a < 8; ++a) Sacc[dt][a] = P[dt][a];
-
-  for (int c = 0; c < tl.nch; ++c) {
-    const int b = c & 1;
-    const int t0 = tl.t_begin + c * kC;
-    const int nv = min(kC, tl.t_end - t0);
-    const bool exact = tl.seg == 0 && c == 0;
-    f32x4 Oacc[2][4];
-    consume_phase_a(sQ[b], sK[b], sQl, sKl, sP, Sacc, Oacc, exact, w, g4, n16);
-    __syncthreads();
-    consume_phase_b(sK[b], sV[b], sG[b], sP, Sacc, Oacc, nv, obase + (int64_t)t0 * rs, rs, w, g4, n16);
-    __syncthreads();
-  }
-  if (last) {
-    float* dst = p.S_out + bh * kD * kD;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int rtk = 0; rtk < 8; ++rtk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dst[state_elem(rtk, r, 2 * w + dt, g4, n16)] = Sacc[dt][rtk][r];
-  }
-}
-
-template <bool kWeights>
-__global__ __launch_bounds__(kOutThreads) void la_fused_prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), bf16
-  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
-  __shared__ float2 sRot[2][kHalf];
-  __shared__ int sItem;
-
-  const bool chained = p.nseg > 1;
-  int item = blockIdx.x;
-  if (chained) {
-    if (threadIdx.x == 0)
-      sItem = (int)__hip_atomic_fetch_add(p.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(sItem);
-  }
-  const int BH = p.B * p.H;
-  const int seg = item / BH;
-  const Tile tl = item_tile(p, item - seg * BH, seg);
-  const bool last = seg == p.nseg - 1;
-  if (threadIdx.x >= kConsumers) {
-    if (chained && !last) produce_state<kWeights>(p, tl, sK, sV, sRot);
-    produce<kWeights>(p, tl, sQ, sK, sV, sG, sQl, sKl, sRot);
-  } else {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    f32x4 Sacc[2][8];
-    if (chained && !last) consume_state(sK, sV, tl.nch, Sacc, w, lane >> 4, lane & 15);
-    consume_fused(p, tl, chained, last, Sacc, sQ, sK, sV, sG, sQl, sKl, sP);
-  }
-}
-
-// Clears the ticket, the error word and the hand-off flags of a single-pass call.
-__global__ __launch_bounds__(256) void la_sync_clear_kernel(uint32_t* sync, int64_t words) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
-    sync[i] = 0u;
-}
 
 // --------------------------------------------------------------------------
 // Wide-chunk output kernel, C = 64 kSub (kSub = 2 or 4).  The chunked form with
@@ -712,14 +446,16 @@ __global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(P
     for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t, rev[e]), L.A[e]);
   };
 
-  // prefix state of this segment: S[:, 16 w .. 16 w + 16)
+  // prefix state of this segment: S[:, 16 w .. 16 w + 16) (direct: S_in, or zero)
+  const bool direct = is_direct(p);
+  const int64_t bh = (int64_t)tl.b * p.H + tl.h;
   f32x4 Sacc[8];
   {
-    const float* src = tl.state;
+    const float* src = direct ? (p.S_in ? p.S_in + bh * kD * kD : nullptr) : tl.state;
 #pragma unroll
     for (int rtk = 0; rtk < 8; ++rtk)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[rtk][r] = src[state_elem(rtk, r, w, g4, n16)];
+      for (int r = 0; r < 4; ++r) Sacc[rtk][r] = src ? src[state_elem(rtk, r, w, g4, n16)] : 0.0f;
   }
   // this lane's output (and gate) columns 16 w + 4 g .. + 3 of (b, h)
   const int64_t col_off = tl.base + 16 * w + 4 * g4;
@@ -830,6 +566,13 @@ __global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(P
 #pragma unroll
     for (int a = 0; a < 8; ++a) Sacc[a] += Dacc[a];
   }
+  if (direct) {
+    float* dst = p.S_out + bh * kD * kD;
+#pragma unroll
+    for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[state_elem(rtk, r, w, g4, n16)] = Sacc[rtk][r];
+  }
 }
 
 }  // namespace
@@ -843,34 +586,15 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
   auto mark = [&](int i) {
     if (events && err == hipSuccess) err = hipEventRecord(events[i], stream);
   };
-  if (plan.fused) {
-    // single pass: clear the sync area (only needed with more than one segment),
-    // then one kernel; events 1 and 2 both mark the start of that kernel
-    mark(0);
-    if (plan.nseg > 1) {
-      const int64_t words = kSyncHeader + (int64_t)p.B * p.H * 2 * kHandoffWaves;
-      hipLaunchKernelGGL(la_sync_clear_kernel, dim3((unsigned)std::min<int64_t>((words + 255) / 256, 1024)),
-                         dim3(256), 0, stream, p.sync, words);
-    }
-    mark(1);
-    mark(2);
-    if (weights)
-      hipLaunchKernelGGL(la_fused_prefill_kernel<true>, grid, dim3(kOutThreads), 0, stream, p);
-    else
-      hipLaunchKernelGGL(la_fused_prefill_kernel<false>, grid, dim3(kOutThreads), 0, stream, p);
-    mark(3);
-    const hipError_t launch = hipGetLastError();
-    return err != hipSuccess ? err : launch;
-  }
   mark(0);
-  if (plan.nwork > 0) {
+  if (plan.nwork > 0 && !plan.direct) {
     if (weights)
       hipLaunchKernelGGL((la_chunk_state_kernel<true, false>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((la_chunk_state_kernel<false, false>), grid, dim3(kThreads), 0, stream, p);
   }
   mark(1);
-  if (plan.scan)
+  if (plan.scan && !plan.direct)
     hipLaunchKernelGGL(la_state_scan_kernel<false>, dim3((unsigned)((scan_threads + 255) / 256)), dim3(256), 0,
                        stream, p);
   mark(2);

@@ -69,8 +69,7 @@ typedef enum {
   LA_ERR_ALIASING = 5,    /* o overlaps an input, or S_out overlaps an activation      */
   LA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than la_prefill_workspace_bytes */
   LA_ERR_HIP = 7,         /* a kernel launch failed                                    */
-  LA_ERR_CAPTURING = 8,   /* la_prefill_varlen on a stream that is capturing a graph   */
-  LA_ERR_SCRATCH = 9      /* la_prefill_noalloc: the plan exceeds its static scratch   */
+  LA_ERR_CAPTURING = 8    /* la_prefill_varlen on a stream that is capturing a graph   */
 } la_status;
 
 typedef uint16_t la_bf16; /* raw bfloat16 bits */
@@ -84,9 +83,13 @@ const char* la_status_string(la_status s);
 /*
  * Bytes of device workspace la_prefill needs for this shape and chunk (0 for an
  * invalid shape).  A segment is a run of consecutive chunks handled by one
- * workgroup.  Chunk 64 (one pass): two fp32 D x D hand-off states per (b, h)
- * when a (b, h) has more than one segment, and a few KiB of flags.  Chunks 128
- * and 256: one fp32 D x D state per (b, h, segment).
+ * workgroup.  When the B * H sequence-heads alone fill the GPU (at least 256 of
+ * them, and the last round of 256 workgroups at least a quarter used) or the
+ * input is one chunk long, each (b, h) is one segment: one kernel reads k and v
+ * once, starts from S_in and writes S_out, and the workspace is a token 256
+ * bytes.  Otherwise the workspace holds one fp32 D x D state per (b, h,
+ * segment): a first kernel sums each segment's Kh^T V, a scan forms the prefix
+ * states, and the output kernel walks each segment from its prefix.
  */
 size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk);
 
@@ -100,12 +103,9 @@ size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk);
  *   chunk : tokens per chunk of the chunked evaluation: 0 (= 64), 64, 128 or 256.
  *           The result is the same closed form for every chunk; the chunk only
  *           decides which token pairs go through the bf16 score products and
- *           which through the bf16 state operand.  64 is the fast path: one
- *           kernel sums each segment's Kh^T V, hands the running state on to
- *           the next segment's workgroup and walks the segment again for the
- *           outputs.  128 and 256 run three kernels (segment sums, scan, a
- *           single-buffered output kernel that stages k and v of a chunk's
- *           earlier 64-row blocks again for every later block).
+ *           which through the bf16 state operand.  64 is the fast path; 128
+ *           and 256 run a single-buffered kernel that stages k and v of a
+ *           chunk's earlier 64-row blocks again for every later block.
  *   rope_base : RoPE base (10000 in the workloads); rms_eps : RMSNorm epsilon.
  *   workspace : device buffer of at least la_prefill_workspace_bytes(...) bytes;
  *               its contents on entry are irrelevant and are clobbered.
@@ -120,11 +120,11 @@ la_status la_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v,
 
 /*
  * la_prefill that also records caller-created HIP events (hipEvent_t passed as
- * void*) on `stream` at its kernel boundaries, for per-kernel timing.
- *   Chunk 64 (one pass): events[0] before the flag-clearing kernel, events[1] and
- *   events[2] before the single-pass kernel, events[3] after it.
- *   Chunks 128 and 256: events[0] before the chunk-state kernel, events[1] before
- *   the state scan, events[2] before the output kernel, events[3] after it.
+ * void*) on `stream` at its kernel boundaries, for per-kernel timing:
+ *   events[0] before the chunk-state kernel, events[1] before the state scan,
+ *   events[2] before the output kernel, events[3] after the output kernel
+ *   (with one segment per (b, h) there is no state kernel or scan: events 0, 1
+ *   and 2 all mark the start of the output kernel).
  * n_events must be 4 and every event non-NULL (else LA_ERR_NULL_PTR); the
  * results are identical to la_prefill's.
  */
@@ -140,17 +140,16 @@ la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16*
  * device memory: code under HIP graph capture, serving loops that must not call
  * hipMalloc, harnesses that forbid allocation.  Same arguments, results and
  * errors as la_prefill otherwise.
- * What la_prefill keeps in its workspace lives in a static device array of the
- * library ("scratch", 64 MiB + 16 KiB: room for 1024 fp32 128 x 128 states and
- * their flags; each GPU the library runs on holds its own copy from the first
- * call on it until the process ends).  The call allocates nothing: the first
- * call on a device looks up the array's device address (hipGetSymbolAddress)
- * and keeps it.  When la_prefill's plan would need more than the scratch holds,
- * chunk 64 runs one segment per (b, h) (no hand-off states) and chunks 128 and
- * 256 cut each (b, h) into fewer, longer segments (same closed form; state sums
- * grouped differently, so results may differ from la_prefill's by rounding);
- * chunks 128 and 256 with B * H above 1024 return LA_ERR_SCRATCH before anything
- * is enqueued.
+ * The segment states live in a static device array of the library ("scratch",
+ * 64 MiB = 1024 fp32 128 x 128 states; each GPU the library runs on holds its own
+ * copy from the first call on it until the process ends).  The call allocates
+ * nothing: the first call on a device looks up the array's device address
+ * (hipGetSymbolAddress) and keeps it.  When la_prefill's plan would need more
+ * than 1024 segment states, the call cuts each (b, h) into fewer, longer
+ * segments, down to one segment per (b, h), which keeps no states at all (same
+ * closed form; the fp32 state sums are grouped differently, so results may
+ * differ from la_prefill's by rounding).  Every shape la_prefill accepts is
+ * served.
  * Every call on a GPU shares that GPU's scratch: calls that overlap in time on
  * one GPU (on different streams, or from several threads without ordering)
  * race and must not be issued; calls ordered on one stream are safe.  The

@@ -41,35 +41,38 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     for s, name in ((0, b"LA_OK"), (1, b"LA_ERR_NULL_PTR"), (2, b"LA_ERR_BAD_SHAPE"), (3, b"LA_ERR_UNSUPPORTED"),
                     (4, b"LA_ERR_ALIGNMENT"), (5, b"LA_ERR_ALIASING"), (6, b"LA_ERR_WORKSPACE"), (7, b"LA_ERR_HIP"),
-                    (8, b"LA_ERR_CAPTURING"), (9, b"LA_ERR_SCRATCH")):
+                    (8, b"LA_ERR_CAPTURING")):
         assert lib.la_status_string(s).startswith(name)
     assert lib.la_status_string(99) == b"unknown la_status"
 
 
 def test_workspace_bytes(lib):
+    # one fp32 128x128 state per (b, h, segment). One round of 256 workgroups while
+    # segments stay within 128 chunks of 64; then 128-chunk segments up to 1024
+    # workgroups; then longer segments. When the B * H sequence-heads fill the
+    # device by themselves (or the input is one chunk), one segment per (b, h) and
+    # no states: 256 bytes.
     st = 128 * 128 * 4
-    # chunk 64 (single pass): two hand-off states per (b, h) when a (b, h) has more
-    # than one segment, plus the sync words (a 64-word header and one flag per
-    # slot and consumer wave); one segment per (b, h) needs only the header
-    sync = lambda slots: (64 + 4 * slots) * 4  # noqa: E731
-    for B, T, H in ((1, 262144, 32), (1, 32768, 32), (1, 65536, 32), (1, 1 << 20, 32), (4, 8192, 32),
-                    (1, 300, 2)):
-        assert lib.la_prefill_workspace_bytes(B, T, H, 128, 0) == 2 * B * H * st + sync(2 * B * H), (B, T, H)
-        assert lib.la_prefill_workspace_bytes(B, T, H, 128, 64) == lib.la_prefill_workspace_bytes(B, T, H, 128, 0)
-    assert lib.la_prefill_workspace_bytes(1, 64, 1, 128, 0) == sync(0)      # one segment
-    assert lib.la_prefill_workspace_bytes(300, 64, 1, 128, 0) == sync(0)
+    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 0) == 32 * 32 * st
+    assert lib.la_prefill_workspace_bytes(1, 32768, 32, 128, 64) == 32 * 8 * st     # 64-chunk segments
+    assert lib.la_prefill_workspace_bytes(1, 65536, 32, 128, 0) == 32 * 8 * st      # 128-chunk segments
+    assert lib.la_prefill_workspace_bytes(1, 131072, 32, 128, 0) == 32 * 16 * st    # 512 workgroups
+    assert lib.la_prefill_workspace_bytes(1, 1 << 20, 32, 128, 0) == 32 * 32 * st   # 512-chunk segments
+    assert lib.la_prefill_workspace_bytes(4, 8192, 32, 128, 0) == 128 * 2 * st
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 0) == 2 * 5 * 128 * 128 * 4
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 64, 0) == 0
     assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 96) == 0
-    # chunks 128 and 256 (state sums, scan, output): one fp32 state per (b, h,
-    # segment); one round of 256 workgroups while segments stay within 128
-    # sub-chunks of 64, then 128-sub-chunk segments up to 1024 workgroups, then
-    # longer segments; segments hold whole chunks
-    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 128) == 2 * 3 * st
-    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 256) == 2 * 2 * st
-    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 256) == 32 * 32 * st
-    assert lib.la_prefill_workspace_bytes(1, 32768, 32, 128, 128) == 32 * 8 * st
-    assert lib.la_prefill_workspace_bytes(1, 1 << 20, 32, 128, 128) == 32 * 32 * st
+    # wider chunks: segments hold whole chunks (5 sub-chunks of 64 -> 3 or 2 segments)
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 128) == 2 * 3 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 300, 2, 128, 256) == 2 * 2 * 128 * 128 * 4
+    assert lib.la_prefill_workspace_bytes(1, 262144, 32, 128, 256) == 32 * 32 * 128 * 128 * 4
     assert lib.la_prefill_workspace_bytes(0, 300, 2, 128, 0) == 0
+    # one segment per (b, h): one chunk, or enough sequence-heads
+    for B, T, H, C in ((1, 64, 2, 0), (1, 200, 3, 256), (8, 32768, 32, 0), (2, 5000, 128, 128),
+                       (1, 100, 1000, 0), (3, 1000, 100, 0)):
+        assert lib.la_prefill_workspace_bytes(B, T, H, 128, C) == 256, (B, T, H, C)
+    # 300 sequence-heads leave the second round of 256 mostly empty: segments
+    assert lib.la_prefill_workspace_bytes(1, 65536, 300, 128, 0) == 300 * 4 * st
 
 
 # fake, never-dereferenced device addresses (validation fails before any use)
@@ -132,10 +135,9 @@ def test_varlen_workspace_bytes(lib):
     assert f(1, _cu([0, 2]), 2, 128, 0) == 256 + 2 * 128 * 128 * 4
     # single-token and empty sequences need no segment states
     assert f(3, _cu([0, 1, 1, 2]), 2, 128, 0) == 256
-    # two 300-token sequences: 5 one-chunk segments each (the three-kernel form),
-    # one state per segment and head, after 10 x 24 + 2 x 16 bytes of tables
-    # rounded up to 512
-    assert f(2, _cu([0, 300, 600]), 2, 128, 0) == 512 + 10 * 2 * 128 * 128 * 4
+    # equal lengths: the same 10 segments as la_prefill, after 10 x 24 + 2 x 16 bytes of
+    # tables rounded up to 512
+    assert f(2, _cu([0, 300, 600]), 2, 128, 0) - 512 == lib.la_prefill_workspace_bytes(2, 300, 2, 128, 0)
     assert f(2, _cu([0, 3, 2]), 2, 128, 0) == 0   # decreasing offsets
     assert f(1, _cu([1, 3]), 2, 128, 0) == 0      # does not start at 0
     assert f(1, _cu([0, 3]), 2, 64, 0) == 0

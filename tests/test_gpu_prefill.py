@@ -88,6 +88,47 @@ def test_wide_chunk_matches_oracle(la, chunk, B, T, H, pos0, S_std, weights):
     assert_S_close(to_np(S), S_ref)
 
 
+DIRECT_CASES = [
+    # chunk, B, T, H, pos0, S_std, weights: enough sequence-heads that each (b, h) is
+    # one segment (no state pass; the output kernel starts from S_in)
+    (64, 8, 1000, 32, 0, 0.0, False),
+    (64, 2, 777, 512, 262144, 0.3, True),
+    (128, 8, 1000, 32, 5, 0.2, False),
+    (256, 4, 613, 64, 1000, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("chunk,B,T,H,pos0,S_std,weights", DIRECT_CASES)
+def test_one_segment_per_head_matches_oracle(la, chunk, B, T, H, pos0, S_std, weights):
+    print(f"one-segment case C={chunk} B={B} T={T} H={H} pos0={pos0}", flush=True)
+    assert la.prefill_workspace_bytes(B, T, H, D, chunk) == 256  # the direct form
+    q, k, v, g, S_in, qw, kw = _inputs(B, T, H, seed=41 + T + chunk, S_std=S_std, weights=weights)
+    o, S = la.prefill(q, k, v, g, S_in=S_in, pos0=pos0, chunk=chunk, q_norm_w=qw, k_norm_w=kw)
+    torch.cuda.synchronize()
+    # every head's final state, and the outputs of sampled (b, h)
+    bs = sorted({0, B - 1})
+    hs = sorted({0, H // 2, H - 1})
+    sel = lambda t: t[bs][:, :, hs]  # noqa: E731
+    o_ref, S_ref = _oracle(sel(q), sel(k), sel(v), sel(g), None if S_in is None else S_in[bs][:, hs], pos0, qw, kw)
+    assert_o_close(to_np(sel(o)), o_ref)
+    assert_S_close(to_np(S[bs][:, hs]), S_ref)
+    _, S_all = _oracle(q, k, v, g, S_in, pos0, qw, kw)
+    assert_S_close(to_np(S), S_all, what="every final state")
+
+
+def test_one_segment_in_place_carry(la):
+    """S_in == S_out with one segment per (b, h): each workgroup reads its state
+    before it writes it."""
+    q, k, v, g, S, _, _ = _inputs(4, 300, 64, seed=43, S_std=0.2)
+    S_ref_in = to_np(S)
+    o, S_out = la.prefill(q, k, v, g, S_in=S, S_out=S, pos0=17)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr()
+    o_ref, S_ref = oracle.forward(to_np32(q), to_np32(k), to_np32(v), to_np32(g), S=S_ref_in, pos0=17)
+    assert_o_close(to_np(o), o_ref)
+    assert_S_close(to_np(S), S_ref)
+
+
 def test_chunk_sizes_agree(la):
     """Every chunk size evaluates the same closed form: the outputs agree with each
     other within the tolerance to the oracle (the typical row far inside it), and

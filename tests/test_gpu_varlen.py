@@ -89,11 +89,7 @@ def test_varlen_without_initial_state_and_in_place(la):
 
 
 def test_varlen_equal_lengths_is_prefill(la):
-    """Equal lengths give the segments la_prefill uses.  Varlen takes the
-    three-kernel form (segment sums, scan, output) and la_prefill the single pass,
-    which forms the same segment prefixes in the same order: the outputs are
-    identical, and the final states differ only in the order of the last
-    segment's fp32 additions."""
+    """Equal lengths give the segments la_prefill uses, so the results are identical."""
     B, T, H = 3, 777, 4
     gen = workloads.generator(61, "cuda")
     q, k, v, g = workloads.activations(B, T, H, D, 61, "cuda", gen=gen)
@@ -104,8 +100,7 @@ def test_varlen_equal_lengths_is_prefill(la):
                              S_in=S_in)
     torch.cuda.synchronize()
     assert torch.equal(o, flat(o_ref))
-    rel = float(torch.linalg.norm(S - S_ref) / torch.linalg.norm(S_ref))
-    assert rel <= 1e-6, rel
+    assert torch.equal(S, S_ref)
 
 
 def test_varlen_decode_rows_are_decode_steps(la):

@@ -48,6 +48,13 @@ DECODE_B64 = Workload("decode_b64_h32_d128_pos262144", 64, 1, 32, 128, seed=4, p
 
 ALL = (TINY, PREFILL_32K, PREFILL_256K, STREAM_1M, DECODE_B64)
 
+# Beside those: a batch of 8 prompts of 32K tokens (as many tokens as the 256K
+# prefill, spread over 256 sequence-heads), and the batched decode at 256
+# sequences, whose 512 MiB of states exceed the GPU's 256 MB memory-side cache.
+PREFILL_B8_32K = Workload("prefill_b8_h32_d128_t32768", 8, 32768, 32, 128, seed=10)
+DECODE_B256 = Workload("decode_b256_h32_d128_pos262144", 256, 1, 32, 128, seed=11, pos0=262144,
+                       steps=200, state_std=0.02)
+
 
 @dataclasses.dataclass(frozen=True)
 class MixedBatch:
