@@ -98,11 +98,12 @@ bool plan_prefill(int B, int T, int H, int chunk, PrefillPlan* plan, bool direct
   // Work is counted in 64-token sub-chunks; a segment holds whole C-chunks.
   const int64_t sub = C / 64;
   const int64_t bh = (int64_t)B * H;
+  if (bh > kMaxHeads) return false;  // before any product with it can overflow
   const int64_t nchunks = ((int64_t)T + 63) / 64;
   int64_t cps = segment_chunks(bh * nchunks, sub);
   if (cps > (nchunks + sub - 1) / sub * sub) cps = (nchunks + sub - 1) / sub * sub;
   const int64_t nseg = (nchunks + cps - 1) / cps;
-  if (bh * nseg > kMaxWorkgroups || bh > kMaxHeads) return false;
+  if (bh * nseg > kMaxWorkgroups) return false;
   plan->C = C;
   plan->nchunks = (int)nchunks;
   plan->cps = (int)cps;
@@ -198,116 +199,6 @@ la_status plan_varlen(int nseq, const int32_t* cu, const int64_t* pos0, int H, i
 
 }  // namespace la
 
-using namespace la;
-
-extern "C" {
-
-int la_version(void) { return 200; }
-
-const char* la_status_string(la_status s) {
-  switch (s) {
-    case LA_OK: return "LA_OK";
-    case LA_ERR_NULL_PTR: return "LA_ERR_NULL_PTR: a required pointer is NULL";
-    case LA_ERR_BAD_SHAPE: return "LA_ERR_BAD_SHAPE: B, T and H must be >= 1 and the launch must fit";
-    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: need D == 128, chunk in {0, 64, 128, 256}, rope_base > 0 and finite, rms_eps >= 0 and finite";
-    case LA_ERR_ALIGNMENT: return "LA_ERR_ALIGNMENT: pointers must be 16-byte aligned";
-    case LA_ERR_ALIASING: return "LA_ERR_ALIASING: an output overlaps another argument";
-    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
-    case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
-    case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
-  }
-  return "unknown la_status";
-}
-
-size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk) {
-  PrefillPlan plan;
-  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan, true)) return 0;
-  return plan.ws_bytes;
-}
-
-static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16* v,
-                              const la_bf16* gate_logits, const float* S_in, float* S_out,
-                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
-                              float rope_base, float rms_eps, const float* q_norm_w,
-                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
-                              void* stream, hipEvent_t const* events,
-                              const PrefillPlan* given_plan = nullptr) {
-  if (!q || !k || !v || !gate_logits || !S_out || !o || !workspace) return LA_ERR_NULL_PTR;
-  if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
-  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
-  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
-  PrefillPlan plan;
-  if (given_plan != nullptr)
-    plan = *given_plan;
-  else if (!plan_prefill(B, T, H, chunk, &plan, true))
-    return LA_ERR_BAD_SHAPE;
-  const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
-  for (const void* ptr : ptrs)
-    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
-
-  const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
-  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
-  const void* ins[] = {q, k, v, gate_logits};
-  for (const void* in : ins) {
-    if (overlaps(o, act, in, act) || overlaps(S_out, st, in, act)) return LA_ERR_ALIASING;
-  }
-  if (overlaps(o, act, S_out, st) || overlaps(o, act, S_in, st)) return LA_ERR_ALIASING;
-  if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;
-  const void* all[] = {q, k, v, gate_logits, S_in, S_out, o};
-  for (const void* x : all)
-    if (overlaps(workspace, plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
-  if (workspace_bytes < plan.ws_bytes) return LA_ERR_WORKSPACE;
-
-  PrefillParams p{};
-  p.q = q;
-  p.k = k;
-  p.v = v;
-  p.g = gate_logits;
-  p.o = o;
-  p.ws = static_cast<float*>(workspace);
-  p.segs = nullptr;
-  p.seqs = nullptr;
-  p.S_in = S_in;
-  p.S_out = S_out;
-  p.qw = q_norm_w;
-  p.kw = k_norm_w;
-  p.B = B;
-  p.T = T;
-  p.H = H;
-  p.nseg = plan.nseg;
-  p.cps = plan.cps;
-  p.pos0 = pos0;
-  p.eps = rms_eps;
-  rope_freqs(rope_base, &p.freqs);
-  return launch_prefill(p, plan, static_cast<hipStream_t>(stream), events) == hipSuccess ? LA_OK
-                                                                                     : LA_ERR_HIP;
-}
-
-la_status la_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v,
-                     const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
-                     int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
-                     float rms_eps, const float* q_norm_w, const float* k_norm_w,
-                     void* workspace, size_t workspace_bytes, void* stream) {
-  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
-                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream, nullptr);
-}
-
-la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16* v,
-                              const la_bf16* gate_logits, const float* S_in, float* S_out,
-                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
-                              float rope_base, float rms_eps, const float* q_norm_w,
-                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
-                              void* stream, void* const* events, int n_events) {
-  if (!events || n_events != 4) return LA_ERR_NULL_PTR;
-  for (int i = 0; i < 4; ++i)
-    if (!events[i]) return LA_ERR_NULL_PTR;
-  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
-                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream,
-                      reinterpret_cast<hipEvent_t const*>(events));
-}
-
-}  // extern "C"
-
 // ---------------------------------------------------------------------------
 // Scratch of la_prefill_noalloc: a static device array holding up to
 // kScratchStates fp32 D x D segment states.  Every GPU the library runs on holds
@@ -359,7 +250,123 @@ la_status scratch_address(hipStream_t stream, void** out) {
 }  // namespace
 }  // namespace la
 
+using namespace la;
+
 extern "C" {
+
+int la_version(void) { return 200; }
+
+const char* la_status_string(la_status s) {
+  // Callers in other languages pass any integer; read it as one (an enum
+  // variable holding a value outside its enumerators would be undefined in C++).
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_NULL_PTR: return "LA_ERR_NULL_PTR: a required pointer is NULL";
+    case LA_ERR_BAD_SHAPE: return "LA_ERR_BAD_SHAPE: B, T and H must be >= 1 and the launch must fit";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: need D == 128, chunk in {0, 64, 128, 256}, rope_base > 0 and finite, rms_eps >= 0 and finite";
+    case LA_ERR_ALIGNMENT: return "LA_ERR_ALIGNMENT: pointers must be 16-byte aligned";
+    case LA_ERR_ALIASING: return "LA_ERR_ALIASING: an output overlaps another argument";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE: workspace missing or too small";
+    case LA_ERR_HIP: return "LA_ERR_HIP: kernel launch failed";
+    case LA_ERR_CAPTURING: return "LA_ERR_CAPTURING: the stream is capturing a graph and this call copies host data";
+  }
+  return "unknown la_status";
+}
+
+size_t la_prefill_workspace_bytes(int B, int T, int H, int D, int chunk) {
+  PrefillPlan plan;
+  if (D != kHeadDim || !plan_prefill(B, T, H, chunk, &plan, true)) return 0;
+  return plan.ws_bytes;
+}
+
+static la_status prefill_impl(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                              const la_bf16* gate_logits, const float* S_in, float* S_out,
+                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
+                              float rope_base, float rms_eps, const float* q_norm_w,
+                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream, hipEvent_t const* events,
+                              const PrefillPlan* given_plan = nullptr, bool use_scratch = false) {
+  // use_scratch: the segment states go to the library's static scratch, whose
+  // address is taken only once the call has passed every check
+  if (!q || !k || !v || !gate_logits || !S_out || !o || (!workspace && !use_scratch)) return LA_ERR_NULL_PTR;
+  if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
+  if (D != kHeadDim || (chunk != 0 && chunk != 64 && chunk != 128 && chunk != 256)) return LA_ERR_UNSUPPORTED;
+  if (!finite_positive(rope_base) || !isfinite(rms_eps) || rms_eps < 0.0f) return LA_ERR_UNSUPPORTED;
+  PrefillPlan plan;
+  if (given_plan != nullptr)
+    plan = *given_plan;
+  else if (!plan_prefill(B, T, H, chunk, &plan, true))
+    return LA_ERR_BAD_SHAPE;
+  const void* ptrs[] = {q, k, v, gate_logits, S_in, S_out, o, workspace, q_norm_w, k_norm_w};
+  for (const void* ptr : ptrs)
+    if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+
+  const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
+  const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
+  const void* ins[] = {q, k, v, gate_logits};
+  for (const void* in : ins) {
+    if (overlaps(o, act, in, act) || overlaps(S_out, st, in, act)) return LA_ERR_ALIASING;
+  }
+  if (overlaps(o, act, S_out, st) || overlaps(o, act, S_in, st)) return LA_ERR_ALIASING;
+  if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;
+  const void* all[] = {q, k, v, gate_logits, S_in, S_out, o};
+  for (const void* x : all)
+    if (overlaps(workspace, plan.ws_bytes, x, x == S_in || x == S_out ? st : act)) return LA_ERR_ALIASING;
+  if (workspace_bytes < plan.ws_bytes) return LA_ERR_WORKSPACE;
+  if (use_scratch) {
+    const la_status got = scratch_address(static_cast<hipStream_t>(stream), &workspace);
+    if (got != LA_OK) return got;
+  }
+
+  PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.g = gate_logits;
+  p.o = o;
+  p.ws = static_cast<float*>(workspace);
+  p.segs = nullptr;
+  p.seqs = nullptr;
+  p.S_in = S_in;
+  p.S_out = S_out;
+  p.qw = q_norm_w;
+  p.kw = k_norm_w;
+  p.B = B;
+  p.T = T;
+  p.H = H;
+  p.nseg = plan.nseg;
+  p.cps = plan.cps;
+  p.pos0 = pos0;
+  p.eps = rms_eps;
+  rope_freqs(rope_base, &p.freqs);
+  return launch_prefill(p, plan, static_cast<hipStream_t>(stream), events) == hipSuccess ? LA_OK
+                                                                                     : LA_ERR_HIP;
+}
+
+la_status la_prefill(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                     const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
+                     int B, int T, int H, int D, int64_t pos0, int chunk, float rope_base,
+                     float rms_eps, const float* q_norm_w, const float* k_norm_w,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
+                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream, nullptr);
+}
+
+la_status la_prefill_profiled(const la_bf16* q, const la_bf16* k, const la_bf16* v,
+                              const la_bf16* gate_logits, const float* S_in, float* S_out,
+                              la_bf16* o, int B, int T, int H, int D, int64_t pos0, int chunk,
+                              float rope_base, float rms_eps, const float* q_norm_w,
+                              const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                              void* stream, void* const* events, int n_events) {
+  if (!events || n_events != 4) return LA_ERR_NULL_PTR;
+  for (int i = 0; i < 4; ++i)
+    if (!events[i]) return LA_ERR_NULL_PTR;
+  return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base,
+                      rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes, stream,
+                      reinterpret_cast<hipEvent_t const*>(events));
+}
 
 la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* v,
                              const la_bf16* gate_logits, const float* S_in, float* S_out, la_bf16* o,
@@ -371,11 +378,8 @@ la_status la_prefill_noalloc(const la_bf16* q, const la_bf16* k, const la_bf16* 
   PrefillPlan plan;
   if (!plan_prefill(B, T, H, chunk, &plan, true)) return LA_ERR_BAD_SHAPE;
   cap_plan(B, H, kScratchBytes, &plan);
-  void* ws = nullptr;
-  const la_status got = scratch_address(static_cast<hipStream_t>(stream), &ws);
-  if (got != LA_OK) return got;
   return prefill_impl(q, k, v, gate_logits, S_in, S_out, o, B, T, H, D, pos0, chunk, rope_base, rms_eps,
-                      q_norm_w, k_norm_w, ws, kScratchBytes, stream, nullptr, &plan);
+                      q_norm_w, k_norm_w, nullptr, kScratchBytes, stream, nullptr, &plan, true);
 }
 
 la_status la_decode_step(const la_bf16* q, const la_bf16* k, const la_bf16* v,
@@ -573,8 +577,8 @@ la_status la_layer_forward(const la_bf16* x, const la_bf16* w_qkvg, const la_bf1
       {w_o, (uint64_t)hidden * HD * sizeof(la_bf16)}, {S_in, st}, {S_out, st}, {y, xbytes}};
   for (const auto& r : regions)
     if (overlaps(workspace, need, r.first, r.second)) return LA_ERR_ALIASING;
-  for (const auto& r : regions)
-    if (r.first != y && overlaps(y, xbytes, r.first, r.second)) return LA_ERR_ALIASING;
+  for (int i = 0; i < 5; ++i)  // every region but y's own (index 5), even one starting at y
+    if (overlaps(y, xbytes, regions[i].first, regions[i].second)) return LA_ERR_ALIASING;
   for (const auto& r : {regions[0], regions[1], regions[2], regions[5]})
     if (overlaps(S_out, st, r.first, r.second)) return LA_ERR_ALIASING;
   if (S_in && S_in != S_out && overlaps(S_in, st, S_out, st)) return LA_ERR_ALIASING;

@@ -215,6 +215,7 @@ def test_linear_and_layer_validation(lib):
     assert layer(H=3) == 3                   # H * D = 384 is not a multiple of 256
     assert layer(y=A + 256 * MB + 8) == 4
     assert layer(y=A + 1024) == 5            # y overlaps x
+    assert layer(y=A) == 5                   # y is x itself
     assert layer(ws=A + 256 * MB) == 5       # workspace overlaps y
     assert layer(ws_bytes=4096) == 6
 
