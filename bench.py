@@ -368,7 +368,7 @@ def bench_layer(la, torch, workloads, hip, args, steps=5):
         "workload": w.name, "tokens": M, "steps": steps,
         "layer_ms": round(layer_ms, 4), "tokens_per_s": round(M / (layer_ms / 1e3), 1),
         "qkvg_projection": {"ms": round(in_ms, 4), "tflops": round(tf_in, 1),
-                            "roofline": {"bound": "mfma", "kernel": "la_linear_kernel", "achieved": round(tf_in, 1),
+                            "roofline": {"bound": "mfma", "kernel": "la_linear_ring_kernel", "achieved": round(tf_in, 1),
                                          "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                          "frac": round(tf_in / BF16_MFMA_PEAK_TFLOPS, 4)}},
         "o_projection": {"ms": round(out_ms, 4), "tflops": round(f_out / (out_ms / 1e3) / 1e12, 1),

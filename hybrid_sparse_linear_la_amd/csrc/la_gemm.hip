@@ -10,13 +10,23 @@
 // nsplit] tensors (the fused q/k/v/gate projection writes q, k, v, g directly).
 // Requires K % 64 == 0 and (N / nsplit) % 256 == 0; M is arbitrary.
 //
-// Workgroup tile 256 x 256, K step 64, LDS double-buffered (160 KiB).  Eight
-// waves, wave (wm, wn) computes rows [64 wm, 64 wm + 64) x columns
-// [128 wn, 128 wn + 128) of the tile as 4 x 8 accumulator tiles of
-// v_mfma_f32_16x16x32_bf16.  Both operands are K-contiguous, so every MFMA
-// operand is one 16-byte LDS read per lane.  The tile is formed transposed
-// (W rows as the A operand), so each lane ends up holding 4 consecutive output
-// columns of one row and stores them as 8 bytes.
+// Workgroup tile 256 x 256, eight waves: wave (wm, wn) computes rows
+// [64 wm, 64 wm + 64) x columns [128 wn, 128 wn + 128) of the tile as 4 x 8
+// accumulator tiles of v_mfma_f32_16x16x32_bf16.  Both operands are
+// K-contiguous, so every MFMA operand is one 16-byte LDS read per lane.  The
+// tile is formed transposed (W rows as the A operand), so each lane ends up
+// holding 4 consecutive output columns of one row and stores them as 8 bytes.
+//
+// Two kernels share that tiling:
+//   * la_linear_ring_kernel (K % 128 == 0, the projection shapes): K steps of
+//     32 through a four-slot LDS ring filled by direct global-to-LDS loads
+//     (16 bytes per lane, no register staging and no LDS store instructions),
+//     three steps in flight; 64-byte rows with an XOR swizzle of the 16-byte
+//     pieces keep the operand reads conflict-free.
+//   * la_linear_kernel (any K % 64 == 0): K steps of 64 double-buffered in LDS
+//     through registers.
+// Both sum each output in the same order (32-deep MFMA steps in K order), so
+// they give identical results.
 #include "la_device.hpp"
 #include "la_internal.hpp"
 
@@ -126,11 +136,152 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_kernel(LinearParams p)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel.  Stage kt (K columns [32 kt, 32 kt + 32)) of both operands sits in
+// slot kt % 4: a 256-row x 64-byte tile per operand, each row's four 16-byte
+// pieces stored at piece position c ^ ((row / 4) % 4).  A wave loads 16 rows per
+// direct load (lane i: row i / 4, position i % 4), so it fetches the global piece
+// that belongs there; the MFMA reads of 16 rows at one piece column then hit 16
+// different bank groups.
+constexpr int kRingBK = 32, kRingSlots = 4;
+constexpr int kRingTile = kBM * kRingBK * 2;  // 16 KiB per operand per stage
+
+__device__ __forceinline__ int ring_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
+
+// Direct global -> LDS load of 16 bytes per lane from base + off (lane i's bytes
+// land at LDS byte address lds + 16 i).  Issued from assembly so that the
+// compiler, which cannot tell the ring slots apart across loop iterations, adds
+// no waits of its own (it would wait for every load before each LDS read); every
+// wait on these loads is explicit in the kernel.  No register is written.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* ptr) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)ptr);
+}
+
+__global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearParams p) {
+  // one LDS object per slot and operand
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kRingTile], sA1[kRingTile], sA2[kRingTile], sA3[kRingTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kRingTile], sB1[kRingTile], sB2[kRingTile], sB3[kRingTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int wm = w & 3, wn = w >> 2;
+  const int tiles_n = p.N / kBN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int64_t m0 = (int64_t)tm * kBM;
+  const int n0 = tn * kBN;
+  const int K = p.K;
+
+  // this wave loads rows 32 w .. 32 w + 31 of both operand tiles, 16 per load
+  const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(p.x + m0 * K);
+  const uint8_t* const wbase = reinterpret_cast<const uint8_t*>(p.w + (int64_t)n0 * K);
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 32 * w + 16 * u + (lane >> 2);
+    const int piece = ring_pos(row, lane & 3);  // the position is its own inverse
+    const int arow = m0 + row < p.M ? row : (int)(p.M - 1 - m0);  // rows past M re-read the last row
+    aoff[u] = (uint32_t)(arow * K + 8 * piece) * 2u;
+    boff[u] = (uint32_t)(row * K + 8 * piece) * 2u;
+  }
+  const uint32_t la[4] = {lds_addr(sA0), lds_addr(sA1), lds_addr(sA2), lds_addr(sA3)};
+  const uint32_t lb[4] = {lds_addr(sB0), lds_addr(sB1), lds_addr(sB2), lds_addr(sB3)};
+  const int nk = K / kRingBK;
+  auto issue = [&](int kt, int slot) {
+    kt = min(kt, nk - 1);  // past the end: reload the last stage into a slot nobody reads
+    const uint8_t* xa = xbase + (int64_t)kt * kRingBK * 2;
+    const uint8_t* wa = wbase + (int64_t)kt * kRingBK * 2;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t rows = __builtin_amdgcn_readfirstlane((32 * w + 16 * u) * 64);
+      dma16(xa, aoff[u], la[slot] + rows);
+      dma16(wa, boff[u], lb[slot] + rows);
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+    bf16x8 xa[4], wb[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wm + 16 * i + n16;
+      xa[i] = as_bf16x8(lds_ld<uint4>(A, row * 64 + 16 * ring_pos(row, g4)));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 128 * wn + 16 * j + n16;
+      wb[j] = as_bf16x8(lds_ld<uint4>(B, row * 64 + 16 * ring_pos(row, g4)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[j], xa[i], acc[i][j]);
+  };
+  // stage kt's loads (this wave's) are done once at most the two later stages'
+  // 4 loads each are outstanding; the barrier makes that hold for every wave,
+  // and also that every wave has finished reading the slot reloaded next
+  auto sync_stage = [&]() {
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  for (int kt = 0; kt < nk; kt += 4) {  // nk % 4 == 0
+    sync_stage();
+    issue(kt + 3, 3);
+    compute(sA0, sB0);
+    sync_stage();
+    issue(kt + 4, 0);
+    compute(sA1, sB1);
+    sync_stage();
+    issue(kt + 5, 1);
+    compute(sA2, sB2);
+    sync_stage();
+    issue(kt + 6, 2);
+    compute(sA3, sB3);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the workgroup ends
+
+  const int split_cols = p.N / p.nsplit;
+  const int part = n0 / split_cols;
+  uint16_t* const out = p.y[part];
+  const int col0 = n0 - part * split_cols + 128 * wn + 4 * g4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t row = m0 + 64 * wm + 16 * i + n16;
+    if (row < p.M) {
+      uint16_t* dst = out + row * split_cols + col0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<uint2*>(dst + 16 * j) =
+            make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_linear(const LinearParams& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + kBM - 1) / kBM) * (int64_t)(p.N / kBN);
-  hipLaunchKernelGGL(la_linear_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, p);
+  // the ring kernel forms per-lane byte offsets within a 256-row tile in 32 bits
+  const bool ring = p.K % (kRingSlots * kRingBK) == 0 && (int64_t)kBM * p.K * 2 < ((int64_t)1 << 32);
+  if (ring)
+    hipLaunchKernelGGL(la_linear_ring_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(la_linear_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, p);
   return hipGetLastError();
 }
 
