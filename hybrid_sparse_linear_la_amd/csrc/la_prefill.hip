@@ -377,13 +377,17 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
     __syncthreads();
   }
   if (direct) {
-    float* dst = p.S_out + bh * kD * kD;
+    // lane offsets formed afresh here, so that none stays live across the loop
+    int t2 = threadIdx.x;
+    asm volatile("" : "+v"(t2));
+    float* dst = p.S_out + ((int64_t)tl.b * p.H + tl.h) * kD * kD + (int64_t)(4 * ((t2 & 63) >> 4)) * kD +
+                 32 * (t2 >> 6) + (t2 & 15);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int rtk = 0; rtk < 8; ++rtk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dst[state_elem(rtk, r, 2 * w + dt, g4, n16)] = Sacc[dt][rtk][r];
+        for (int r = 0; r < 4; ++r) dst[(16 * rtk + r) * kD + 16 * dt] = Sacc[dt][rtk][r];
   }
 }
 
