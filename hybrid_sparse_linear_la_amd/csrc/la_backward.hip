@@ -38,6 +38,22 @@ namespace {
 
 constexpr int kBwdThreads = 512;
 
+// Row loads that stay in L2: q, k, do and the gate are read again later in the
+// same chunk (do and the gate by the outputs in another lane layout, q and k by the
+// prologue backward), and with streaming loads those second reads went to the
+// fabric (the chunk kernel moved 27.9 GB at 256K against 19.5 GB by design).  v is read
+// once and keeps the streaming loads of load_rows.
+template <int M, int kStep>
+__device__ __forceinline__ void load_rows_cached(const uint16_t* __restrict__ base, int64_t rs, int nvalid, int rg,
+                                                 int j, Rows<M>& R) {
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const uint16_t* src = base + (int64_t)min(rg + kStep * m, nvalid - 1) * rs;
+    R.lo[m] = *reinterpret_cast<const uint2*>(src + 4 * j);
+    R.hi[m] = *reinterpret_cast<const uint2*>(src + kHalf + 4 * j);
+  }
+}
+
 // The chunk's q, k, v and du tiles use the TilePi layout (288-byte rows, key
 // dims stored in order pi); the S^T, G^T snapshots and the score tiles are
 // row-major with natural columns.
@@ -134,7 +150,7 @@ __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const flo
 
 // The prologue backward of one chunk inside the chunk kernel: thread (rg, j) takes
 // rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
-// (the snapshot area's rows), q, k again from memory (cached since the chunk's staging).
+// (the snapshot area's rows), q, k again from memory (L2, since the chunk's staging).
 // dw receives the thread's norm-weight gradient terms (its two rows summed).
 template <bool kWeights>
 __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
@@ -142,8 +158,8 @@ __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const
                                                    const uint8_t* sDq, const uint8_t* sDk, const uint8_t* sQ,
                                                    float (&dw)[2][8]) {
   Rows<2> X[2];
-  load_rows<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
-  load_rows<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
+  load_rows_cached<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
+  load_rows_cached<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
   float w[2][8];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -243,11 +259,11 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     {
       Rows<2> Qr, Kr, Vr, Dr, Gr;
       const int64_t off = tl.base + (int64_t)t0 * rs;
-      load_rows<2, 32>(p.q + off, rs, nv, rg, j, Qr);
-      load_rows<2, 32>(p.k + off, rs, nv, rg, j, Kr);
+      load_rows_cached<2, 32>(p.q + off, rs, nv, rg, j, Qr);
+      load_rows_cached<2, 32>(p.k + off, rs, nv, rg, j, Kr);
       load_rows<2, 32>(p.v + off, rs, nv, rg, j, Vr);
-      load_rows<2, 32>(p.dout + off, rs, nv, rg, j, Dr);
-      load_rows<2, 32>(p.g + off, rs, nv, rg, j, Gr);
+      load_rows_cached<2, 32>(p.dout + off, rs, nv, rg, j, Dr);
+      load_rows_cached<2, 32>(p.g + off, rs, nv, rg, j, Gr);
       float2 E[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
@@ -264,6 +280,19 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
       du_stage<2, 32, TilePi>(sU, exact ? sUl : nullptr, Dr, Gr, nv, rg, j);
     }
     __syncthreads();
+    // do and g of this lane's output rows in the outputs' layout (rows past the chunk
+    // clamped to its last row), loaded here so that their latency passes under the
+    // scores (L2 hits: the staging loaded the same rows)
+    uint2 dor[4], gr[4];
+    {
+      const int col = 16 * w + 4 * g4;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int64_t crow = tl.base + (int64_t)(t0 + min(16 * rt + n16, nv - 1)) * rs + col;
+        dor[rt] = *reinterpret_cast<const uint2*>(p.dout + crow);
+        gr[rt] = *reinterpret_cast<const uint2*>(p.g + crow);
+      }
+    }
     // ---- scores P = Qh Kh^T and dP = dU V^T (masked to s <= t), 20 tiles over 8 waves
     for (int idx = w; idx < 20; idx += 8) {
       const bool grad = idx >= 10;
@@ -322,14 +351,6 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
     uint2 dqp[4], dkp[4];  // fused: this lane's bf16 dqh, dkh (rows 16 rt + n16, 4 columns)
     {
       const int col = 16 * w + 4 * g4;
-      // do and g of the lane's output rows (rows past the chunk clamped to its last row)
-      uint2 dor[4], gr[4];
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const int64_t crow = tl.base + (int64_t)(t0 + min(16 * rt + n16, nv - 1)) * rs + col;
-        dor[rt] = *reinterpret_cast<const uint2*>(p.dout + crow);
-        gr[rt] = *reinterpret_cast<const uint2*>(p.g + crow);
-      }
       f32x4 acc[4];
       // u = Qh S + (P V)  ->  dg = do * u * sigmoid'(g)
 #pragma unroll
