@@ -411,172 +411,336 @@ __global__ __launch_bounds__(kOutThreads) void la_chunk_output_kernel(PrefillPar
 
 
 // --------------------------------------------------------------------------
-// Wide-chunk output kernel, C = 64 kSub (kSub = 2 or 4).  The chunked form with
-// chunk C: query sub-block i (64 rows) of a chunk takes its scores against key
-// sub-blocks jj <= i (causally masked at jj = i) and its inter-chunk term from the
-// state at the chunk start; the chunk's Kh^T V joins the state after the chunk.
-// Tiles are single-buffered and k, v of sub-block jj are staged again for every
-// i >= jj, so a wider chunk costs more work and more reads than C = 64.  Eight
-// waves; wave w owns value columns [16 w, 16 w + 16) of S and o.  Three barriers
-// per (i, jj): after staging, after the scores, after the intra-chunk product.
-constexpr int kWideThreads = 512;
+// Wide-chunk output kernel, C = 64 kSub (kSub = 2 or 4), in the producer/consumer
+// form of the C = 64 kernel.  The chunked form with chunk C: query sub-block i
+// (64 rows) of a chunk takes its scores against key sub-blocks jj <= i (causally
+// masked at jj = i) and its inter-chunk term from the state at the chunk start;
+// the chunk's Kh^T V joins the state after the chunk.  A segment's work is a
+// sequence of units (i, jj), kSub (kSub + 1) / 2 per chunk in the order of
+// WideSchedule (a segment's last chunk stops after the rows of its sub-blocks).
+// Threads 0..255 are the consumer waves (wave w owns value columns [32w, 32w + 32)
+// of S and o), threads 256..511 the producer waves (thread (rg, j) stages rows
+// rg + 16m, m < 4).  While the consumers work on unit u, the producers stage unit
+// u + 1 into the tiles the consumers are not reading: k and v of sub-block jj into
+// the tile half the schedule names, unless that half already holds them, and q and
+// the gate of sub-block i (at a row's first unit) by the parity of i.  Units u + 2
+// and u + 3 load into registers meanwhile.  Two barriers per unit on both sides.
+// The inter-chunk term of every sub-block of a chunk uses the chunk-start state,
+// kept as bf16 operands while the fp32 state already takes the chunk's sub-blocks.
+constexpr int kWideConsumers = 256;
+constexpr int kWideThreads = kWideConsumers + 256;
+
+// The units of one chunk in order, and the k/v tile half each one reads.  A row
+// (query sub-block i) takes its units together; a unit whose key sub-block is
+// already in a tile half reuses it, and a new one goes to the half the previous
+// unit does not read.  Fields, unit e of the chunk at bits 2e (i, jj) or e:
+// query sub-block, key sub-block, tile half, staged here, first unit of its row.
+// kSub = 2: (0,0) (1,0) (1,1); halves 0 0 1, staged 1 0 1: two k/v stagings per
+// chunk.  kSub = 4: (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,2) (3,1) (3,0) (3,3);
+// halves 0 0 1 0 1 0 0 1 0 1, staged 1 0 1 0 0 1 0 0 1 1: five per chunk.  Every
+// chunk's schedule ends in half 1 and starts in half 0, and each row ends with its
+// diagonal unit.
+template <int kSub>
+struct WideSchedule;
+template <>
+struct WideSchedule<2> {
+  static constexpr uint32_t kI = 0x14, kJ = 0x10, kHalfBuf = 0x4, kStage = 0x5, kFirst = 0x3;
+};
+template <>
+struct WideSchedule<4> {
+  static constexpr uint32_t kI = 0xffa94, kJ = 0xc6910, kHalfBuf = 0x294, kStage = 0x325, kFirst = 0x4b;
+};
+
+// Units of a segment of n tokens (the last chunk's rows stop at its sub-blocks).
+template <int kSub>
+__device__ __forceinline__ int wide_units(int n) {
+  if (n <= 0) return 0;
+  constexpr int kU = kSub * (kSub + 1) / 2;
+  const int nchunk = (n + kSub * kC - 1) / (kSub * kC);
+  const int last = (n - (nchunk - 1) * kSub * kC + kC - 1) / kC;  // sub-blocks of the last chunk
+  return (nchunk - 1) * kU + last * (last + 1) / 2;
+}
+
+// Unit u of a segment: its sub-blocks' first tokens and its schedule fields.
+template <int kSub>
+struct WideUnit {
+  int i, jj, ti, tj, buf;
+  bool stage, first, chunk_start;
+  __device__ __forceinline__ WideUnit(const Tile& tl, int u) {
+    using Sch = WideSchedule<kSub>;
+    constexpr int kU = kSub * (kSub + 1) / 2;
+    const int c = u / kU, e = u - c * kU;
+    i = (Sch::kI >> (2 * e)) & 3;
+    jj = (Sch::kJ >> (2 * e)) & 3;
+    buf = (Sch::kHalfBuf >> e) & 1;
+    stage = (Sch::kStage >> e) & 1;
+    first = (Sch::kFirst >> e) & 1;
+    chunk_start = e == 0;
+    const int t0 = tl.t_begin + c * kSub * kC;
+    ti = t0 + i * kC;
+    tj = t0 + jj * kC;
+  }
+};
 
 template <bool kWeights, int kSub>
-__global__ __launch_bounds__(kWideThreads, 2) void la_chunk_output_wide_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sK[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int n16 = lane & 15, g4 = lane >> 4;
-  const int j = tid & 15, rg = tid >> 4;
-  const Tile tl = decode_tile(p);
+__device__ __forceinline__ void wide_produce(const PrefillParams& p, const Tile& tl, int nunit,
+                                             uint8_t (*sQ)[kTileBytes], uint8_t (*sK)[kTileBytes],
+                                             uint8_t (*sV)[kTileBytes], uint8_t (*sG)[kTileBytes], uint8_t* sQl,
+                                             uint8_t* sKl) {
+  __builtin_amdgcn_s_setprio(1);
+  const int ptid = threadIdx.x - kWideConsumers;
+  const int j = ptid & 15, rg = ptid >> 4;
   const int64_t rs = (int64_t)p.H * kD;
-
   float wq[8], wk[8];
   load_norm_weights(p.qw, j, wq);
   load_norm_weights(p.kw, j, wk);
   Rope L;
-  rope_init<32>(p, tid, rg, j, L);
+  rope_init<16>(p, ptid, rg, j, L);
   double rev[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) rev[e] = p.freqs.rev[4 * j + e];
-  // rotations of row rg of a sub-block starting at token t
-  auto first_rows = [&](int t, float2 (&E)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t, rev[e]), L.A[e]);
+  struct Set {
+    Rows<4> q, k, v, g;
   };
-
-  // prefix state of this segment: S[:, 16 w .. 16 w + 16) (direct: S_in, or zero)
-  const bool direct = is_direct(p);
-  const int64_t bh = (int64_t)tl.b * p.H + tl.h;
-  f32x4 Sacc[8];
-  {
-    const float* src = direct ? (p.S_in ? p.S_in + bh * kD * kD : nullptr) : tl.state;
+  Set X, Y;
+  auto load_unit = [&](int u, Set& R) {
+    const WideUnit<kSub> U(tl, u);
+    if (U.stage) {
+      load_rows<4, 16>(p.k + tl.base + (int64_t)U.tj * rs, rs, min(kC, tl.t_end - U.tj), rg, j, R.k);
+      load_rows<4, 16>(p.v + tl.base + (int64_t)U.tj * rs, rs, min(kC, tl.t_end - U.tj), rg, j, R.v);
+    }
+    if (U.first) {
+      load_rows<4, 16>(p.q + tl.base + (int64_t)U.ti * rs, rs, min(kC, tl.t_end - U.ti), rg, j, R.q);
+      load_rows<4, 16>(p.g + tl.base + (int64_t)U.ti * rs, rs, min(kC, tl.t_end - U.ti), rg, j, R.g);
+    }
+  };
+  auto stage = [&](int u, const Set& R) {
+    const WideUnit<kSub> U(tl, u);
+    const bool exact = tl.seg == 0 && u == 0;  // the hi/lo rows: a call's first unit
+    float2 E[4];
+    if (U.stage) {
 #pragma unroll
-    for (int rtk = 0; rtk < 8; ++rtk)
+      for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + U.tj, rev[e]), L.A[e]);
+      norm_rope_rows<kWeights, 4, 16>(R.k, wk, p.eps, E, L, rg, j, sK[U.buf], exact ? sKl : nullptr);
+      store_rows_masked<4, 16>(sV[U.buf], R.v, min(kC, tl.t_end - U.tj), rg, j);
+    }
+    if (U.first) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Sacc[rtk][r] = src ? src[state_elem(rtk, r, w, g4, n16)] : 0.0f;
+      for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + U.ti, rev[e]), L.A[e]);
+      norm_rope_rows<kWeights, 4, 16>(R.q, wq, p.eps, E, L, rg, j, sQ[U.i & 1], exact ? sQl : nullptr);
+      sigmoid_stage<4, 16>(sG[U.i & 1], R.g, rg, j);
+    }
+  };
+  // one step while the consumers work on unit u: stage unit u + 1 from R, then reuse
+  // R for unit u + 3 (unit u + 2 is in flight in the other register set)
+  auto step = [&](int u, Set& R) {
+    if (u + 1 < nunit) {
+      stage(u + 1, R);
+      if (u + 3 < nunit) load_unit(u + 3, R);
+    }
+    __syncthreads();
+    __syncthreads();
+  };
+  if (nunit > 0) load_unit(0, Y);
+  __syncthreads();
+  if (nunit > 0) stage(0, Y);
+  if (nunit > 1) load_unit(1, X);
+  if (nunit > 2) load_unit(2, Y);
+  __syncthreads();
+  for (int u = 0; u < nunit; u += 2) {
+    step(u, X);
+    if (u + 1 < nunit) step(u + 1, Y);
   }
-  // this lane's output (and gate) columns 16 w + 4 g .. + 3 of (b, h)
-  const int64_t col_off = tl.base + 16 * w + 4 * g4;
+}
 
-  for (int t0 = tl.t_begin; t0 < tl.t_end; t0 += kSub * kC) {
-    f32x4 Dacc[8];
+template <int kSub>
+__device__ __forceinline__ void wide_consume(const PrefillParams& p, const Tile& tl, int nunit,
+                                             uint8_t (*sQ)[kTileBytes], uint8_t (*sK)[kTileBytes],
+                                             uint8_t (*sV)[kTileBytes], uint8_t (*sG)[kTileBytes],
+                                             const uint8_t* sQl, const uint8_t* sKl, uint8_t* sP) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n16 = lane & 15, g4 = lane >> 4;
+  const int64_t rs = (int64_t)p.H * kD;
+
+  // prefix state of this segment: S[:, 32w + 16 dt .. + 16) in accumulator tiles
+  // (direct: S_in, or zero)
+  const bool direct = is_direct(p);
+  f32x4 Sacc[2][8];
+  {
+    const float* src =
+        direct ? (p.S_in ? p.S_in + ((int64_t)tl.b * p.H + tl.h) * kD * kD : nullptr) : tl.state;
 #pragma unroll
-    for (int a = 0; a < 8; ++a) Dacc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < kSub; ++i) {
-      const int ti = t0 + i * kC;
-      if (ti >= tl.t_end) break;
-      const int nvi = min(kC, tl.t_end - ti);
-      // scores of the first 16 rows of a call use the hi/lo split (see the C = 64 kernel)
-      const bool exact = tl.seg == 0 && t0 == tl.t_begin && i == 0;
-      // gate logits of the lane's rows ti + 16 rt + n16 (clamped to the sub-block's last valid row)
-      uint2 graw[4];
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        graw[rt] = ld_stream(p.g + col_off + (int64_t)(ti + min(16 * rt + n16, nvi - 1)) * rs);
-      f32x4 Oacc[4];
-      for (int jj = 0; jj <= i; ++jj) {
-        const int tj = t0 + jj * kC;
-        const int nvj = min(kC, tl.t_end - tj);
-        {
-          Rows<2> Kr, Vr;
-          load_rows<2, 32>(p.k + tl.base + (int64_t)tj * rs, rs, nvj, rg, j, Kr);
-          load_rows<2, 32>(p.v + tl.base + (int64_t)tj * rs, rs, nvj, rg, j, Vr);
-          if (jj == 0) {
-            Rows<2> Qr;
-            load_rows<2, 32>(p.q + tl.base + (int64_t)ti * rs, rs, nvi, rg, j, Qr);
-            float2 E[4];
-            first_rows(ti, E);
-            norm_rope_rows<kWeights, 2, 32>(Qr, wq, p.eps, E, L, rg, j, sQ, exact ? sQl : nullptr);
+      for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sacc[dt][rtk][r] = src ? src[state_elem(rtk, r, 2 * w + dt, g4, n16)] : 0.0f;
+  }
+  uint16_t* const obase = p.o + tl.base + (int64_t)n16 * rs + 32 * w + 4 * g4;
+  // score tiles above the diagonal that a diagonal unit reads stay zero (off-diagonal
+  // units overwrite them, and a diagonal unit zeroes them again)
+  for (int i = tid; i < kC * kScoreRowBytes / 16; i += kWideConsumers)
+    reinterpret_cast<uint4*>(sP)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  __syncthreads();
+
+  bf16x8 SA[2][4];  // chunk-start state S^T as A operand (bf16), key dims in order pi
+  f32x4 Oacc[2][4];
+  for (int u = 0; u < nunit; ++u) {
+    const WideUnit<kSub> U(tl, u);
+    const uint8_t* Q = sQ[U.i & 1];
+    const uint8_t* K = sK[U.buf];
+    const uint8_t* V = sV[U.buf];
+    const uint8_t* G = sG[U.i & 1];
+    const bool diag = U.jj == U.i;
+    const bool exact = tl.seg == 0 && u == 0;
+    if (U.chunk_start) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) SA[dt][kk] = pack8(Sacc[dt][2 * kk], Sacc[dt][2 * kk + 1]);
+    }
+    // ---- phase A: scores P = Qh_i Kh_jj^T (as P^T tiles: lane holds 4 consecutive
+    // keys of one query), causal at jj = i; the inter-chunk term at jj = 0
+    if (diag) {
+      for (int idx = w; idx < 10; idx += 4) {
+        const int rt = (kTileRT >> (2 * idx)) & 3, st = (kTileST >> (2 * idx)) & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks) {
+          const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
+          const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
+          const bf16x8 kf = as_bf16x8(lds_ld<uint4>(K, ka));
+          const bf16x8 qf = as_bf16x8(lds_ld<uint4>(Q, qa));
+          if (exact && idx == 0) {
+            acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qf, acc);
+            acc = mma(kf, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
           }
-          float2 E[4];
-          first_rows(tj, E);
-          norm_rope_rows<kWeights, 2, 32>(Kr, wk, p.eps, E, L, rg, j, sK, exact && jj == 0 ? sKl : nullptr);
-          store_rows_masked<2, 32>(sV, Vr, nvj, rg, j);
+          acc = mma(kf, qf, acc);
         }
-        __syncthreads();
-        if (jj == 0) {
-          // inter-chunk term O^T = S^T Qh^T (key dims in order pi)
-          bf16x8 SA[4];
+        if (st == rt) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) SA[kk] = pack8(Sacc[2 * kk], Sacc[2 * kk + 1]);
-#pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            Oacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) Oacc[rt] = mma(SA[kk], pi_operand(sQ, 16 * rt + n16, kk, g4), Oacc[rt]);
-          }
+          for (int r = 0; r < 4; ++r)
+            if (4 * g4 + r > n16) acc[r] = 0.f;
         }
-        // scores of query sub-block i against key sub-block jj, two 16x16 tiles per wave
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int idx = w + 8 * u;
-          const int rt = idx >> 2, st = idx & 3;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < kD / 32; ++ks) {
-            const int ka = tile_off(16 * st + n16, 32 * ks + 8 * g4);
-            const int qa = tile_off(16 * rt + n16, 32 * ks + 8 * g4);
-            const bf16x8 kf = as_bf16x8(lds_ld<uint4>(sK, ka));
-            const bf16x8 qf = as_bf16x8(lds_ld<uint4>(sQ, qa));
-            if (exact && idx == 0) {
-              acc = mma(as_bf16x8(lds_ld<uint4>(sKl, ka)), qf, acc);
-              acc = mma(kf, as_bf16x8(lds_ld<uint4>(sQl, qa)), acc);
-            }
-            acc = mma(kf, qf, acc);
-          }
-          if (jj == i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (st > rt || (st == rt && 4 * g4 + r > n16)) acc[r] = 0.f;
-          }
-          lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
-                        make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
-        }
-        bf16x8 Vf[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) Vf[kk] = v_operand(sV, kk, 16 * w, g4, n16);
-        if (jj == i) accumulate_state(Dacc, sK, Vf, g4, n16);
-        __syncthreads();
-        // O^T += V^T P^T
-#pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const int t = 16 * rt + n16;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const bf16x8 pb = as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
-                                        lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
-            Oacc[rt] = mma(Vf[kk], pb, Oacc[rt]);
-          }
-        }
-        __syncthreads();
+        lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
+                      make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
       }
-      // gate and store: lane holds o[ti + 16 rt + n16][16 w + 4 g .. + 3]
+      if (U.i > 0 && w < 2) {
+        // the two tiles above the diagonal that the products below read: (0, 1), (2, 3)
+        const int rt = 2 * w, st = rt + 1;
+        lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4), make_uint2(0u, 0u));
+      }
+    } else {
+      for (int idx = w; idx < 16; idx += 4) {
+        const int rt = idx >> 2, st = idx & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kD / 32; ++ks) {
+          const bf16x8 kf = as_bf16x8(lds_ld<uint4>(K, tile_off(16 * st + n16, 32 * ks + 8 * g4)));
+          const bf16x8 qf = as_bf16x8(lds_ld<uint4>(Q, tile_off(16 * rt + n16, 32 * ks + 8 * g4)));
+          acc = mma(kf, qf, acc);
+        }
+        lds_st<uint2>(sP, score_off(16 * rt + n16, 16 * st + 4 * g4),
+                      make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3])));
+      }
+    }
+    if (U.first) {
+      // O^T = S_start^T Qh_i^T for all 64 queries
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        if (16 * rt + n16 < nvi) {
-          const uint2 gr = graw[rt];
-          const uint2 out = make_uint2(pack2(Oacc[rt][0] * sigmoidf_(bf2f_lo(gr.x)), Oacc[rt][1] * sigmoidf_(bf2f_hi(gr.x))),
-                                       pack2(Oacc[rt][2] * sigmoidf_(bf2f_lo(gr.y)), Oacc[rt][3] * sigmoidf_(bf2f_hi(gr.y))));
-          *reinterpret_cast<uint2*>(p.o + col_off + (int64_t)(ti + 16 * rt + n16) * rs) = out;
+        bf16x8 Qf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Qf[kk] = pi_operand(Q, 16 * rt + n16, kk, g4);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          Oacc[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) Oacc[dt][rt] = mma(SA[dt][kk], Qf[kk], Oacc[dt][rt]);
         }
       }
     }
+    __syncthreads();
+    // ---- phase B: O^T += V_jj^T P^T (scores read in key order pi)
+    bf16x8 Vf[2][2];  // V^T (token order pi), columns 32w + 16 dt + n16
 #pragma unroll
-    for (int a = 0; a < 8; ++a) Sacc[a] += Dacc[a];
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) Vf[dt][kk] = v_operand(V, kk, 32 * w + 16 * dt, g4, n16);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int t = 16 * rt + n16;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        if (diag && kk > rt / 2) continue;
+        const bf16x8 pb = as_bf16x8(lds_ld<uint2>(sP, score_off(t, 32 * kk + 4 * g4)),
+                                    lds_ld<uint2>(sP, score_off(t, 32 * kk + 16 + 4 * g4)));
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) Oacc[dt][rt] = mma(Vf[dt][kk], pb, Oacc[dt][rt]);
+      }
+    }
+    if (diag) {
+      // gate and store sub-block i: lane holds o[ti + 16 rt + n16][32 w + 16 dt + 4 g .. + 3]
+      const int nv = min(kC, tl.t_end - U.ti);
+      uint16_t* const orow = obase + (int64_t)U.ti * rs;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int t = 16 * rt + n16;
+        uint16_t* dst = orow + (int64_t)(16 * rt) * rs;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const uint2 sg = lds_ld<uint2>(G, tile_off(t, 32 * w + 16 * dt + 4 * g4));
+          const uint2 out = make_uint2(pack2(Oacc[dt][rt][0] * bf2f_lo(sg.x), Oacc[dt][rt][1] * bf2f_hi(sg.x)),
+                                       pack2(Oacc[dt][rt][2] * bf2f_lo(sg.y), Oacc[dt][rt][3] * bf2f_hi(sg.y)));
+          if (t < nv) *reinterpret_cast<uint2*>(dst + 16 * dt) = out;
+        }
+      }
+      // S += Kh_i^T V_i
+#pragma unroll
+      for (int kk = 0; kk < kC / 32; ++kk) {
+        const int tr0 = 32 * kk + 4 * g4 + (n16 >> 2);
+#pragma unroll
+        for (int rtk = 0; rtk < 8; ++rtk) {
+          const int col = 16 * rtk + 4 * (n16 & 3);
+          const bf16x8 a = as_bf16x8(lds_tr(K, tile_off(tr0, col)), lds_tr(K, tile_off(tr0 + 16, col)));
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) Sacc[dt][rtk] = mma(a, Vf[dt][kk], Sacc[dt][rtk]);
+        }
+      }
+    }
+    __syncthreads();
   }
   if (direct) {
-    float* dst = p.S_out + bh * kD * kD;
+    // lane offsets formed afresh here, so that none stays live across the loop
+    int t2 = threadIdx.x;
+    asm volatile("" : "+v"(t2));
+    float* dst = p.S_out + ((int64_t)tl.b * p.H + tl.h) * kD * kD + (int64_t)(4 * ((t2 & 63) >> 4)) * kD +
+                 32 * (t2 >> 6) + (t2 & 15);
 #pragma unroll
-    for (int rtk = 0; rtk < 8; ++rtk)
+    for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[state_elem(rtk, r, w, g4, n16)] = Sacc[rtk][r];
+      for (int rtk = 0; rtk < 8; ++rtk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * rtk + r) * kD + 16 * dt] = Sacc[dt][rtk][r];
   }
+}
+
+template <bool kWeights, int kSub>
+__global__ __launch_bounds__(kWideThreads) void la_chunk_output_wide_kernel(PrefillParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sK[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sV[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sG[2][kTileBytes];  // sigmoid(gate), bf16
+  __shared__ __attribute__((aligned(16))) uint8_t sQl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sKl[kExactRows * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t sP[kC * kScoreRowBytes];
+
+  const Tile tl = decode_tile(p);
+  const int nunit = wide_units<kSub>(tl.t_end - tl.t_begin);
+  if (threadIdx.x >= kWideConsumers)
+    wide_produce<kWeights, kSub>(p, tl, nunit, sQ, sK, sV, sG, sQl, sKl);
+  else
+    wide_consume<kSub>(p, tl, nunit, sQ, sK, sV, sG, sQl, sKl, sP);
 }
 
 }  // namespace
