@@ -487,9 +487,9 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
   const int r0 = i * kSB, nv = min(kSB, p.T - r0);
   const uint32_t rsb = (uint32_t)rs * 2;  // bytes between rows (at most 64 rows are addressed from a block start)
 
-  // lane x < topk holds chosen block x (the chosen ones first, in increasing order)
+  // lane x < topk holds chosen block x (the chosen ones first, in increasing order);
+  // loaded first, so that the q and own-block loads below go out before its wait
   const int myblk = lane < p.topk ? sel[((int64_t)bh * nqb + i) * p.topk + lane] : -1;
-  const int nblk = 1 + __popcll(__ballot(myblk >= 0));
   auto block_row0 = [&](int n) -> int { return n == 0 ? r0 : kSB * __builtin_amdgcn_readlane(myblk, n - 1); };
   // rows of block n that exist: the own block may end at T, and then its missing rows
   // repeat its last row (finite values that the causal mask and the unstored query
@@ -556,6 +556,10 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
     for (int u = 0; u < 16; ++u) lds_st<uint4>(sV, (4 * u + g4) * kRowBytes + 16 * n16, Vr[u]);
   };
 
+  load_v(0);  // the own block of the first pass: its rows do not depend on the choice
+  load_k(0);
+  const int nblk = 1 + __popcll(__ballot(myblk >= 0));
+
   f32x4 O[8][4];  // O^T[16 dt + 4 g4 + r][query 16 qt + n16]
   float m_ref[4], l_run[4];
 #pragma unroll
@@ -571,8 +575,10 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) O[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    load_v(0);  // V before K, as in the loop: the waits stay partial across the back edge
-    load_k(0);
+    if (pass > 0) {
+      load_v(0);  // V before K, as in the loop: the waits stay partial across the back edge
+      load_k(0);
+    }
     for (int n = 0; n < nblk; ++n) {
       store_v();
       if (n + 1 < nblk) load_v(n + 1);
@@ -658,7 +664,17 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
       }
     }
   }
-  // normalize, gate, store 4 consecutive values of a query row per lane
+  // normalize, gate, store 4 consecutive values of a query row per lane.  Every gate
+  // value is loaded before the first store: o may alias g as far as the compiler
+  // knows, so a load placed after a store waits for it, and the 32 loads interleaved
+  // with the stores cost one memory round trip each (about a fifth of the kernel).
+  uint2 gg[4][8];
+#pragma unroll
+  for (int qt = 0; qt < 4; ++qt) {
+    const int64_t grow = base + (int64_t)(r0 + min(16 * qt + n16, nv - 1)) * rs;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) gg[qt][dt] = *reinterpret_cast<const uint2*>(p.g + grow + 16 * dt + 4 * g4);
+  }
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
     float lt = l_run[qt] + __shfl_xor(l_run[qt], 16);
@@ -670,11 +686,11 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int d = 16 * dt + 4 * g4;
-        const uint2 gg = *reinterpret_cast<const uint2*>(p.g + orow + d);
-        const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(gg.x));
-        const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(gg.x));
-        const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(gg.y));
-        const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(gg.y));
+        const uint2 g2 = gg[qt][dt];
+        const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(g2.x));
+        const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(g2.x));
+        const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(g2.y));
+        const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(g2.y));
         *reinterpret_cast<uint2*>(p.o + orow + d) = make_uint2(pack2(o0, o1), pack2(o2, o3));
       }
     }
