@@ -19,10 +19,10 @@
 //
 // Two kernels share that tiling:
 //   * la_linear_ring_kernel (K % 128 == 0, the projection shapes): K steps of
-//     32 through a four-slot LDS ring filled by direct global-to-LDS loads
-//     (16 bytes per lane, no register staging and no LDS store instructions),
-//     three steps in flight; 64-byte rows with an XOR swizzle of the 16-byte
-//     pieces keep the operand reads conflict-free.
+//     64 double-buffered in LDS, filled by direct global-to-LDS loads (16 bytes
+//     per lane, no register staging and no LDS store instructions, whole 128-byte
+//     lines per request); 128-byte rows with an XOR swizzle of the 16-byte pieces
+//     keep the operand reads conflict-free.
 //   * la_linear_kernel (any K % 64 == 0): K steps of 64 double-buffered in LDS
 //     through registers.
 // Both sum each output in the same order (32-deep MFMA steps in K order), so
@@ -137,16 +137,19 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_kernel(LinearParams p)
 }
 
 // ---------------------------------------------------------------------------
-// Ring kernel.  Stage kt (K columns [32 kt, 32 kt + 32)) of both operands sits in
-// slot kt % 4: a 256-row x 64-byte tile per operand, each row's four 16-byte
-// pieces stored at piece position c ^ ((row / 4) % 4).  A wave loads 16 rows per
-// direct load (lane i: row i / 4, position i % 4), so it fetches the global piece
-// that belongs there; the MFMA reads of 16 rows at one piece column then hit 16
-// different bank groups.
-constexpr int kRingBK = 32, kRingSlots = 4;
-constexpr int kRingTile = kBM * kRingBK * 2;  // 16 KiB per operand per stage
+// Ring kernel.  Stage kt (K columns [64 kt, 64 kt + 64)) of both operands sits in
+// slot kt % 2: a 256-row x 128-byte tile per operand, each row's eight 16-byte
+// pieces stored at piece position c ^ ((row / 2) % 8).  A wave loads 8 rows per
+// direct load (lane i: row i / 8, position i % 8), so it fetches the global piece
+// that belongs there, and every 8 lanes read one 128-byte row: each direct load
+// asks L2 for whole 128-byte lines.  (With 32-deep stages a row gave 64 bytes, and
+// the kernel sent twice the requests for the same bytes: 3.6-3.8 ms against
+// 3.5 ms for the q/k/v/gate projection of a 32K layer.)  The MFMA reads of 16 rows
+// at one piece column hit 16 different 16-byte bank groups.
+constexpr int kRingBK = 64, kRingSlots = 2;
+constexpr int kRingTile = kBM * kRingBK * 2;  // 32 KiB per operand per stage
 
-__device__ __forceinline__ int ring_pos(int row, int piece) { return piece ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int ring_pos(int row, int piece) { return piece ^ ((row >> 1) & 7); }
 
 // Direct global -> LDS load of 16 bytes per lane from base + off (lane i's bytes
 // land at LDS byte address lds + 16 i).  Issued from assembly so that the
@@ -166,9 +169,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* ptr) {
 }
 
 __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearParams p) {
-  // one LDS object per slot and operand
-  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kRingTile], sA1[kRingTile], sA2[kRingTile], sA3[kRingTile];
-  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kRingTile], sB1[kRingTile], sB2[kRingTile], sB3[kRingTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sA0[kRingTile], sA1[kRingTile];
+  __shared__ __attribute__((aligned(1024))) uint8_t sB0[kRingTile], sB1[kRingTile];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n16 = lane & 15, g4 = lane >> 4;
@@ -179,28 +181,27 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
   const int n0 = tn * kBN;
   const int K = p.K;
 
-  // this wave loads rows 32 w .. 32 w + 31 of both operand tiles, 16 per load
+  // this wave loads rows 32 w .. 32 w + 31 of both operand tiles, 8 per load
   const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(p.x + m0 * K);
   const uint8_t* const wbase = reinterpret_cast<const uint8_t*>(p.w + (int64_t)n0 * K);
-  uint32_t aoff[2], boff[2];
+  uint32_t aoff[4], boff[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = 32 * w + 16 * u + (lane >> 2);
-    const int piece = ring_pos(row, lane & 3);  // the position is its own inverse
+  for (int u = 0; u < 4; ++u) {
+    const int row = 32 * w + 8 * u + (lane >> 3);
+    const int piece = ring_pos(row, lane & 7);  // the position is its own inverse
     const int arow = m0 + row < p.M ? row : (int)(p.M - 1 - m0);  // rows past M re-read the last row
     aoff[u] = (uint32_t)(arow * K + 8 * piece) * 2u;
     boff[u] = (uint32_t)(row * K + 8 * piece) * 2u;
   }
-  const uint32_t la[4] = {lds_addr(sA0), lds_addr(sA1), lds_addr(sA2), lds_addr(sA3)};
-  const uint32_t lb[4] = {lds_addr(sB0), lds_addr(sB1), lds_addr(sB2), lds_addr(sB3)};
+  const uint32_t la[2] = {lds_addr(sA0), lds_addr(sA1)};
+  const uint32_t lb[2] = {lds_addr(sB0), lds_addr(sB1)};
   const int nk = K / kRingBK;
   auto issue = [&](int kt, int slot) {
-    kt = min(kt, nk - 1);  // past the end: reload the last stage into a slot nobody reads
     const uint8_t* xa = xbase + (int64_t)kt * kRingBK * 2;
     const uint8_t* wa = wbase + (int64_t)kt * kRingBK * 2;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t rows = __builtin_amdgcn_readfirstlane((32 * w + 16 * u) * 64);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t rows = __builtin_amdgcn_readfirstlane((32 * w + 8 * u) * 128);
       dma16(xa, aoff[u], la[slot] + rows);
       dma16(wa, boff[u], lb[slot] + rows);
     }
@@ -211,47 +212,43 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two 32-deep MFMA steps per stage, in K order
   auto compute = [&](const uint8_t* A, const uint8_t* B) {
-    bf16x8 xa[4], wb[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 64 * wm + 16 * i + n16;
-      xa[i] = as_bf16x8(lds_ld<uint4>(A, row * 64 + 16 * ring_pos(row, g4)));
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 xa[4], wb[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 64 * wm + 16 * i + n16;
+        xa[i] = as_bf16x8(lds_ld<uint4>(A, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int row = 128 * wn + 16 * j + n16;
+        wb[j] = as_bf16x8(lds_ld<uint4>(B, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[j], xa[i], acc[i][j]);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 128 * wn + 16 * j + n16;
-      wb[j] = as_bf16x8(lds_ld<uint4>(B, row * 64 + 16 * ring_pos(row, g4)));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[j], xa[i], acc[i][j]);
   };
-  // stage kt's loads (this wave's) are done once at most the two later stages'
-  // 4 loads each are outstanding; the barrier makes that hold for every wave,
-  // and also that every wave has finished reading the slot reloaded next
+  // stage kt's loads (this wave's) are done once none is outstanding: the next
+  // stage's loads go out after the barrier; the barrier makes that hold for every
+  // wave, and also that every wave has finished reading the slot reloaded next
   auto sync_stage = [&]() {
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
   issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  for (int kt = 0; kt < nk; kt += 4) {  // nk % 4 == 0
+  for (int kt = 0; kt < nk; kt += 2) {  // nk % 2 == 0
     sync_stage();
-    issue(kt + 3, 3);
+    if (kt + 1 < nk) issue(kt + 1, 1);
     compute(sA0, sB0);
     sync_stage();
-    issue(kt + 4, 0);
+    if (kt + 2 < nk) issue(kt + 2, 0);
     compute(sA1, sB1);
-    sync_stage();
-    issue(kt + 5, 1);
-    compute(sA2, sB2);
-    sync_stage();
-    issue(kt + 6, 2);
-    compute(sA3, sB3);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the workgroup ends
 
