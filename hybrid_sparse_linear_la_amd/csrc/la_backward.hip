@@ -150,16 +150,13 @@ __device__ __forceinline__ void store_row_pieces(uint16_t* dst, int j, const flo
 
 // The prologue backward of one chunk inside the chunk kernel: thread (rg, j) takes
 // rows rg and rg + 32 (E: row rg's rotations); dqh, dkh come from LDS row tiles
-// (the snapshot area's rows), q, k again from memory (L2, since the chunk's staging).
+// (the snapshot area's rows), the raw q, k rows X from memory (loaded by the caller).
 // dw receives the thread's norm-weight gradient terms (its two rows summed).
 template <bool kWeights>
 __device__ __forceinline__ void prologue_back_rows(const PrefillParams& p, const BackwardParams& bp, int64_t base,
                                                    int nv, int64_t rs, int rg, int j, const Rope& L, float2 (&E)[4],
                                                    const uint8_t* sDq, const uint8_t* sDk, const uint8_t* sQ,
-                                                   float (&dw)[2][8]) {
-  Rows<2> X[2];
-  load_rows_cached<2, 32>(p.q + base, rs, nv, rg, j, X[0]);
-  load_rows_cached<2, 32>(p.k + base, rs, nv, rg, j, X[1]);
+                                                   const Rows<2> (&X)[2], float (&dw)[2][8]) {
   float w[2][8];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -445,6 +442,13 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
         store_rows4(bp.dqh, acc, tl.base, t0, rs, col, nv, n16);
       }
     }
+    // the prologue backward's raw q, k rows (L2 hits: the staging loaded them), issued
+    // here so that their latency passes under the two barriers and the tile stores
+    Rows<2> PX[2];
+    if (kFuse) {
+      load_rows_cached<2, 32>(p.q + tl.base + (int64_t)t0 * rs, rs, nv, rg, j, PX[0]);
+      load_rows_cached<2, 32>(p.k + tl.base + (int64_t)t0 * rs, rs, nv, rg, j, PX[1]);
+    }
     __syncthreads();
     if (kFuse) {
       // dqh, dkh of this chunk through LDS (the snapshot area is free now) into the
@@ -460,7 +464,8 @@ __global__ __launch_bounds__(kBwdThreads) void la_backward_chunk_kernel(Backward
 #pragma unroll
       for (int e = 0; e < 4; ++e) E[e] = cmul(rope_rotation(tl.pos_base + t0, rev[e]), L.A[e]);
       float dw[2][8];
-      prologue_back_rows<kWeights>(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, sQ, dw);
+      prologue_back_rows<kWeights>(p, bp, tl.base + (int64_t)t0 * rs, nv, rs, rg, j, L, E, sX, sX + kSnapBytes, sQ, PX,
+                                   dw);
       if (wgrad) {
         // the wave's four row groups (lanes 16 apart) summed, then the 8 waves' parts in
         // the unused middle of the area, summed in a fixed order into dw_acc
