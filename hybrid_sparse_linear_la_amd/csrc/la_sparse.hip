@@ -664,36 +664,45 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
       }
     }
   }
-  // normalize, gate, store 4 consecutive values of a query row per lane.  Every gate
-  // value is loaded before the first store: o may alias g as far as the compiler
-  // knows, so a load placed after a store waits for it, and the 32 loads interleaved
-  // with the stores cost one memory round trip each (about a fifth of the kernel).
-  uint2 gg[4][8];
+  // normalize, gate, store, with every global access in whole rows: the gate rows
+  // come in 16 bytes per lane (4 rows of 256 bytes per load) into the V tile, free
+  // after the last products; each lane reads back its accumulator positions, writes
+  // the bf16 outputs over them, and the rows go out 16 bytes per lane.  Accesses in
+  // the accumulator layout (16 rows x 8 bytes per instruction) ran 4 times the L2
+  // transactions, about a fifth of the kernel at this size; all gate loads also come
+  // before the first store (o may alias g as far as the compiler knows, and a load
+  // placed after a store waits for it).
+  const int lr = lane >> 4, lc = 8 * (lane & 15);  // rows 4 m + lr, dims lc .. lc + 7
+  uint4 grow[16];
 #pragma unroll
-  for (int qt = 0; qt < 4; ++qt) {
-    const int64_t grow = base + (int64_t)(r0 + min(16 * qt + n16, nv - 1)) * rs;
+  for (int m = 0; m < 16; ++m)
+    grow[m] = *reinterpret_cast<const uint4*>(p.g + base + (int64_t)(r0 + min(4 * m + lr, nv - 1)) * rs + lc);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) gg[qt][dt] = *reinterpret_cast<const uint2*>(p.g + grow + 16 * dt + 4 * g4);
-  }
+  for (int m = 0; m < 16; ++m) lds_st<uint4>(sV, tile_off(4 * m + lr, lc), grow[m]);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the gate tile written
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
     float lt = l_run[qt] + __shfl_xor(l_run[qt], 16);
     lt += __shfl_xor(lt, 32);
     const float inv = 1.0f / lt;
     const int qr = 16 * qt + n16;
-    if (qr < nv) {
-      const int64_t orow = base + (int64_t)(r0 + qr) * rs;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const int d = 16 * dt + 4 * g4;
-        const uint2 g2 = gg[qt][dt];
-        const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(g2.x));
-        const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(g2.x));
-        const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(g2.y));
-        const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(g2.y));
-        *reinterpret_cast<uint2*>(p.o + orow + d) = make_uint2(pack2(o0, o1), pack2(o2, o3));
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      const int off = tile_off(qr, 16 * dt + 4 * g4);
+      const uint2 g2 = lds_ld<uint2>(sV, off);
+      const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(g2.x));
+      const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(g2.x));
+      const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(g2.y));
+      const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(g2.y));
+      lds_st<uint2>(sV, off, make_uint2(pack2(o0, o1), pack2(o2, o3)));
     }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the output tile written
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int row = 4 * m + lr;
+    const uint4 ov = lds_ld<uint4>(sV, tile_off(row, lc));
+    if (row < nv) *reinterpret_cast<uint4*>(p.o + base + (int64_t)(r0 + row) * rs + lc) = ov;
   }
 }
 
