@@ -246,7 +246,7 @@ def bench_decode(la, torch, workloads, hip, args):
                      "unit": "GB/s", "frac": round(bytes_step / (best * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": bytes_step,
                      "note": ("the 128 MiB of states can stay in the 256 MB memory-side cache between steps, so this "
-                              "rate may be cache-assisted at any value; the b256 entry (512 MiB) is DRAM-bound")},
+                              "rate may be cache-assisted at any value; the b384 entry (768 MiB) is DRAM-bound")},
     }
 
 
@@ -581,28 +581,33 @@ def _decode_steps_us(la, torch, hip, S0, q, k, v, g, pos):
 
 def bench_decode_more(la, torch, workloads, hip, steps=200):
     """Decode step time at three positions (a step's cost must not depend on it),
-    and at 256 sequences, whose 512 MiB of states exceed the 256 MB memory-side
-    cache, so every step streams its state from DRAM."""
+    and at batches whose states exceed the 256 MB memory-side cache: 256 sequences
+    (512 MiB; written back with non-temporal stores, which still leaves part of the
+    working set to that cache) and 384 (768 MiB: every step streams its states from
+    and to DRAM, at the same rate with either store kind)."""
     w = workloads.DECODE_B64
     S0, q, k, v, g = workloads.decode_inputs(w, steps=steps, device="cuda")
     pos = {str(p): round(_decode_steps_us(la, torch, hip, S0, q, k, v, g, p), 3) for p in (0, 262144, 1048575)}
     vals = list(pos.values())
     del S0, q, k, v, g
-    w2 = workloads.DECODE_B256
-    S0, q, k, v, g = workloads.decode_inputs(w2, steps=w2.steps, device="cuda")
-    us = _decode_steps_us(la, torch, hip, S0, q, k, v, g, w2.pos0)
-    bytes_step = 2 * w2.B * w2.H * STATE_BYTES + 5 * w2.B * w2.H * w2.D * 2
-    gbs = bytes_step / (us * 1e-6) / 1e9
-    del S0, q, k, v, g
-    return {
-        "us_per_step_by_position": pos, "position_max_over_min": round(max(vals) / min(vals), 4),
-        "b256": {"workload": w2.name, "steps": w2.steps, "us_per_step": round(us, 3), "bytes_per_step": bytes_step,
-                 "state_bytes": w2.B * w2.H * STATE_BYTES,
-                 "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": round(gbs, 1),
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                              "note": "the 512 MiB of states exceed the 256 MB memory-side cache: "
-                                      "each step reads and writes them in DRAM"}},
-    }
+    out = {"us_per_step_by_position": pos, "position_max_over_min": round(max(vals) / min(vals), 4)}
+    notes = {"b256": "the 512 MiB of states exceed the 256 MB memory-side cache; written back with non-temporal "
+                     "stores, part of them is still served by that cache (compare b384)",
+             "b384": "the 768 MiB of states exceed the 256 MB memory-side cache: each step reads and writes them "
+                     "in DRAM (plain and non-temporal stores measured the same)"}
+    for key, w2 in (("b256", workloads.DECODE_B256), ("b384", workloads.DECODE_B384)):
+        S0, q, k, v, g = workloads.decode_inputs(w2, steps=w2.steps, device="cuda")
+        us = _decode_steps_us(la, torch, hip, S0, q, k, v, g, w2.pos0)
+        bytes_step = 2 * w2.B * w2.H * STATE_BYTES + 5 * w2.B * w2.H * w2.D * 2
+        gbs = bytes_step / (us * 1e-6) / 1e9
+        del S0, q, k, v, g
+        torch.cuda.empty_cache()
+        out[key] = {"workload": w2.name, "steps": w2.steps, "us_per_step": round(us, 3), "bytes_per_step": bytes_step,
+                    "state_bytes": w2.B * w2.H * STATE_BYTES,
+                    "roofline": {"bound": "hbm", "kernel": "la_decode_kernel", "achieved": round(gbs, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                 "note": notes[key]}}
+    return out
 
 
 def _sclk_files():
@@ -656,7 +661,7 @@ def environment(torch, workloads, busy_fn):
             top = t if top is None else max(top, t or 0)
         time.sleep(0.005)
     torch.cuda.synchronize()
-    seeds = {w.name: w.seed for w in (*workloads.ALL, workloads.PREFILL_B8_32K, workloads.DECODE_B256,
+    seeds = {w.name: w.seed for w in (*workloads.ALL, workloads.PREFILL_B8_32K, workloads.DECODE_B256, workloads.DECODE_B384,
                                       workloads.SERVING_MIX, workloads.LAYER_32K, workloads.SPARSE_32K,
                                       workloads.SPARSE_DECODE)}
     return {"gpu": torch.cuda.get_device_name(0), "torch": torch.__version__, "hip": torch.version.hip,

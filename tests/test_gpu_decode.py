@@ -44,6 +44,33 @@ def test_decode_matches_oracle(la, B, H, steps, pos, S_std, weights):
         assert_S_close(to_np(S), S_ref, what=f"S step {n}")
 
 
+def test_decode_batch_beyond_the_cache(la):
+    """A batch whose states exceed 192 MiB (100 x 32 heads: 200 MiB) is written back
+    with non-temporal stores: the same step split into two halves (100 MiB each,
+    plain stores) gives bit-identical o and S, and sampled sequences match the
+    oracle."""
+    B, H, steps, pos = 100, 32, 2, 262144
+    gen = workloads.generator(4242, "cuda")
+    S = workloads.state(B, H, D, 0.02, gen, "cuda")
+    q, k, v, g = workloads.activations(steps, B, H, D, 0, "cuda", gen=gen)
+    S_half = S.clone()
+    picks = (0, 37, 99)
+    S_ref = {b: to_np(S[b:b + 1]) for b in picks}
+    for n in range(steps):
+        o = la.decode_step(q[n], k[n], v[n], g[n], S, pos + n)
+        halves = [la.decode_step(q[n][h0:h0 + 50].contiguous(), k[n][h0:h0 + 50].contiguous(),
+                                 v[n][h0:h0 + 50].contiguous(), g[n][h0:h0 + 50].contiguous(),
+                                 S_half[h0:h0 + 50], pos + n) for h0 in (0, 50)]
+        torch.cuda.synchronize()
+        assert torch.equal(o, torch.cat(halves)), f"o step {n}"
+        assert torch.equal(S, S_half), f"S step {n}"
+        for b in picks:
+            o_ref, S_ref[b] = oracle.decode_step(to_np32(q[n][b:b + 1]), to_np32(k[n][b:b + 1]),
+                                                 to_np32(v[n][b:b + 1]), to_np32(g[n][b:b + 1]), S_ref[b], pos + n)
+            assert_o_close(to_np(o[b:b + 1]), o_ref, what=f"o step {n} sequence {b}")
+            assert_S_close(to_np(S[b:b + 1]), S_ref[b], what=f"S step {n} sequence {b}")
+
+
 def test_decode_steps_equal_prefill(la):
     B, H, N, pos0 = 2, 4, 24, 4000
     gen = workloads.generator(55, "cuda")

@@ -54,6 +54,9 @@ ALL = (TINY, PREFILL_32K, PREFILL_256K, STREAM_1M, DECODE_B64)
 PREFILL_B8_32K = Workload("prefill_b8_h32_d128_t32768", 8, 32768, 32, 128, seed=10)
 DECODE_B256 = Workload("decode_b256_h32_d128_pos262144", 256, 1, 32, 128, seed=11, pos0=262144,
                        steps=200, state_std=0.02)
+# 384 sequences: 768 MiB of states, three times that cache.
+DECODE_B384 = Workload("decode_b384_h32_d128_pos262144", 384, 1, 32, 128, seed=12, pos0=262144,
+                       steps=100, state_std=0.02)
 
 
 @dataclasses.dataclass(frozen=True)
