@@ -13,11 +13,14 @@
 // its carried state, so k and v are read once.  Otherwise three launches on the
 // caller's stream:
 //   1. la_chunk_state_kernel : one workgroup per (b, h, segment of cps chunks)
-//      sums Kh^T V over its segment (bf16 MFMA, fp32 accumulate) -> workspace.
+//      sums Kh^T V over its segment (bf16 MFMA, fp32 accumulate) -> workspace;
+//      the last segment of each sequence has no later segment to feed and is
+//      skipped.
 //   2. la_state_scan_kernel  : per state element, exclusive prefix over segments
-//      (plus S_in) in place, and the final state -> S_out.
+//      (plus S_in) in place.
 //   3. la_chunk_output_kernel: one workgroup per (b, h, segment) starts from its
-//      segment's prefix state and walks the chunks.  Eight producer waves apply
+//      segment's prefix state and walks the chunks; the last segment of each
+//      sequence writes its carried state to S_out.  Eight producer waves apply
 //      QK-RMSNorm + RoPE to q, k and the sigmoid to the gate of chunk c+1 (bf16) and
 //      stage the tiles into one half of a ping-pong LDS buffer (their global
 //      loads run two chunks further ahead), while four consumer waves run all
@@ -63,6 +66,9 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
   const int n16 = lane & 15, g4 = lane >> 4;
   const int j = tid & 15, rg = tid >> 4;
   const Tile tl = decode_tile(p);
+  // forward: the last segment's sum feeds no prefix (its output workgroup carries
+  // the state to S_out); the backward's gradient sums feed every segment
+  if (!kGrad && last_segment(p, tl)) return;
   const int64_t rs = (int64_t)p.H * kD;
   const uint16_t* const kin = kGrad ? p.q : p.k;
   const uint16_t* const vin = kGrad ? p.dout : p.v;
@@ -122,12 +128,13 @@ __global__ __launch_bounds__(kThreads) void la_chunk_state_kernel(PrefillParams 
 }
 
 // --------------------------------------------------------------------------
-// Exclusive prefix of the per-segment states, in place, seeded with S_in; the
-// inclusive total is the final state.  One thread per 4 consecutive elements.
-// A variable-length batch walks each sequence's own run of segments (none for an
-// empty sequence, whose final state is S_in) and skips single-token sequences.
-// kReverse (backward): the inclusive suffix seeded with dS_out (in S_in), so each
-// segment gets the state gradient at its first token; the total goes to S_out.
+// Exclusive prefix of the per-segment states, in place, seeded with S_in (the last
+// segment's sum is not formed: its output workgroup writes S_out).  One thread per
+// 4 consecutive elements.  A variable-length batch walks each sequence's own run
+// of segments and skips single-token sequences; an empty sequence has none, and
+// its final state S_in is written here.  kReverse (backward): the inclusive suffix
+// seeded with dS_out (in S_in), so each segment gets the state gradient at its
+// first token; the total goes to S_out.
 template <bool kReverse>
 __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
   constexpr int64_t per = kD * kD / 4;
@@ -147,6 +154,10 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
   float4 run = p.S_in ? reinterpret_cast<const float4*>(p.S_in)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int i = 0; i < nseg; ++i) {
     const int s = kReverse ? nseg - 1 - i : i;
+    if (!kReverse && i == nseg - 1) {
+      ws[s * stride] = run;
+      break;
+    }
     const float4 d = ws[s * stride];
     if (!kReverse) ws[s * stride] = run;
     run.x += d.x;
@@ -155,7 +166,7 @@ __global__ __launch_bounds__(256) void la_state_scan_kernel(PrefillParams p) {
     run.w += d.w;
     if (kReverse) ws[s * stride] = run;
   }
-  reinterpret_cast<float4*>(p.S_out)[idx] = run;
+  if (kReverse || nseg == 0) reinterpret_cast<float4*>(p.S_out)[idx] = run;
 }
 
 // --------------------------------------------------------------------------
@@ -376,7 +387,7 @@ __device__ __forceinline__ void consume(const PrefillParams& p, const Tile& tl, 
     consume_phase_b(K, V, G, sP, Sacc, Oacc, nv, obase + (int64_t)t0 * rs, rs, w, g4, n16);
     __syncthreads();
   }
-  if (direct) {
+  if (last_segment(p, tl)) {  // the sequence's final state (direct: its only segment)
     // lane offsets formed afresh here, so that none stays live across the loop
     int t2 = threadIdx.x;
     asm volatile("" : "+v"(t2));
@@ -710,7 +721,7 @@ __device__ __forceinline__ void wide_consume(const PrefillParams& p, const Tile&
     }
     __syncthreads();
   }
-  if (direct) {
+  if (last_segment(p, tl)) {  // the sequence's final state (direct: its only segment)
     // lane offsets formed afresh here, so that none stays live across the loop
     int t2 = threadIdx.x;
     asm volatile("" : "+v"(t2));

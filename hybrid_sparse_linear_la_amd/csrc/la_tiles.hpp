@@ -307,6 +307,13 @@ __device__ __forceinline__ Tile decode_tile(const PrefillParams& p) {
   return tl;
 }
 
+// Whether the tile is the last segment of its sequence: its output workgroup
+// carries the state to the sequence's end and writes S_out, so the state pass
+// has no sum to form for it.
+__device__ __forceinline__ bool last_segment(const PrefillParams& p, const Tile& tl) {
+  return p.segs != nullptr ? tl.seg == p.seqs[tl.b].nseg - 1 : tl.seg == p.nseg - 1;
+}
+
 // S accumulator tile rtk of wave w: lane (g, n16) element r is
 // S[16 rtk + 4 g + r][16 w + n16].
 __device__ __forceinline__ int64_t state_elem(int rtk, int r, int w, int g4, int n16) {
