@@ -133,9 +133,13 @@ def bench_prefill(la, torch, workloads, hip, args):
     tokens = B * T
     step_s = wall / args.steps
     comp_bytes = TOKEN_HEAD_BYTES * B * T * H
-    out_bytes = comp_bytes + STATE_BYTES * B * H * plan_nseg        # output kernel: + prefix states
-    state_bytes = 512 * B * T * H + STATE_BYTES * B * H * plan_nseg  # state kernel: k, v -> per-segment states
-    scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg + STATE_BYTES * B * H
+    # the state pass sums every segment but a sequence's last (whose output workgroup
+    # writes S_out from its carried state); segments are whole 64-token chunks
+    seg_tokens = -(-(-(-T // 64)) // plan_nseg) * 64
+    state_tokens = min(T, (plan_nseg - 1) * seg_tokens)
+    out_bytes = comp_bytes + STATE_BYTES * B * H * (plan_nseg + 1)  # output kernel: + prefix states, S_out
+    state_bytes = 512 * B * state_tokens * H + STATE_BYTES * B * H * (plan_nseg - 1)  # k, v -> segment sums
+    scan_bytes = 2 * STATE_BYTES * B * H * plan_nseg  # S_in and the sums in, the prefixes out
     flops = (4 * D * D + 2 * D * (chunk + 1)) * B * T * H
     out_s = per["chunk_output"] / 1e3
     traffic = measured_traffic(tokens) if chunk == la.DEFAULT_CHUNK else None
