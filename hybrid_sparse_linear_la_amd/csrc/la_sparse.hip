@@ -470,12 +470,32 @@ __global__ __launch_bounds__(64) void la_sparse_select_kernel(SparseParams p, in
 //   read feeds the four query tiles.
 // The next block's K and V loads are in flight while the current block computes;
 // V goes through one LDS tile (the wave's LDS operations run in order).
+// Direct global -> LDS load of 16 bytes per lane from a per-lane address (lane i's
+// bytes land at LDS byte address lds + 16 i).  Issued from assembly: it writes no
+// register, and the kernel waits for it explicitly before reading the LDS it fills.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_lane(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The gate tile: 64 rows of 256 bytes, row r's 16-byte piece p at position
+// p ^ (r % 16), so that 16 rows' pieces at one column fall in 16 different bank
+// groups.
+constexpr int kGateRow = kD * 2;
+__device__ __forceinline__ int gate_off(int row, int byte) {
+  return row * kGateRow + 16 * ((byte >> 4) ^ (row & 15)) + (byte & 15);
+}
+
 constexpr float kRestart = 64.0f;  // base-2 units: P, l and O stay far inside the fp32 range
 constexpr float kRestartSum = 18446744073709551616.0f;  // 2^kRestart
 constexpr int kMaxPasses = 8;  // bounds the passes for non-finite logits
 
 __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, const int32_t* sel) {
   __shared__ __attribute__((aligned(16))) uint8_t sV[kVTile];
+  __shared__ __attribute__((aligned(256))) uint8_t sG[kSB * kGateRow];  // gate rows, then the output rows
   const int lane = threadIdx.x, n16 = lane & 15, g4 = lane >> 4;
   const int nqb = (p.T + kSB - 1) / kSB;
   const int item = xcd_item(nqb * p.H * p.B);
@@ -558,6 +578,19 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
 
   load_v(0);  // the own block of the first pass: its rows do not depend on the choice
   load_k(0);
+  // the gate rows go straight to LDS now, so the epilogue finds them there: load
+  // m brings rows 4 m .. 4 m + 3, lane i the row's piece at position i % 16
+  {
+    const int lr = lane >> 4, pos = lane & 15;
+    const uint32_t lds_g = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)sG);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const int row = 4 * m + lr;
+      const uint16_t* src = p.g + base + (int64_t)(r0 + min(row, nv - 1)) * rs + 8 * (pos ^ (row & 15));
+      dma16_lane(src, lds_g + 1024u * m);
+    }
+  }
   const int nblk = 1 + __popcll(__ballot(myblk >= 0));
 
   f32x4 O[8][4];  // O^T[16 dt + 4 g4 + r][query 16 qt + n16]
@@ -665,21 +698,13 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
     }
   }
   // normalize, gate, store, with every global access in whole rows: the gate rows
-  // come in 16 bytes per lane (4 rows of 256 bytes per load) into the V tile, free
-  // after the last products; each lane reads back its accumulator positions, writes
-  // the bf16 outputs over them, and the rows go out 16 bytes per lane.  Accesses in
-  // the accumulator layout (16 rows x 8 bytes per instruction) ran 4 times the L2
-  // transactions, about a fifth of the kernel at this size; all gate loads also come
-  // before the first store (o may alias g as far as the compiler knows, and a load
-  // placed after a store waits for it).
-  const int lr = lane >> 4, lc = 8 * (lane & 15);  // rows 4 m + lr, dims lc .. lc + 7
-  uint4 grow[16];
-#pragma unroll
-  for (int m = 0; m < 16; ++m)
-    grow[m] = *reinterpret_cast<const uint4*>(p.g + base + (int64_t)(r0 + min(4 * m + lr, nv - 1)) * rs + lc);
-#pragma unroll
-  for (int m = 0; m < 16; ++m) lds_st<uint4>(sV, tile_off(4 * m + lr, lc), grow[m]);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the gate tile written
+  // came into LDS 16 bytes per lane (4 rows of 256 bytes per load) at the start;
+  // each lane reads back its accumulator positions, writes the bf16 outputs over
+  // them, and the rows go out 16 bytes per lane.  Accesses in the accumulator
+  // layout (16 rows x 8 bytes per instruction) ran 4 times the L2 transactions,
+  // about a fifth of the kernel at this size.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the gate tile's loads landed
+  const int lr = lane >> 4, lc = 16 * (lane & 15);  // rows 4 m + lr, bytes lc .. lc + 15
 #pragma unroll
   for (int qt = 0; qt < 4; ++qt) {
     float lt = l_run[qt] + __shfl_xor(l_run[qt], 16);
@@ -688,21 +713,21 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
     const int qr = 16 * qt + n16;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      const int off = tile_off(qr, 16 * dt + 4 * g4);
-      const uint2 g2 = lds_ld<uint2>(sV, off);
+      const int off = gate_off(qr, 2 * (16 * dt + 4 * g4));
+      const uint2 g2 = lds_ld<uint2>(sG, off);
       const float o0 = O[dt][qt][0] * inv * sigmoidf_(bf2f_lo(g2.x));
       const float o1 = O[dt][qt][1] * inv * sigmoidf_(bf2f_hi(g2.x));
       const float o2 = O[dt][qt][2] * inv * sigmoidf_(bf2f_lo(g2.y));
       const float o3 = O[dt][qt][3] * inv * sigmoidf_(bf2f_hi(g2.y));
-      lds_st<uint2>(sV, off, make_uint2(pack2(o0, o1), pack2(o2, o3)));
+      lds_st<uint2>(sG, off, make_uint2(pack2(o0, o1), pack2(o2, o3)));
     }
   }
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the output tile written
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int row = 4 * m + lr;
-    const uint4 ov = lds_ld<uint4>(sV, tile_off(row, lc));
-    if (row < nv) *reinterpret_cast<uint4*>(p.o + base + (int64_t)(r0 + row) * rs + lc) = ov;
+    const uint4 ov = lds_ld<uint4>(sG, gate_off(row, lc));
+    if (row < nv) *reinterpret_cast<uint4*>(p.o + base + (int64_t)(r0 + row) * rs + lc / 2) = ov;
   }
 }
 
