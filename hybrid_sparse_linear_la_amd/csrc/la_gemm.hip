@@ -22,7 +22,9 @@
 //     64 double-buffered in LDS, filled by direct global-to-LDS loads (16 bytes
 //     per lane, no register staging and no LDS store instructions, whole 128-byte
 //     lines per request); 128-byte rows with an XOR swizzle of the 16-byte pieces
-//     keep the operand reads conflict-free.
+//     keep the operand reads conflict-free.  The two waves of each SIMD take turns
+//     between workgroup barriers: one issues a 32-deep step's MFMAs while the other
+//     reads the next step's operands from LDS.
 //   * la_linear_kernel (any K % 64 == 0): K steps of 64 double-buffered in LDS
 //     through registers.
 // Both sum each output in the same order (32-deep MFMA steps in K order), so
@@ -212,44 +214,73 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // two 32-deep MFMA steps per stage, in K order
-  auto compute = [&](const uint8_t* A, const uint8_t* B) {
+  // Ping-pong: the SIMD's two waves (group 0: waves 0-3, group 1: waves 4-7) run the
+  // same program, group 1 one workgroup barrier behind, so that in each turn between
+  // two barriers one group issues a k-step's MFMAs while the other reads the next
+  // k-step's operands from LDS.  k-step s is the 32-deep half s % 2 of stage s / 2.
+  const int group = __builtin_amdgcn_readfirstlane(w >> 2);
+  bf16x8 xa[2][4], wb[2][8];
+  auto read = [&](int buf, const uint8_t* A, const uint8_t* B, int ks) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 xa[4], wb[8];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 64 * wm + 16 * i + n16;
-        xa[i] = as_bf16x8(lds_ld<uint4>(A, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = 128 * wn + 16 * j + n16;
-        wb[j] = as_bf16x8(lds_ld<uint4>(B, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[j], xa[i], acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 64 * wm + 16 * i + n16;
+      xa[buf][i] = as_bf16x8(lds_ld<uint4>(A, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 128 * wn + 16 * j + n16;
+      wb[buf][j] = as_bf16x8(lds_ld<uint4>(B, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
+    }
+    // the reads of a stage's second half have returned before the turn ends: the
+    // slot is reloaded after the barrier that follows them
+    if (ks == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  // stage kt's loads (this wave's) are done once none is outstanding: the next
-  // stage's loads go out after the barrier; the barrier makes that hold for every
-  // wave, and also that every wave has finished reading the slot reloaded next
-  auto sync_stage = [&]() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the MFMA turn issues at raised priority (the SIMD's other wave is reading LDS)
+  auto mfma = [&](int buf) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mma(wb[buf][j], xa[buf][i], acc[i][j]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto bar = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
   };
+  // stages 0 and 1 in flight, stage 0 landed everywhere, k-step 0 read
   issue(0, 0);
-  for (int kt = 0; kt < nk; kt += 2) {  // nk % 2 == 0
-    sync_stage();
-    if (kt + 1 < nk) issue(kt + 1, 1);
-    compute(sA0, sB0);
-    sync_stage();
-    if (kt + 2 < nk) issue(kt + 2, 0);
-    compute(sA1, sB1);
+  issue(1, 1);  // nk >= 2
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 1's 8 loads may still be out
+  bar();
+  read(0, sA0, sB0, 0);
+  if (group == 1) bar();
+  // one stage per iteration: k-step 2u (operands in set 0) and 2u + 1 (set 1).  Stage
+  // u + 1 must have landed everywhere before the barrier that ends group 0's k-step
+  // 2u, which is group 1's middle barrier of that k-step: each group waits for its
+  // own loads before that barrier.
+  for (int u = 0; u < nk; ++u) {
+    const int slot = u & 1;
+    const uint8_t* const Ac = slot ? sA1 : sA0;
+    const uint8_t* const Bc = slot ? sB1 : sB0;
+    const uint8_t* const An = slot ? sA0 : sA1;
+    const uint8_t* const Bn = slot ? sB0 : sB1;
+    read(1, Ac, Bc, 1);
+    if (group == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bar();
+    mfma(0);
+    if (group == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    bar();
+    // both groups have read stage u for the last time: stage u + 2 may take its slot
+    if (u + 2 < nk) issue(u + 2, slot);
+    if (u + 1 < nk) read(0, An, Bn, 0);
+    bar();
+    mfma(1);
+    bar();
   }
+  if (group == 0) bar();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the workgroup ends
 
   const int split_cols = p.N / p.nsplit;
