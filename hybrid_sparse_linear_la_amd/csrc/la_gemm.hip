@@ -24,7 +24,9 @@
 //     lines per request); 128-byte rows with an XOR swizzle of the 16-byte pieces
 //     keep the operand reads conflict-free.  The two waves of each SIMD take turns
 //     between workgroup barriers: one issues a 32-deep step's MFMAs while the other
-//     reads the next step's operands from LDS.
+//     reads the next step's operands from LDS.  One workgroup per compute unit walks
+//     the tiles blockIdx.x, blockIdx.x + gridDim.x, ...; a tile's first two stages
+//     are loaded while the previous tile's outputs are stored.
 //   * la_linear_kernel (any K % 64 == 0): K steps of 64 double-buffered in LDS
 //     through registers.
 // Both sum each output in the same order (32-deep MFMA steps in K order), so
@@ -178,26 +180,30 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
   const int n16 = lane & 15, g4 = lane >> 4;
   const int wm = w & 3, wn = w >> 2;
   const int tiles_n = p.N / kBN;
-  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
-  const int64_t m0 = (int64_t)tm * kBM;
-  const int n0 = tn * kBN;
+  const int64_t ntiles = (p.M + kBM - 1) / kBM * (int64_t)tiles_n;
   const int K = p.K;
-
-  // this wave loads rows 32 w .. 32 w + 31 of both operand tiles, 8 per load
-  const uint8_t* const xbase = reinterpret_cast<const uint8_t*>(p.x + m0 * K);
-  const uint8_t* const wbase = reinterpret_cast<const uint8_t*>(p.w + (int64_t)n0 * K);
-  uint32_t aoff[4], boff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 32 * w + 8 * u + (lane >> 3);
-    const int piece = ring_pos(row, lane & 7);  // the position is its own inverse
-    const int arow = m0 + row < p.M ? row : (int)(p.M - 1 - m0);  // rows past M re-read the last row
-    aoff[u] = (uint32_t)(arow * K + 8 * piece) * 2u;
-    boff[u] = (uint32_t)(row * K + 8 * piece) * 2u;
-  }
+  const int nk = K / kRingBK;
   const uint32_t la[2] = {lds_addr(sA0), lds_addr(sA1)};
   const uint32_t lb[2] = {lds_addr(sB0), lds_addr(sB1)};
-  const int nk = K / kRingBK;
+
+  // per tile: this wave loads rows 32 w .. 32 w + 31 of both operand tiles, 8 per load
+  const uint8_t* xbase;
+  const uint8_t* wbase;
+  uint32_t aoff[4], boff[4];
+  auto setup = [&](int64_t t) {
+    const int tm = (int)(t / tiles_n), tn = (int)(t - (int64_t)tm * tiles_n);
+    const int64_t m0 = (int64_t)tm * kBM;
+    xbase = reinterpret_cast<const uint8_t*>(p.x + m0 * K);
+    wbase = reinterpret_cast<const uint8_t*>(p.w + (int64_t)tn * kBN * K);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 32 * w + 8 * u + (lane >> 3);
+      const int piece = ring_pos(row, lane & 7);  // the position is its own inverse
+      const int arow = m0 + row < p.M ? row : (int)(p.M - 1 - m0);  // rows past M re-read the last row
+      aoff[u] = (uint32_t)(arow * K + 8 * piece) * 2u;
+      boff[u] = (uint32_t)(row * K + 8 * piece) * 2u;
+    }
+  };
   auto issue = [&](int kt, int slot) {
     const uint8_t* xa = xbase + (int64_t)kt * kRingBK * 2;
     const uint8_t* wa = wbase + (int64_t)kt * kRingBK * 2;
@@ -209,16 +215,8 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
     }
   };
 
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Ping-pong: the SIMD's two waves (group 0: waves 0-3, group 1: waves 4-7) run the
-  // same program, group 1 one workgroup barrier behind, so that in each turn between
-  // two barriers one group issues a k-step's MFMAs while the other reads the next
-  // k-step's operands from LDS.  k-step s is the 32-deep half s % 2 of stage s / 2.
   const int group = __builtin_amdgcn_readfirstlane(w >> 2);
+  f32x4 acc[4][8];
   bf16x8 xa[2][4], wb[2][8];
   auto read = [&](int buf, const uint8_t* A, const uint8_t* B, int ks) {
 #pragma unroll
@@ -231,11 +229,8 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
       const int row = 128 * wn + 16 * j + n16;
       wb[buf][j] = as_bf16x8(lds_ld<uint4>(B, row * 128 + 16 * ring_pos(row, g4 + 4 * ks)));
     }
-    // the reads of a stage's second half have returned before the turn ends: the
-    // slot is reloaded after the barrier that follows them
     if (ks == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
-  // the MFMA turn issues at raised priority (the SIMD's other wave is reading LDS)
   auto mfma = [&](int buf) {
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -250,54 +245,70 @@ __global__ __launch_bounds__(kGemmThreads) void la_linear_ring_kernel(LinearPara
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
   };
-  // stages 0 and 1 in flight, stage 0 landed everywhere, k-step 0 read
+  // tiles blockIdx.x + k gridDim.x; with gridDim.x a multiple of 8, tile t stays on
+  // XCD t % 8, as with one workgroup per tile
+  int64_t t = blockIdx.x;
+  setup(t);
   issue(0, 0);
   issue(1, 1);  // nk >= 2
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 1's 8 loads may still be out
-  bar();
-  read(0, sA0, sB0, 0);
-  if (group == 1) bar();
-  // one stage per iteration: k-step 2u (operands in set 0) and 2u + 1 (set 1).  Stage
-  // u + 1 must have landed everywhere before the barrier that ends group 0's k-step
-  // 2u, which is group 1's middle barrier of that k-step: each group waits for its
-  // own loads before that barrier.
-  for (int u = 0; u < nk; ++u) {
-    const int slot = u & 1;
-    const uint8_t* const Ac = slot ? sA1 : sA0;
-    const uint8_t* const Bc = slot ? sB1 : sB0;
-    const uint8_t* const An = slot ? sA0 : sA1;
-    const uint8_t* const Bn = slot ? sB0 : sB1;
-    read(1, Ac, Bc, 1);
-    if (group == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    bar();
-    mfma(0);
-    if (group == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    bar();
-    // both groups have read stage u for the last time: stage u + 2 may take its slot
-    if (u + 2 < nk) issue(u + 2, slot);
-    if (u + 1 < nk) read(0, An, Bn, 0);
-    bar();
-    mfma(1);
-    bar();
-  }
-  if (group == 0) bar();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the workgroup ends
-
-  const int split_cols = p.N / p.nsplit;
-  const int part = n0 / split_cols;
-  uint16_t* const out = p.y[part];
-  const int col0 = n0 - part * split_cols + 128 * wn + 4 * g4;
+  for (;;) {
+    const int tm = (int)(t / tiles_n), tn = (int)(t - (int64_t)tm * tiles_n);
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int n0 = tn * kBN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = m0 + 64 * wm + 16 * i + n16;
-    if (row < p.M) {
-      uint16_t* dst = out + row * split_cols + col0;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *reinterpret_cast<uint2*>(dst + 16 * j) =
-            make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // stage 1's 8 loads may still be out
+    bar();
+    read(0, sA0, sB0, 0);
+    if (group == 1) bar();
+    for (int u = 0; u < nk; ++u) {
+      const int slot = u & 1;
+      const uint8_t* const Ac = slot ? sA1 : sA0;
+      const uint8_t* const Bc = slot ? sB1 : sB0;
+      const uint8_t* const An = slot ? sA0 : sA1;
+      const uint8_t* const Bn = slot ? sB0 : sB1;
+      read(1, Ac, Bc, 1);
+      if (group == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      bar();
+      mfma(0);
+      if (group == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      bar();
+      if (u + 2 < nk) issue(u + 2, slot);
+      if (u + 1 < nk) read(0, An, Bn, 0);
+      bar();
+      mfma(1);
+      bar();
     }
+    if (group == 0) bar();
+    // every wave has read this tile's last stage: the next tile's first two stages
+    // go out before this tile's outputs
+    const int64_t tnext = t + gridDim.x;
+    if (tnext < ntiles) {
+      setup(tnext);
+      issue(0, 0);
+      issue(1, 1);
+    }
+    const int split_cols = p.N / p.nsplit;
+    const int part = n0 / split_cols;
+    uint16_t* const out = p.y[part];
+    const int col0 = n0 - part * split_cols + 128 * wn + 4 * g4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + 64 * wm + 16 * i + n16;
+      if (row < p.M) {
+        uint16_t* dst = out + row * split_cols + col0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint2*>(dst + 16 * j) =
+              make_uint2(pack2(acc[i][j][0], acc[i][j][1]), pack2(acc[i][j][2], acc[i][j][3]));
+      }
+    }
+    if (tnext >= ntiles) break;
+    t = tnext;
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no load may still write LDS when the workgroup ends
 }
 
 }  // namespace
@@ -306,8 +317,12 @@ hipError_t launch_linear(const LinearParams& p, hipStream_t stream) {
   const int64_t tiles = ((p.M + kBM - 1) / kBM) * (int64_t)(p.N / kBN);
   // the ring kernel forms per-lane byte offsets within a 256-row tile in 32 bits
   const bool ring = p.K % (kRingSlots * kRingBK) == 0 && (int64_t)kBM * p.K * 2 < ((int64_t)1 << 32);
+  // the ring kernel holds 128 KiB of LDS, so one workgroup per compute unit (256 on
+  // gfx950); it walks the tiles, and any grid size gives the same results
+  constexpr int64_t kRingGrid = 256;
   if (ring)
-    hipLaunchKernelGGL(la_linear_ring_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, p);
+    hipLaunchKernelGGL(la_linear_ring_kernel, dim3((unsigned)(tiles < kRingGrid ? tiles : kRingGrid)), dim3(kGemmThreads),
+                       0, stream, p);
   else
     hipLaunchKernelGGL(la_linear_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, stream, p);
   return hipGetLastError();
