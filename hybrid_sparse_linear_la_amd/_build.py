@@ -36,12 +36,17 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        # the compiler's per-kernel resource report (registers, spills, scratch, LDS)
+        # is kept beside the object for the checks
+        cmd = [hipcc(), *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}\n{res.stderr}")
+        with open(os.path.join(objdir, os.path.splitext(src)[0] + ".resources.txt"), "w") as f:
+            f.write(res.stderr)
         return obj
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
