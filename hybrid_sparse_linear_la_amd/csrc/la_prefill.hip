@@ -219,14 +219,16 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   };
   // One step of the pipeline while the consumers work on chunk c: stage chunk
   // c + 1 from R, then reuse R for chunk c + 3 (chunk c + 2 is in flight in the
-  // other register set).
+  // other register set).  Every step issues the same loads and staging, past the
+  // segment's end too (the last chunk's rows again, staged into the tile half that
+  // the consumers no longer read): a load issued on some paths only made the
+  // compiler wait for both register sets' loads before staging, which left one
+  // chunk in flight instead of two.
   auto step = [&](int c, Chunk& R) {
-    if (c + 1 < tl.nch) {
-      stage(c + 1, R);
-      if (c + 3 < tl.nch) load_chunk(c + 3, R);
-      if (c + 2 < tl.nch && ptid < kHalf)
-        sRot[c & 1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + (c + 2) * kC, L.base_rev);
-    }
+    stage(c + 1, R);
+    load_chunk(min(c + 3, tl.nch - 1), R);
+    if (c + 2 < tl.nch && ptid < kHalf)
+      sRot[c & 1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + (c + 2) * kC, L.base_rev);
     __syncthreads();
     __syncthreads();
   };
@@ -238,13 +240,15 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   }
   __syncthreads();
   stage(0, Y);
-  if (tl.nch > 1) load_chunk(1, X);
-  if (tl.nch > 2) load_chunk(2, Y);
+  load_chunk(min(1, tl.nch - 1), X);
+  load_chunk(min(2, tl.nch - 1), Y);
   __syncthreads();
-  for (int c = 0; c < tl.nch; c += 2) {
+  int c = 0;
+  for (; c + 1 < tl.nch; c += 2) {
     step(c, X);
-    if (c + 1 < tl.nch) step(c + 1, Y);
+    step(c + 1, Y);
   }
+  if (c < tl.nch) step(c, X);
 }
 
 // Phase A of a consumer chunk: this wave's share of the masked scores P = Qh Kh^T
