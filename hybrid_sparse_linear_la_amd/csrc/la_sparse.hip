@@ -516,27 +516,20 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
   // rows leave without effect)
   auto block_rows = [&](int n) -> int { return n == 0 ? nv : kSB; };
 
-  // per-lane byte offsets from a block's first row
-  const uint32_t voff = (uint32_t)g4 * rsb + 16u * n16;  // row 4 u + g4, bytes 16 n16 ..
-  uint32_t koff[4];                                       // row 16 kt + n16, bytes 16 g4 ..
-#pragma unroll
-  for (int kt = 0; kt < 4; ++kt) koff[kt] = (uint32_t)(16 * kt + n16) * rsb + 16u * g4;
   auto row_ptr = [&](const uint16_t* x, int row0) {
     return reinterpret_cast<const uint8_t*>(x + base + (int64_t)row0 * rs);
   };
 
+  // Every block's K and V loads take the same form (rows clamped to the block's
+  // last row, which only the own block can need), so that the compiler counts the
+  // loads in flight alike on every path and waits for exactly the ones it needs.
   uint4 Vr[16];  // rows 4 u + g4, bytes 16 n16 .. 16 n16 + 15
   auto load_rows = [&](const uint16_t* x, int row0, int rows) {
     const uint8_t* src = row_ptr(x, row0);
-    if (rows == kSB) {
 #pragma unroll
-      for (int u = 0; u < 16; ++u) Vr[u] = *reinterpret_cast<const uint4*>(src + voff + (uint32_t)(4 * u) * rsb);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const uint32_t r = (uint32_t)min(4 * u + g4, rows - 1);
-        Vr[u] = *reinterpret_cast<const uint4*>(src + r * rsb + 16u * n16);
-      }
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t r = (uint32_t)min(4 * u + g4, rows - 1);
+      Vr[u] = *reinterpret_cast<const uint4*>(src + r * rsb + 16u * n16);
     }
   };
   // B operand Q[16 qt + n16][32 ks + 8 g4 + e], held in registers (rows past the
@@ -554,20 +547,12 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
   auto load_k = [&](int n) {
     const uint8_t* src = row_ptr(p.k, block_row0(n));
     const int rows = block_rows(n);
-    if (rows == kSB) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      const uint32_t r = (uint32_t)min(16 * kt + n16, rows - 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + koff[kt] + 64 * ks));
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const uint32_t r = (uint32_t)min(16 * kt + n16, rows - 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + r * rsb + 16u * g4 + 64 * ks));
-      }
+      for (int ks = 0; ks < 4; ++ks)
+        Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + r * rsb + 16u * g4 + 64 * ks));
     }
   };
   auto load_v = [&](int n) { load_rows(p.v, block_row0(n), block_rows(n)); };
@@ -609,12 +594,16 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
       for (int dt = 0; dt < 8; ++dt) O[dt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (pass > 0) {
-      load_v(0);  // V before K, as in the loop: the waits stay partial across the back edge
+      load_v(0);  // V before K, as in the loop
       load_k(0);
     }
     for (int n = 0; n < nblk; ++n) {
       store_v();
-      if (n + 1 < nblk) load_v(n + 1);
+      // the next block's loads, issued on every block (after the last block they
+      // fetch it again): a load issued on some paths only made the compiler wait for
+      // all loads in flight, the next block's V included, before the first products
+      const int nn = min(n + 1, nblk - 1);
+      load_v(nn);
       // per query tile: S^T = K Q^T, then its softmax numerators (the next tile's
       // products can run meanwhile)
       bf16x8 P[4][2];  // B operand of O^T += V^T P^T, keys in order pi
@@ -662,7 +651,7 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
         P[qt][0] = pack8(S[0], S[1]);
         P[qt][1] = pack8(S[2], S[3]);
       }
-      if (n + 1 < nblk) load_k(n + 1);
+      load_k(nn);
       // a lane's 16 numerators summing past 2^kRestart: a key far above the reference
       bool need = false;
 #pragma unroll
