@@ -326,11 +326,18 @@ __global__ __launch_bounds__(64) void la_sparse_select_kernel(SparseParams p, in
   float qm[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   {
     uint4 x[16];
+    // every row is loaded (rows past the block's end: its last row again) and the
+    // extra ones zeroed afterwards, so no load sits under a branch of its own and all
+    // sixteen are in flight together
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
       const int r = rg + 4 * m;
-      x[m] = r < nv ? *reinterpret_cast<const uint4*>(p.q + base + (int64_t)(r0 + r) * rs + 8 * c)
-                    : make_uint4(0u, 0u, 0u, 0u);
+      x[m] = *reinterpret_cast<const uint4*>(p.q + base + (int64_t)(r0 + min(r, nv - 1)) * rs + 8 * c);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      const uint32_t keep = rg + 4 * m < nv ? 0xffffffffu : 0u;
+      x[m] = make_uint4(x[m].x & keep, x[m].y & keep, x[m].z & keep, x[m].w & keep);
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) add_bf16x8(qm, x[m]);
