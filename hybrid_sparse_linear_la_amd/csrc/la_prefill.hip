@@ -199,14 +199,16 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
     Rows<2> q, k, v, g;
   };
   Chunk X, Y;
-  auto load_chunk = [&](int c, Chunk& R) {
+  // chunk c's rows into R; with real false, the same loads of one row (row stride
+  // 0: one cache line per load), whose values are never used
+  auto load_chunk = [&](int c, Chunk& R, bool real) {
     const int t = tl.t_begin + c * kC;
-    const int nv = min(kC, tl.t_end - t);
-    const int64_t off = tl.base + (int64_t)t * rs;
-    load_rows<2, 32>(p.q + off, rs, nv, rg, j, R.q);
-    load_rows<2, 32>(p.k + off, rs, nv, rg, j, R.k);
-    load_rows<2, 32>(p.v + off, rs, nv, rg, j, R.v);
-    load_rows<2, 32>(p.g + off, rs, nv, rg, j, R.g);
+    const int nv = real ? min(kC, tl.t_end - t) : 1;
+    const int64_t off = tl.base + (int64_t)t * rs, rs_c = real ? rs : 0;
+    load_rows<2, 32>(p.q + off, rs_c, nv, rg, j, R.q);
+    load_rows<2, 32>(p.k + off, rs_c, nv, rg, j, R.k);
+    load_rows<2, 32>(p.v + off, rs_c, nv, rg, j, R.v);
+    load_rows<2, 32>(p.g + off, rs_c, nv, rg, j, R.g);
   };
   auto stage = [&](int c, const Chunk& R) {
     const int b = c & 1;
@@ -220,28 +222,28 @@ __device__ __forceinline__ void produce(const PrefillParams& p, const Tile& tl, 
   // One step of the pipeline while the consumers work on chunk c: stage chunk
   // c + 1 from R, then reuse R for chunk c + 3 (chunk c + 2 is in flight in the
   // other register set).  Every step issues the same loads and staging, past the
-  // segment's end too (the last chunk's rows again, staged into the tile half that
-  // the consumers no longer read): a load issued on some paths only made the
-  // compiler wait for both register sets' loads before staging, which left one
+  // segment's end too (one row of the last chunk per load, staged into the tile
+  // half that the consumers no longer read): a load issued on some paths only made
+  // the compiler wait for both register sets' loads before staging, which left one
   // chunk in flight instead of two.
   auto step = [&](int c, Chunk& R) {
     stage(c + 1, R);
-    load_chunk(min(c + 3, tl.nch - 1), R);
+    load_chunk(min(c + 3, tl.nch - 1), R, c + 3 < tl.nch);
     if (c + 2 < tl.nch && ptid < kHalf)
       sRot[c & 1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + (c + 2) * kC, L.base_rev);
     __syncthreads();
     __syncthreads();
   };
 
-  load_chunk(0, Y);
+  load_chunk(0, Y, true);
   if (ptid < kHalf) {
     sRot[0][ptid] = rope_rotation(tl.pos_base + tl.t_begin, L.base_rev);
     if (tl.nch > 1) sRot[1][ptid] = rope_rotation(tl.pos_base + tl.t_begin + kC, L.base_rev);
   }
   __syncthreads();
   stage(0, Y);
-  load_chunk(min(1, tl.nch - 1), X);
-  load_chunk(min(2, tl.nch - 1), Y);
+  load_chunk(min(1, tl.nch - 1), X, tl.nch > 1);
+  load_chunk(min(2, tl.nch - 1), Y, tl.nch > 2);
   __syncthreads();
   int c = 0;
   for (; c + 1 < tl.nch; c += 2) {
