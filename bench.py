@@ -353,7 +353,7 @@ def bench_layer(la, torch, workloads, hip, args, steps=5):
     stream = torch.cuda.current_stream().cuda_stream
 
     def timed(fn):
-        fn()
+        settle(torch, fn)
         e = hip.create(2)
         torch.cuda.synchronize()
         hip.record(e[0], stream)
@@ -389,7 +389,7 @@ def bench_backward(la, torch, workloads, hip, tensors, steps=3):
     gen = workloads.generator(7, "cuda")
     d_o = torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16)
     ws = torch.empty(la.backward_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
-    la.backward(q, k, v, g, d_o, workspace=ws)
+    settle(torch, lambda: la.backward(q, k, v, g, d_o, workspace=ws))
     stream = torch.cuda.current_stream().cuda_stream
     e = hip.create(2)
     torch.cuda.synchronize()
@@ -430,7 +430,7 @@ def bench_sparse(la, torch, workloads, hip, steps=5):
     stream = torch.cuda.current_stream().cuda_stream
 
     def timed(fn, n):
-        fn()
+        settle(torch, fn)
         e = hip.create(2)
         torch.cuda.synchronize()
         hip.record(e[0], stream)
@@ -509,11 +509,20 @@ def bench_stream(la, torch, workloads, hip, steps=3):
     return out
 
 
+def settle(torch, fn, min_s=0.05, min_calls=2):
+    """Untimed calls of fn until min_s seconds have passed (at least min_calls): the
+    GPU clock takes tens of milliseconds to settle under a new load."""
+    t0, n = time.perf_counter(), 0
+    while n < min_calls or time.perf_counter() - t0 < min_s:
+        fn()
+        torch.cuda.synchronize()
+        n += 1
+
+
 def timed_calls(torch, hip, fn, n, warm=2):
     """GPU ms of each of n calls of fn (HIP events on the current stream around
     each call), after `warm` untimed calls."""
-    for _ in range(warm):
-        fn()
+    settle(torch, fn, min_calls=warm)
     stream = torch.cuda.current_stream().cuda_stream
     evs = [hip.create(2) for _ in range(n)]
     torch.cuda.synchronize()
