@@ -530,14 +530,16 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
   // Every block's K and V loads take the same form (rows clamped to the block's
   // last row, which only the own block can need), so that the compiler counts the
   // loads in flight alike on every path and waits for exactly the ones it needs.
+  // The clamp is taken on the byte offset within the block (uniform block base plus
+  // a 32-bit lane offset): one add and one min per load, no multiply or 64-bit add.
   uint4 Vr[16];  // rows 4 u + g4, bytes 16 n16 .. 16 n16 + 15
+  const uint32_t v_lane = (uint32_t)g4 * rsb + 16u * n16;
   auto load_rows = [&](const uint16_t* x, int row0, int rows) {
     const uint8_t* src = row_ptr(x, row0);
+    const uint32_t last = (uint32_t)(rows - 1) * rsb + 16u * n16;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t r = (uint32_t)min(4 * u + g4, rows - 1);
-      Vr[u] = *reinterpret_cast<const uint4*>(src + r * rsb + 16u * n16);
-    }
+    for (int u = 0; u < 16; ++u)
+      Vr[u] = *reinterpret_cast<const uint4*>(src + min(4u * u * rsb + v_lane, last));
   };
   // B operand Q[16 qt + n16][32 ks + 8 g4 + e], held in registers (rows past the
   // block's end repeat its last row; their outputs are not stored)
@@ -551,15 +553,15 @@ __global__ __launch_bounds__(64) void la_sparse_attn_kernel(SparseParams p, cons
   }
   auto q_operand = [&](int qt, int ks) { return Qf[qt][ks]; };
   bf16x8 Kf[4][4];  // [key tile][k-step]: A operand, K[16 kt + n16][32 ks + 8 g4 + e]
+  const uint32_t k_lane = (uint32_t)n16 * rsb + 16u * g4;
   auto load_k = [&](int n) {
     const uint8_t* src = row_ptr(p.k, block_row0(n));
-    const int rows = block_rows(n);
+    const uint32_t last = (uint32_t)(block_rows(n) - 1) * rsb + 16u * g4;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const uint32_t r = (uint32_t)min(16 * kt + n16, rows - 1);
+      const uint8_t* row = src + min(16u * kt * rsb + k_lane, last);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(src + r * rsb + 16u * g4 + 64 * ks));
+      for (int ks = 0; ks < 4; ++ks) Kf[kt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(row + 64 * ks));
     }
   };
   auto load_v = [&](int n) { load_rows(p.v, block_row0(n), block_rows(n)); };
