@@ -389,22 +389,41 @@ def bench_backward(la, torch, workloads, hip, tensors, steps=3):
     gen = workloads.generator(7, "cuda")
     d_o = torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16)
     ws = torch.empty(la.backward_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
-    settle(torch, lambda: la.backward(q, k, v, g, d_o, workspace=ws))
     stream = torch.cuda.current_stream().cuda_stream
-    e = hip.create(2)
-    torch.cuda.synchronize()
-    hip.record(e[0], stream)
-    for _ in range(steps):
-        la.backward(q, k, v, g, d_o, workspace=ws)
-    hip.record(e[1], stream)
-    ms = hip.ms(e[0], e[1]) / steps
-    hip.destroy(e)
+
+    def timed(fn):
+        settle(torch, fn)
+        e = hip.create(2)
+        torch.cuda.synchronize()
+        hip.record(e[0], stream)
+        for _ in range(steps):
+            fn()
+        hip.record(e[1], stream)
+        ms = hip.ms(e[0], e[1]) / steps
+        hip.destroy(e)
+        return ms
+
+    ms = timed(lambda: la.backward(q, k, v, g, d_o, workspace=ws))
+    # the backward reusing the segment states of the forward call that produced o
+    fws = torch.empty(la.prefill_workspace_bytes(B, T, H, D), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    la.prefill(q, k, v, g, out=o, workspace=fws)
+    saved_ms = timed(lambda: la.backward(q, k, v, g, d_o, workspace=ws, fwd_workspace=fws))
+    step_ms = timed(lambda: (la.prefill(q, k, v, g, out=o, workspace=fws),
+                             la.backward(q, k, v, g, d_o, workspace=ws, fwd_workspace=fws)))
+    del o, fws
     # bytes every backward must move: read q, k, v, g, d_o and write dq, dk, dv, dgate
     comp = 9 * 256 * B * T * H
+    roof = comp / (HBM_PEAK_GBS * 1e9)
     return {"workload": "backward_" + workloads.PREFILL_256K.name, "steps": steps, "ms": round(ms, 4),
             "tokens_per_s": round(B * T / (ms / 1e3), 1), "compulsory_bytes": comp,
-            "hbm_roof_ms": round(comp / (HBM_PEAK_GBS * 1e9) * 1e3, 4),
-            "path_frac": round(comp / (HBM_PEAK_GBS * 1e9) / (ms / 1e3), 4)}
+            "hbm_roof_ms": round(roof * 1e3, 4), "path_frac": round(roof / (ms / 1e3), 4),
+            "saved_forward_states": {
+                "note": "la_backward_saved: the segment states of the la_prefill call that computed the "
+                        "forward are reused (no forward state pass or scan in the backward)",
+                "ms": round(saved_ms, 4), "tokens_per_s": round(B * T / (saved_ms / 1e3), 1),
+                "path_frac": round(roof / (saved_ms / 1e3), 4),
+                "forward_plus_backward_ms": round(step_ms, 4)}}
 
 
 def sparse_prefill_keys(T: int, topk: int, block: int = 64) -> int:

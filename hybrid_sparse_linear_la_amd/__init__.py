@@ -93,6 +93,8 @@ def library():
         lib.la_backward.restype = ctypes.c_int
         lib.la_backward.argtypes = [_vp] * 14 + [ctypes.c_int] * 4 + [
             ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.la_backward_saved.restype = ctypes.c_int
+        lib.la_backward_saved.argtypes = lib.la_backward.argtypes[:-1] + [_vp, ctypes.c_size_t, _vp]
         lib.la_decode_step.restype = ctypes.c_int
         lib.la_decode_step.argtypes = [_vp] * 6 + [ctypes.c_int] * 3 + [
             ctypes.c_int64, ctypes.c_float, ctypes.c_float, _vp, _vp, _vp]
@@ -374,11 +376,13 @@ def backward_workspace_bytes(B: int, T: int, H: int, D: int = HEAD_DIM, chunk: i
 
 def backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0: int = 0, chunk: int = 0,
              rope_base: float = 10000.0, rms_eps: float = 1e-6, q_norm_w=None, k_norm_w=None,
-             weight_grads: bool = False, workspace=None):
+             weight_grads: bool = False, workspace=None, fwd_workspace=None):
     """Gradients of la_prefill for output gradient d_o (bf16 [B, T, H, 128]) and
     final-state gradient dS_out (fp32 [B, H, 128, 128] or None).  Returns a dict
     with dq, dk, dv, dgate (bf16), dS_in (fp32) and, with weight_grads, dq_norm_w
-    and dk_norm_w (fp32 [128]; at weights of one when none are given)."""
+    and dk_norm_w (fp32 [128]; at weights of one when none are given).
+    ``fwd_workspace``: the workspace of the ``prefill`` call that computed this
+    forward (la_backward_saved: its segment states are reused)."""
     lib = library()
     for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("d_o", d_o)):
         _act(n, t, 4)
@@ -400,12 +404,19 @@ def backward(q, k, v, gate, d_o, S_in=None, dS_out=None, pos0: int = 0, chunk: i
         status = 3 if (D != HEAD_DIM or chunk not in (0, 64)) else 2
         raise LAError(status, lib.la_status_string(status).decode())
     workspace = _workspace(workspace, need, dev)
-    _check(lib.la_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(d_o), _ptr(dS_out),
-                           _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
-                           _ptr(out["dS_in"]), _ptr(out.get("dq_norm_w")), _ptr(out.get("dk_norm_w")), B, T, H, D,
-                           int(pos0), int(chunk), float(rope_base), float(rms_eps), _ptr(q_norm_w),
-                           _ptr(k_norm_w), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream(q.device)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S_in), _ptr(d_o), _ptr(dS_out),
+            _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dgate"]),
+            _ptr(out["dS_in"]), _ptr(out.get("dq_norm_w")), _ptr(out.get("dk_norm_w")), B, T, H, D,
+            int(pos0), int(chunk), float(rope_base), float(rms_eps), _ptr(q_norm_w),
+            _ptr(k_norm_w), _ptr(workspace), workspace.numel() * workspace.element_size())
+    if fwd_workspace is None:
+        _check(lib.la_backward(*args, _stream(q.device)))
+    else:
+        if not isinstance(fwd_workspace, torch.Tensor) or fwd_workspace.device != dev or \
+                not fwd_workspace.is_contiguous():
+            raise ValueError(f"fwd_workspace must be a contiguous tensor on {dev}")
+        _check(lib.la_backward_saved(*args, _ptr(fwd_workspace),
+                                     fwd_workspace.numel() * fwd_workspace.element_size(), _stream(q.device)))
     return out
 
 

@@ -635,12 +635,15 @@ size_t la_backward_workspace_bytes(int B, int T, int H, int D, int chunk) {
   return off[5] + (size_t)2 * kPrologueBlocks * kHeadDim * sizeof(float);
 }
 
-la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
-                      const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
-                      la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
-                      int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
-                      const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+// The backward, with the forward segment states recomputed (fwd_ws null) or read
+// from the workspace of the forward call (fwd_ws, when that call kept them).
+static la_status backward_impl(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                               const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq,
+                               la_bf16* dk, la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w,
+                               float* dk_norm_w, int B, int T, int H, int D, int64_t pos0, int chunk,
+                               float rope_base, float rms_eps, const float* q_norm_w, const float* k_norm_w,
+                               void* workspace, size_t workspace_bytes, const void* fwd_ws, size_t fwd_ws_bytes,
+                               void* stream) {
   if (!q || !k || !v || !gate_logits || !d_o || !dq || !dk || !dv || !dgate || !dS_in || !workspace)
     return LA_ERR_NULL_PTR;
   if (B < 1 || T < 1 || H < 1) return LA_ERR_BAD_SHAPE;
@@ -650,14 +653,30 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
   if (!plan_prefill(B, T, H, chunk, &plan)) return LA_ERR_BAD_SHAPE;
   const size_t need = la_backward_workspace_bytes(B, T, H, D, chunk);
   const void* ptrs[] = {q, k, v, gate_logits, S_in, d_o, dS_out, dq, dk, dv, dgate, dS_in,
-                        dq_norm_w, dk_norm_w, q_norm_w, k_norm_w, workspace};
+                        dq_norm_w, dk_norm_w, q_norm_w, k_norm_w, workspace, fwd_ws};
   for (const void* ptr : ptrs)
     if (!aligned16(ptr)) return LA_ERR_ALIGNMENT;
+  // The forward kept its segment states when its own plan (la_prefill's) is not the
+  // one-workgroup-per-(b, h) form; it is then this plan, so the layouts agree.
+  const float* saved = nullptr;
+  uint64_t saved_bytes = 0;
+  if (fwd_ws) {
+    PrefillPlan fplan;
+    plan_prefill(B, T, H, chunk, &fplan, true);
+    if (!fplan.direct) {
+      if (fplan.nseg != plan.nseg || fplan.cps != plan.cps) return LA_ERR_UNSUPPORTED;
+      if (fwd_ws_bytes < fplan.ws_bytes) return LA_ERR_WORKSPACE;
+      saved = static_cast<const float*>(fwd_ws);
+      saved_bytes = fplan.ws_bytes;
+    }
+  }
   const uint64_t act = (uint64_t)B * T * H * D * sizeof(la_bf16);
   const uint64_t st = (uint64_t)B * H * D * D * sizeof(float);
   const uint64_t wb = (uint64_t)D * sizeof(float);
-  const std::pair<const void*, uint64_t> ins[] = {{q, act}, {k, act}, {v, act}, {gate_logits, act}, {d_o, act},
-                                                  {S_in, st}, {dS_out, st}, {q_norm_w, wb}, {k_norm_w, wb}};
+  const std::pair<const void*, uint64_t> ins[] = {{q, act},      {k, act},          {v, act},
+                                                  {gate_logits, act}, {d_o, act},    {S_in, st},
+                                                  {dS_out, st},  {q_norm_w, wb},    {k_norm_w, wb},
+                                                  {saved, saved_bytes}};
   const std::pair<const void*, uint64_t> outs[] = {{dq, act}, {dk, act}, {dv, act}, {dgate, act}, {dS_in, st},
                                                    {dq_norm_w, wb}, {dk_norm_w, wb}, {workspace, need}};
   for (size_t a = 0; a < sizeof(outs) / sizeof(outs[0]); ++a) {
@@ -678,7 +697,8 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
   p.v = v;
   p.g = gate_logits;
   p.o = nullptr;
-  p.ws = reinterpret_cast<float*>(ws + off[0]);
+  // the kernels only read the forward states once they are formed
+  p.ws = saved ? const_cast<float*>(saved) : reinterpret_cast<float*>(ws + off[0]);
   p.segs = nullptr;
   p.seqs = nullptr;
   p.S_in = S_in;
@@ -707,8 +727,30 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
   bp.dk_w = dk_norm_w;
   bp.wpart = reinterpret_cast<float*>(ws + off[5]);
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_segment_states(bp, plan, s) != hipSuccess) return LA_ERR_HIP;
+  if (launch_segment_states(bp, plan, saved != nullptr, s) != hipSuccess) return LA_ERR_HIP;
   return launch_backward_chunks(bp, plan, s) == hipSuccess ? LA_OK : LA_ERR_HIP;
+}
+
+la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                      const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
+                      la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
+                      int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
+                      const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return backward_impl(q, k, v, gate_logits, S_in, d_o, dS_out, dq, dk, dv, dgate, dS_in, dq_norm_w, dk_norm_w, B,
+                       T, H, D, pos0, chunk, rope_base, rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes,
+                       nullptr, 0, stream);
+}
+
+la_status la_backward_saved(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                            const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
+                            la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
+                            int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
+                            const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                            const void* fwd_workspace, size_t fwd_workspace_bytes, void* stream) {
+  return backward_impl(q, k, v, gate_logits, S_in, d_o, dS_out, dq, dk, dv, dgate, dS_in, dq_norm_w, dk_norm_w, B,
+                       T, H, D, pos0, chunk, rope_base, rms_eps, q_norm_w, k_norm_w, workspace, workspace_bytes,
+                       fwd_workspace, fwd_workspace_bytes, stream);
 }
 
 static bool sparse_shape_ok(int B, int T, int H, int D, int block, int topk, la_status* st) {

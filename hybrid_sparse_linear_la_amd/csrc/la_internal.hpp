@@ -133,7 +133,10 @@ constexpr int kPrologueBlocks = 2048;
 
 // The forward segment states of la_prefill into f.ws (f.S_out receives the final
 // state), then the gradient segment states into wsg and dS_in.
-hipError_t launch_segment_states(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
+// forward_saved: f.ws already holds the forward segment states (only the gradient
+// states are formed)
+hipError_t launch_segment_states(const BackwardParams& p, const PrefillPlan& plan, bool forward_saved,
+                                 hipStream_t stream);
 hipError_t launch_backward_chunks(const BackwardParams& p, const PrefillPlan& plan, hipStream_t stream);
 
 // Sparse attention layer (block-selected causal softmax attention, NoPE, output

@@ -804,15 +804,18 @@ hipError_t launch_prefill(const PrefillParams& p, const PrefillPlan& plan, hipSt
   return err != hipSuccess ? err : launch;
 }
 
-hipError_t launch_segment_states(const BackwardParams& bp, const PrefillPlan& plan, hipStream_t stream) {
+hipError_t launch_segment_states(const BackwardParams& bp, const PrefillPlan& plan, bool forward_saved,
+                                 hipStream_t stream) {
   const dim3 grid((unsigned)(plan.nwork * bp.f.H));
   const dim3 scan_grid((unsigned)(((int64_t)bp.f.B * bp.f.H * kD * kD / 4 + 255) / 256));
   PrefillParams f = bp.f;  // forward states into f.ws, final state into f.S_out
-  if (f.kw)
-    hipLaunchKernelGGL((la_chunk_state_kernel<true, false>), grid, dim3(kThreads), 0, stream, f);
-  else
-    hipLaunchKernelGGL((la_chunk_state_kernel<false, false>), grid, dim3(kThreads), 0, stream, f);
-  hipLaunchKernelGGL(la_state_scan_kernel<false>, scan_grid, dim3(256), 0, stream, f);
+  if (!forward_saved) {
+    if (f.kw)
+      hipLaunchKernelGGL((la_chunk_state_kernel<true, false>), grid, dim3(kThreads), 0, stream, f);
+    else
+      hipLaunchKernelGGL((la_chunk_state_kernel<false, false>), grid, dim3(kThreads), 0, stream, f);
+    hipLaunchKernelGGL(la_state_scan_kernel<false>, scan_grid, dim3(256), 0, stream, f);
+  }
   PrefillParams g = bp.f;  // gradient states: sums of Qh^T dU, suffix-scanned from dS_out
   g.ws = bp.wsg;
   g.S_in = bp.dS_out;

@@ -267,6 +267,32 @@ la_status la_backward(const la_bf16* q, const la_bf16* k, const la_bf16* v, cons
                       void* stream);
 
 /*
+ * la_backward with the forward's segment states taken from the workspace of the
+ * la_prefill call that computed the same forward (same q, k, v, gate_logits,
+ * S_in, B, T, H, D, pos0, chunk, rope_base, rms_eps and norm weights, its
+ * workspace not written since; la_prefill_varlen and la_prefill_noalloc
+ * workspaces do not qualify).  That call's state pass and scan already formed the
+ * state at every segment start, so the backward's own forward state pass (a read
+ * of k and v) and scan are skipped; the results are those of la_backward, bit for
+ * bit.  The reverse mode is that of la_backward ("MiniCPM-SALA: Hybridizing
+ * Sparse and Linear Attention for Efficient Long-Context Modeling", 前置知识 >
+ * 线性注意力; the report's 04 技術報告 > 03 模型訓練).
+ *   fwd_workspace : that call's workspace (read only; NULL: recompute, as
+ *       la_backward), fwd_workspace_bytes its size.  When la_prefill walks each
+ *       (b, h) in one workgroup for this shape it keeps no states, and they are
+ *       recomputed.
+ * Other arguments as la_backward.  Errors as la_backward, plus LA_ERR_WORKSPACE
+ * when fwd_workspace_bytes is below la_prefill_workspace_bytes for the shape, and
+ * LA_ERR_ALIASING when an output or the workspace overlaps fwd_workspace.
+ */
+la_status la_backward_saved(const la_bf16* q, const la_bf16* k, const la_bf16* v, const la_bf16* gate_logits,
+                            const float* S_in, const la_bf16* d_o, const float* dS_out, la_bf16* dq, la_bf16* dk,
+                            la_bf16* dv, la_bf16* dgate, float* dS_in, float* dq_norm_w, float* dk_norm_w, int B,
+                            int T, int H, int D, int64_t pos0, int chunk, float rope_base, float rms_eps,
+                            const float* q_norm_w, const float* k_norm_w, void* workspace, size_t workspace_bytes,
+                            const void* fwd_workspace, size_t fwd_workspace_bytes, void* stream);
+
+/*
  * One decode step: one token per sequence at absolute position pos.
  *   q, k, v, gate_logits : [B, H, D] bf16.
  *   S : [B, H, D, D] fp32 state, updated in place (S += kh v^T).

@@ -23,7 +23,7 @@ namespace la {
 hipError_t launch_linear(const LinearParams&, hipStream_t) { reached("launch_linear"); }
 hipError_t launch_prefill(const PrefillParams&, const PrefillPlan&, hipStream_t, hipEvent_t const*) { reached("launch_prefill"); }
 hipError_t launch_decode(const DecodeParams&, hipStream_t) { reached("launch_decode"); }
-hipError_t launch_segment_states(const BackwardParams&, const PrefillPlan&, hipStream_t) { reached("launch_segment_states"); }
+hipError_t launch_segment_states(const BackwardParams&, const PrefillPlan&, bool, hipStream_t) { reached("launch_segment_states"); }
 hipError_t launch_backward_chunks(const BackwardParams&, const PrefillPlan&, hipStream_t) { reached("launch_backward_chunks"); }
 hipError_t launch_sparse_means(const SparseParams&, int, int, hipStream_t) { reached("launch_sparse_means"); }
 hipError_t launch_sparse_prefill(const SparseParams&, int32_t*, hipStream_t) { reached("launch_sparse_prefill"); }
@@ -84,6 +84,14 @@ int main() {
   CHECK(la_backward(A, at(8), at(16), at(24), nullptr, at(32), nullptr, at(40), at(48), at(56), at(64), Sf, nullptr,
                     nullptr, 1, 64, 2, 128, 0, 128, 1e4f, 1e-6f, nullptr, nullptr, at(300), 1 << 30,
                     nullptr) == LA_ERR_UNSUPPORTED);
+  // the forward's workspace: smaller than la_prefill's for the shape, then overlapping an output
+  // (activations of 10 MiB at this shape, 16 MiB apart)
+  CHECK(la_backward_saved(A, at(16), at(32), at(48), nullptr, at(64), nullptr, at(80), at(96), at(112), at(128), Sf,
+                          nullptr, nullptr, 1, 20000, 2, 128, 0, 0, 1e4f, 1e-6f, nullptr, nullptr, at(300), 1 << 30,
+                          at(2048), 4096, nullptr) == LA_ERR_WORKSPACE);
+  CHECK(la_backward_saved(A, at(16), at(32), at(48), nullptr, at(64), nullptr, at(80), at(96), at(112), at(128), Sf,
+                          nullptr, nullptr, 1, 20000, 2, 128, 0, 0, 1e4f, 1e-6f, nullptr, nullptr, at(300), 1 << 30,
+                          at(90), 1 << 26, nullptr) == LA_ERR_ALIASING);   // overlaps dq and dk
   CHECK(la_sparse_prefill(A, at(8), at(16), at(24), at(32), nullptr, 1, 100, 2, 128, 0, 0, at(300), 1 << 30,
                           nullptr) == LA_ERR_UNSUPPORTED);
   CHECK(la_sparse_block_means(A, Sf, 1, 1024, 2, 128, 0, 10, 7, nullptr) == LA_ERR_BAD_SHAPE);

@@ -28,7 +28,7 @@ def test_header_declares_the_boundary():
         ["la_version", "la_status_string", "la_prefill_workspace_bytes", "la_prefill", "la_prefill_profiled",
          "la_prefill_noalloc",
          "la_prefill_varlen_workspace_bytes", "la_prefill_varlen", "la_linear", "la_layer_workspace_bytes",
-         "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_decode_step",
+         "la_layer_forward", "la_backward_workspace_bytes", "la_backward", "la_backward_saved", "la_decode_step",
          "la_sparse_prefill_workspace_bytes", "la_sparse_prefill", "la_sparse_block_means", "la_sparse_decode"])
 
 
@@ -241,6 +241,28 @@ def test_backward_validation(lib):
     assert bwd(dk=A + 8 * MB + 64) == 5   # dk overlaps dq
     assert bwd(ws=A + 12 * MB) == 5       # workspace overlaps dS_in
     assert bwd(ws_bytes=4096) == 6
+
+
+def test_backward_saved_validation(lib):
+    """la_backward_saved checks the forward workspace before anything is launched:
+    alignment, size (la_prefill's for the shape) and overlap with the outputs."""
+    vp = ctypes.c_void_p
+    B, T, H = 1, 20000, 2             # la_prefill keeps segment states for this shape
+    fwd_need = lib.la_prefill_workspace_bytes(B, T, H, 128, 0)
+    assert fwd_need > 4096
+    act = B * T * H * 128 * 2
+
+    def bwd(fwd=A + 512 * MB, fwd_bytes=fwd_need, dq=A + 100 * MB, ws_bytes=1 << 30):
+        return lib.la_backward_saved(vp(A), vp(A + 20 * MB), vp(A + 40 * MB), vp(A + 60 * MB), None,
+                                     vp(A + 80 * MB), None, vp(dq), vp(A + 120 * MB), vp(A + 140 * MB),
+                                     vp(A + 160 * MB), vp(A + 180 * MB), None, None, B, T, H, 128, 0, 0, 10000.0,
+                                     1e-6, None, None, vp(A + 200 * MB), ws_bytes, vp(fwd) if fwd else None,
+                                     fwd_bytes, None)
+    assert act < 20 * MB
+    assert bwd(fwd=A + 512 * MB + 8) == 4               # misaligned forward workspace
+    assert bwd(fwd_bytes=fwd_need - 256) == 6           # smaller than la_prefill's
+    assert bwd(dq=A + 512 * MB + 4096) == 5             # an output inside the forward workspace
+    assert bwd(ws_bytes=4096) == 6                      # the backward's own workspace still checked
 
 
 def test_sparse_validation(lib):

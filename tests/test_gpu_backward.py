@@ -176,3 +176,26 @@ def test_backward_random_shapes_match_oracle(la, B, T, H, pos0, S_std, dS_std, w
                         weight_grads=weight_grads)
     torch.cuda.synchronize()
     _check(grads, q, k, v, g, d_o, S_in, dS_out, pos0, qw, kw, weight_grads)
+
+
+@pytest.mark.parametrize("B,T,H,pos0,S_std,weights,weight_grads", [
+    (1, 5000, 4, 0, 0.0, False, False),     # many segments per (b, h)
+    (2, 777, 3, 9000, 0.02, True, True),     # ragged tail, initial state, norm weights and their gradients
+    (2, 200, 128, 0, 0.02, False, False),    # 256 (b, h): la_prefill keeps no states, they are recomputed
+])
+def test_backward_with_saved_forward_states(la, B, T, H, pos0, S_std, weights, weight_grads):
+    """la_backward_saved, given the workspace of the la_prefill call that computed the
+    forward, reuses its segment states: the gradients equal la_backward's bit for bit
+    (the same kernels form the same states), and the oracle's within tolerance."""
+    print(f"backward saved states B={B} T={T} H={H}", flush=True)
+    q, k, v, g, d_o, S_in, dS_out, qw, kw = _inputs(B, T, H, 4242 + T, S_std, 0.01, weights)
+    kw_args = dict(S_in=S_in, pos0=pos0, q_norm_w=qw, k_norm_w=kw)
+    fws = torch.full((la.prefill_workspace_bytes(B, T, H),), 0xFF, dtype=torch.uint8, device="cuda")
+    la.prefill(q, k, v, g, workspace=fws, **kw_args)
+    ref = la.backward(q, k, v, g, d_o, dS_out=dS_out, weight_grads=weight_grads, **kw_args)
+    got = la.backward(q, k, v, g, d_o, dS_out=dS_out, weight_grads=weight_grads, fwd_workspace=fws, **kw_args)
+    torch.cuda.synchronize()
+    for name in ref:
+        assert torch.equal(ref[name].view(torch.int8) if ref[name].dtype == torch.bfloat16 else ref[name],
+                           got[name].view(torch.int8) if got[name].dtype == torch.bfloat16 else got[name]), name
+    _check(got, q, k, v, g, d_o, S_in, dS_out, pos0, qw, kw, weight_grads)
